@@ -1,0 +1,165 @@
+#!/usr/bin/env python
+"""Throughput of the W4A4 + LoRA linear layer on one MI355X.
+
+One step = one pass of the whole hot path over one batch already resident in
+HBM: w4a4_quantize_act (int4 codes + scales + LoRA-down) followed by
+w4a4_linear (integer MFMA GEMM + per-group dequant + LoRA-up + affine).
+Default workload: the MLP up-projection at a 700-token batch
+(M=700, K=1024, N=3072, LoRA rank 32, group 64), seeded synthetic inputs.
+
+Prints ONE JSON line (rank 0, N=1 only).  Per-kernel durations come from HIP
+events recorded on the stream the kernels are launched on.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "W4A4+LoRA linear TOPS & HBM GB/s at 1 GPU; % of roofline per shape"
+PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA, 10^12 ops/s
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+
+
+def algorithmic_counts(M, N, K, R):
+    """Ops and bytes the method must do / move (not those of an fp16 GEMM).
+
+    linear kernel: ops 2MNK + 2MNR; bytes X_q + s_x + lora_act + W_q + s_w +
+    L_up + a + b + Y.  quantize kernel: ops 2MKR; bytes X + L_down + X_q + s_x
+    + lora_act.  Padding rows (M rounded up to 16) are counted as moved only
+    where the kernel actually reads them (the activation blob)."""
+    Mp = (M + 15) // 16 * 16
+    G = K // 64
+    lin_bytes = (Mp * K // 2 + Mp * G * 2 + Mp * R * 4 + N * K // 2 + N * G * 2 + N * R * 2
+                 + 8 * N + M * N * 2)
+    q_bytes = M * K * 2 + K * R * 2 + Mp * K // 2 + Mp * G * 2 + Mp * R * 4
+    return dict(lin_ops=2 * M * N * K + 2 * M * N * R, lin_bytes=lin_bytes,
+                q_ops=2 * M * K * R, q_bytes=q_bytes,
+                layer_ops=2 * M * N * K + 2 * M * R * (K + N))
+
+
+def cpu_baseline(case, budget_s=10.0):
+    """The oracle, as it stands, on the same workload: whole layers repeated
+    until about budget_s seconds of CPU time have been spent."""
+    from oracle import w4a4_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    n, t0 = 0, time.perf_counter()
+    while True:
+        O.linear(case["x"], case["lora_down"], case["lora_up"], case["col_scale"], case["bias"],
+                 w16=case["w"])
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 50:
+            break
+    c = algorithmic_counts(case["M"], case["N"], case["K"], case["R"])
+    return {"value": round(c["layer_ops"] * n / el / 1e12, 6), "unit": "TOPS", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{n} full-layer oracle evaluations (M={case['M']} K={case['K']} N={case['N']} "
+                      f"R={case['R']}), numpy fp64 + BLAS, {el:.1f} s wall"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="mlp_up")
+    ap.add_argument("--m", type=int, default=None, help="row count override (decode sweep)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the layer's "
+              "multi-GPU sharding is a design note, not a measured path.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    import w4a4_gemm_lora_amd as W
+    from w4a4_gemm_lora_amd import workloads
+
+    torch.cuda.set_device(0)
+    case = workloads.generate(args.workload, M=args.m)
+    M, K, N, R = case["M"], case["K"], case["N"], case["R"]
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    x = dev(case["x"])
+    wblob = W.alloc_weight_blob(N, K, R)
+    W.w4a4_pack_weights(N, K, R, wblob, w_fp16=dev(case["w"]), lora_down=dev(case["lora_down"]),
+                        lora_up=dev(case["lora_up"]), col_scale=dev(case["col_scale"]),
+                        bias=dev(case["bias"]))
+    act = W.alloc_act_blob(M, K, R)
+    y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def step():
+        W.w4a4_quantize_act(M, K, R, x, wblob, act, stream=sh)
+        W.w4a4_linear(M, N, K, R, act, wblob, y, stream=sh)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K whole steps, with events around each kernel
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        W.w4a4_quantize_act(M, K, R, x, wblob, act, stream=sh)
+        ev[i][1].record(stream)
+        W.w4a4_linear(M, N, K, R, act, wblob, y, stream=sh)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    q_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    l_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+
+    c = algorithmic_counts(M, N, K, R)
+    value = c["layer_ops"] / (ms_per_step * 1e-3) / 1e12
+    lin_tops = c["lin_ops"] / (l_ms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: W4A4+LoRA linear M={M} K={K} N={N} R={R} group 64",
+                   "M": M, "K": K, "N": N, "R": R, "group": 64,
+                   "variant": W.w4a4_query_variant(M, N, K, R)},
+        "hbm_gbps_step": round((c["lin_bytes"] + c["q_bytes"]) / (ms_per_step * 1e-3) / 1e9, 1),
+        "kernels": {
+            "w4a4_linear": {"avg_us": round(l_ms * 1e3, 3), "TOPS": round(lin_tops, 2),
+                             "GBps": round(c["lin_bytes"] / (l_ms * 1e-3) / 1e9, 1)},
+            "w4a4_quantize_act": {"avg_us": round(q_ms * 1e3, 3),
+                                   "GBps": round(c["q_bytes"] / (q_ms * 1e-3) / 1e9, 1)},
+        },
+        "roofline": {"bound": "mfma", "achieved": round(lin_tops, 2), "peak": PEAK_INT8_TOPS,
+                     "unit": "TFLOP/s", "frac": round(lin_tops / PEAK_INT8_TOPS, 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(case)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

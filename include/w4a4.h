@@ -1,0 +1,153 @@
+/*
+ * w4a4.h -- C ABI of libw4a4.so: a W4A4 linear layer with a fused low-rank
+ * (LoRA / SVDQuant) correction and a column-wise affine, for AMD MI355X
+ * (gfx950).
+ *
+ *   Y[m,n] = a[n] * ( sum_g s_x[m,g] s_w[n,g] P[m,n,g]
+ *                     + sum_r lora_act[m,r] L_up[n,r] ) + b[n]
+ *   P[m,n,g]      = sum over the 64 k of group g of q_x[m,k] q_w[n,k]
+ *   lora_act[m,r] = sum_k X[m,k] L_down[k,r]
+ *
+ * Sources: "W4A4 CUDA Kernel for Voice Clone: From Profiling to 2.6x Faster
+ * Than FP16" (section 2.1 low-rank correction; 2.3 checkpoint tensors; 3.4
+ * the three-kernel forward; 3.6 fused quantize + LoRA-down; 3.7 GEMM +
+ * per-group dequant + LoRA-up), and "High-Performance Kernel Design for W4A4
+ * Quantized Matrix Multiplication on Blackwell Architecture" (section 1:
+ * scaled low-bit matmul + low-rank residual + column-wise affine).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every pointer argument is a DEVICE pointer unless stated otherwise; fp16
+ *   tensors are passed as uint16_t bit patterns.  `stream` is a hipStream_t
+ *   (NULL = the legacy default stream).  Every call only enqueues work on
+ *   `stream` and returns; nothing is synchronized.
+ * - The library allocates no memory and keeps no per-call state: the caller
+ *   owns every buffer (sizes come from w4a4_weight_layout / w4a4_act_layout).
+ * - Arguments are validated on the host before anything is enqueued; on error
+ *   nothing is launched and a non-zero w4a4_status is returned.  Shapes the
+ *   kernels do not support return W4A4_ERR_SHAPE; there is no fallback path.
+ * - Shape rules: K % 128 == 0 (two 64-wide quantization groups per 128),
+ *   N % 16 == 0, R % 16 == 0 with 0 <= R <= 64, M >= 0 (M == 0 is a no-op).
+ *   Mp = M rounded up to a multiple of 16 (padding rows of the activation
+ *   blob hold q = 0 and scale 0).
+ * - Inputs must be finite.
+ * - Calls that write the same buffer must not overlap on different streams.
+ *
+ * Packed layouts (the one definition of both blobs)
+ * -------------------------------------------------
+ * Codes: q in [-8, 7] stored as the low 4 bits of q (two's complement).
+ * A "16 x 128 tile" of codes (16 rows of X, or 16 rows n of W, times 128
+ * consecutive k = two 64-groups) is 1024 bytes: lane l = r + 16*c
+ * (r = row in tile 0..15, c = 0..3) owns bytes [16*l, 16*l + 16):
+ * bytes 0..7 hold group 0 of the tile and bytes 8..15 group 1; within a
+ * group's 8 bytes, byte b holds k = 16*c + 2*b (low nibble) and 16*c + 2*b + 1
+ * (high nibble), k counted from the start of that group.
+ *
+ * Weight blob (w4a4_pack_weights writes it; offsets from w4a4_weight_layout;
+ * every section starts on a 256-byte boundary), KP = K/128, G = K/64:
+ *   [0] L_down: fp16, [KP][R/16][4][64][8]: entry (p, t, s, l = n + 16c, j)
+ *       = L_down[128p + 64*(s/2) + 16c + 8*(s%2) + j][16t + n]
+ *   [1] W_q:    [N/16][KP] tiles of 1024 bytes (layout above, rows = n)
+ *   [2] s_w:    fp16, [N/16][KP][16][2]: entry (nt, p, i, h) = s_w[16nt+i][2p+h]
+ *   [3] L_up:   fp16, [N/16][R/16][64][4]: entry (nt, t, l = i + 16c, j)
+ *       = L_up[16nt + i][16t + 4c + j]
+ *   [4] a:      fp32 [N]   (column scale)
+ *   [5] b:      fp32 [N]   (bias)
+ * Activation blob (w4a4_quantize_act writes it; offsets from w4a4_act_layout):
+ *   [0] X_q:      [Mp/16][KP] tiles of 1024 bytes (rows = m)
+ *   [1] s_x:      fp16, [Mp/16][KP][16][2]: entry (mt, p, i, h) = s_x[16mt+i][2p+h]
+ *   [2] lora_act: fp32 [Mp][R], row-major
+ */
+#ifndef W4A4_H_
+#define W4A4_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes of every call below. */
+typedef enum {
+  W4A4_OK = 0,
+  W4A4_ERR_NULL = 1,   /* a required pointer is NULL                       */
+  W4A4_ERR_SHAPE = 2,  /* a shape rule above is violated (no fallback)     */
+  W4A4_ERR_ALIGN = 3,  /* a pointer or leading dimension is misaligned     */
+  W4A4_ERR_ARG = 4,    /* inconsistent optional arguments                  */
+  W4A4_ERR_HIP = 5     /* the HIP runtime reported an error at launch      */
+} w4a4_status;
+
+/* Static, NUL-terminated name of a status code (host only, never NULL). */
+const char* w4a4_status_string(int status);
+
+/* Sizes of the weight blob (host-only, no GPU needed).  total_bytes and
+ * offsets[6] (section order as above) are HOST pointers; offsets may be NULL.
+ * Errors: W4A4_ERR_NULL if total_bytes is NULL, W4A4_ERR_SHAPE on bad shapes. */
+int w4a4_weight_layout(int64_t N, int64_t K, int32_t R,
+                       size_t* total_bytes, size_t* offsets);
+
+/* Sizes of the activation blob for M rows (host-only).  offsets[3] as above;
+ * offsets may be NULL.  Errors as for w4a4_weight_layout. */
+int w4a4_act_layout(int64_t M, int64_t K, int32_t R,
+                    size_t* total_bytes, size_t* offsets);
+
+/* Offline weight preparation, once per layer ("W4A4 CUDA Kernel for Voice
+ * Clone", section 2.3: repack the checkpoint into the kernel's layout once at
+ * load).  Exactly one source of codes is given:
+ *   w_fp16 [N][K] fp16 row-major: quantized here with the activation rule
+ *     (per (n, 64-group) absmax, scale fp16(absmax/7), round-half-even);
+ *   or qweight [N][K/2] uint8 (byte j: k=2j low nibble, k=2j+1 high nibble,
+ *     two's complement) together with w_scales [N][K/64] fp16.
+ * lora_down [K][R] and lora_up [N][R] fp16 row-major (both ignored if R==0,
+ * required otherwise).  col_scale, bias fp32 [N] (NULL -> 1 and 0).
+ * wblob: device buffer of w4a4_weight_layout's total_bytes, 256-byte aligned.
+ * Pointers must be 16-byte aligned, except qweight / w_scales / col_scale /
+ * bias / lora_* which need only their element alignment. */
+int w4a4_pack_weights(int64_t N, int64_t K, int32_t R,
+                      const uint16_t* w_fp16, const uint8_t* qweight,
+                      const uint16_t* w_scales, const uint16_t* lora_down,
+                      const uint16_t* lora_up, const float* col_scale,
+                      const float* bias, void* wblob, void* stream);
+
+/* Per forward, kernel 1 ("W4A4 CUDA Kernel for Voice Clone", section 3.6):
+ * reads X once and writes the activation blob: int4 codes and fp16 scales per
+ * (row, 64-group) -- scale = fp16(fp32(absmax/7)), a zero scale replaced by
+ * 2^-24, q = clamp(rint(x / scale), -8, 7) with an IEEE fp32 division -- and
+ * lora_act = X L_down (fp32, from the fp16 X, not the codes).
+ * x: fp16 [M][ldx], ldx >= K, ldx % 8 == 0, 16-byte aligned.
+ * wblob: a blob packed for this (K, R) (any N).  act: device buffer of
+ * w4a4_act_layout's total_bytes, 256-byte aligned. */
+int w4a4_quantize_act(int64_t M, int64_t K, int32_t R, const uint16_t* x,
+                      int64_t ldx, const void* wblob, void* act, void* stream);
+
+/* Per forward, kernel 2 ("W4A4 CUDA Kernel for Voice Clone", section 3.7;
+ * affine: Blackwell article, section 1): Y = a * (int4 GEMM with per-group
+ * fp32 dequant + lora_act L_up^T) + b, rounded to fp16.
+ * act from w4a4_quantize_act with the same (M, K, R); wblob from
+ * w4a4_pack_weights with the same (N, K, R).
+ * y: fp16 [M][ldy], ldy >= N, ldy % 8 == 0, 16-byte aligned, not aliasing
+ * act or wblob.  Rows m >= M are never written. */
+int w4a4_linear(int64_t M, int64_t N, int64_t K, int32_t R, const void* act,
+                const void* wblob, uint16_t* y, int64_t ldy, void* stream);
+
+/* Which GEMM kernel w4a4_linear runs for a shape (host-only):
+ * 0 = generic, 1 = decode (M <= 16), 2 = prefill; -W4A4_ERR_SHAPE if the
+ * shape is unsupported.  Lets a caller log the kernel chosen per layer
+ * ("INT4 Kernel Architecture, in depth", section "Failure modes"). */
+int w4a4_query_variant(int64_t M, int64_t N, int64_t K, int32_t R);
+
+/* Diagnostic: the exact per-group integer sums P[m,n,g] of a window,
+ * computed by the GEMM's own unpack + integer MFMA path.
+ * out: int32 device buffer [mc][nc][K/64] (row-major).  m0, mc, n0, nc must be
+ * multiples of 16 with m0 + mc <= Mp and n0 + nc <= N. */
+int w4a4_debug_group_psums(int64_t M, int64_t N, int64_t K, int32_t R,
+                           const void* act, const void* wblob, int64_t m0,
+                           int64_t mc, int64_t n0, int64_t nc, int32_t* out,
+                           void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A4_H_ */

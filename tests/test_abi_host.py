@@ -1,0 +1,103 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+declared in include/w4a4.h, reports blob sizes, and rejects bad arguments on
+the host before anything is enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import w4a4_gemm_lora_amd as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+pytestmark = pytest.mark.skipif(not os.path.exists(W.lib_path()),
+                                reason="libw4a4.so not built (run __graft_entry__.build())")
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "w4a4.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(w4a4_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    lib = W.load_library()
+    names = _declared()
+    assert set(names) == set(W.EXPORTED_SYMBOLS), names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert W.w4a4_status_string(0) == "W4A4_OK"
+    assert "SHAPE" in W.w4a4_status_string(2)
+
+
+def test_layout_sizes():
+    N, K, R = 3072, 1024, 32
+    tot, offs = W.w4a4_weight_layout(N, K, R)
+    assert offs[0] == 0 and all(o % 256 == 0 for o in offs)
+    assert offs[1] >= K * R * 2
+    assert offs[2] - offs[1] >= N * K // 2
+    assert offs[3] - offs[2] >= N * (K // 64) * 2
+    assert offs[4] - offs[3] >= N * R * 2
+    assert tot >= offs[5] + 4 * N
+    tot, offs = W.w4a4_act_layout(700, K, R)
+    Mp = 704
+    assert offs[1] - offs[0] >= Mp * K // 2
+    assert offs[2] - offs[1] >= Mp * (K // 64) * 2
+    assert tot >= offs[2] + Mp * R * 4
+
+
+@pytest.mark.parametrize("N,K,R", [(16, 64, 16), (16, 192, 16), (8, 128, 16), (24, 128, 16),
+                                   (16, 128, 8), (16, 128, 80), (16, 128, -16), (0, 128, 16)])
+def test_bad_shapes_rejected(N, K, R):
+    with pytest.raises(W.W4A4Error) as e:
+        W.w4a4_weight_layout(N, K, R)
+    assert e.value.status == 2
+    assert W.load_library().w4a4_query_variant(1, N, K, R) == -2
+
+
+def _lib():
+    return W.load_library()
+
+
+FAKE = 1 << 20  # a non-NULL, 256-byte aligned host address; never dereferenced
+
+
+def test_validation_errors_before_any_launch():
+    lib = _lib()
+    # linear: NULL y, misaligned y, ldy < N, bad ldy, bad shape
+    assert lib.w4a4_linear(4, 64, 128, 16, FAKE, FAKE, None, 64, None) == 1
+    assert lib.w4a4_linear(4, 64, 128, 16, FAKE, FAKE, FAKE + 2, 64, None) == 3
+    assert lib.w4a4_linear(4, 64, 128, 16, FAKE, FAKE, FAKE, 32, None) == 2
+    assert lib.w4a4_linear(4, 64, 128, 16, FAKE, FAKE, FAKE, 68, None) == 3
+    assert lib.w4a4_linear(4, 64, 100, 16, FAKE, FAKE, FAKE, 64, None) == 2
+    assert lib.w4a4_linear(4, 64, 128, 16, None, FAKE, FAKE, 64, None) == 1
+    assert lib.w4a4_linear(4, 64, 128, 16, FAKE + 16, FAKE, FAKE * 4, 64, None) == 3
+    # y overlapping a blob
+    assert lib.w4a4_linear(4, 64, 128, 16, FAKE, FAKE * 4, FAKE, 64, None) == 4
+    # M == 0 is a no-op success; negative M is a shape error
+    assert lib.w4a4_linear(0, 64, 128, 16, None, None, None, 64, None) == 0
+    assert lib.w4a4_linear(-1, 64, 128, 16, FAKE, FAKE, FAKE, 64, None) == 2
+    # quantize: ldx < K, misaligned x, NULL act, missing weight blob with R > 0
+    assert lib.w4a4_quantize_act(4, 128, 16, FAKE, 64, FAKE, FAKE, None) == 2
+    assert lib.w4a4_quantize_act(4, 128, 16, FAKE + 8, 128, FAKE, FAKE, None) == 3
+    assert lib.w4a4_quantize_act(4, 128, 16, FAKE, 130, FAKE, FAKE, None) == 3
+    assert lib.w4a4_quantize_act(4, 128, 16, FAKE, 128, FAKE, None, None) == 1
+    assert lib.w4a4_quantize_act(4, 128, 16, FAKE, 128, None, FAKE, None) == 1
+    assert lib.w4a4_quantize_act(0, 128, 16, None, 128, None, None, None) == 0
+    # pack: both or neither code source, half a checkpoint pair, missing LoRA
+    assert lib.w4a4_pack_weights(16, 128, 16, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None) == 4
+    assert lib.w4a4_pack_weights(16, 128, 16, None, None, None, FAKE, FAKE, None, None, FAKE, None) == 4
+    assert lib.w4a4_pack_weights(16, 128, 16, None, FAKE, None, FAKE, FAKE, None, None, FAKE, None) == 1
+    assert lib.w4a4_pack_weights(16, 128, 16, FAKE, None, None, None, FAKE, None, None, FAKE, None) == 1
+    assert lib.w4a4_pack_weights(16, 128, 16, FAKE, None, None, FAKE, FAKE, None, None, FAKE + 16, None) == 3
+    assert lib.w4a4_pack_weights(16, 128, 16, FAKE, None, None, FAKE, FAKE, None, None, None, None) == 1
+    # debug psums: window not on 16 boundaries / outside
+    assert lib.w4a4_debug_group_psums(20, 64, 128, 16, FAKE, FAKE, 8, 16, 0, 16, FAKE, None) == 2
+    assert lib.w4a4_debug_group_psums(20, 64, 128, 16, FAKE, FAKE, 16, 32, 0, 16, FAKE, None) == 2
+    assert lib.w4a4_debug_group_psums(20, 64, 128, 16, FAKE, FAKE, 0, 16, 64, 16, FAKE, None) == 2
+
+
+def test_query_variant_is_host_only():
+    for M in (1, 4, 16, 700, 8192):
+        assert W.w4a4_query_variant(M, 4096, 4096, 32) in (0, 1, 2)

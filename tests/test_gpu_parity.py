@@ -1,0 +1,303 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bar: packed codes, scales and per-group integer sums bit-exact; lora_act
+within 1e-4 * rms; Y within max|dY| <= 2e-2 * rms(Y_oracle) and
+mean|dY| <= 2e-3 * rms(Y_oracle).  Full-size workloads compare every output
+the oracle finishes in seconds and sampled windows of the largest one.
+"""
+import json
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import w4a4_gemm_lora_amd as W
+from w4a4_gemm_lora_amd import workloads
+from oracle import w4a4_oracle as O
+from tests.layout_unpack import split_act_blob, split_weight_blob
+
+pytestmark = pytest.mark.gpu
+
+MAX_TOL = 2e-2
+MEAN_TOL = 2e-3
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _torch():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU test run without a GPU")
+    return torch
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _to_dev(a):
+    torch = _torch()
+    if a is None:
+        return None
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+class GpuRun:
+    """Pack, quantize and run one layer on the GPU; keep host copies."""
+
+    def __init__(self, case, use_qweight=False, ldx=None, ldy=None, R=None):
+        torch = _torch()
+        self.M, self.K, self.N = case["M"], case["K"], case["N"]
+        self.R = case["R"] if R is None else R
+        M, K, N, R = self.M, self.K, self.N, self.R
+        self.ldx = K if ldx is None else ldx
+        self.ldy = N if ldy is None else ldy
+        self.wblob = W.alloc_weight_blob(N, K, R)
+        self.wblob.fill_(0xA5)   # garbage: every byte the packer owns must be written
+        kw = dict(lora_down=_to_dev(case["lora_down"]) if R else None,
+                  lora_up=_to_dev(case["lora_up"]) if R else None,
+                  col_scale=_to_dev(case.get("col_scale")), bias=_to_dev(case.get("bias")))
+        if use_qweight:
+            W.w4a4_pack_weights(N, K, R, self.wblob, qweight=_to_dev(case["qweight"]),
+                                w_scales=_to_dev(case["w_scales"]), **kw)
+        else:
+            W.w4a4_pack_weights(N, K, R, self.wblob, w_fp16=_to_dev(case["w"]), **kw)
+        xs = np.zeros((max(M, 1), self.ldx), np.float16)
+        xs[:M, :K] = case["x"]
+        self.x = _to_dev(xs)
+        self.act = W.alloc_act_blob(M, K, R)
+        self.act.fill_(0x5A)
+        W.w4a4_quantize_act(M, K, R, self.x, self.wblob, self.act, ldx=self.ldx)
+        self.y = torch.full((max(M, 1), self.ldy), float("nan"), dtype=torch.float16, device="cuda")
+        W.w4a4_linear(M, N, K, R, self.act, self.wblob, self.y, ldy=self.ldy)
+        torch.cuda.synchronize()
+
+    def host_act(self):
+        _, offs = W.w4a4_act_layout(self.M, self.K, self.R)
+        return split_act_blob(self.act.cpu().numpy(), self.M, self.K, self.R, offs)
+
+    def host_weights(self):
+        _, offs = W.w4a4_weight_layout(self.N, self.K, self.R)
+        return split_weight_blob(self.wblob.cpu().numpy(), self.N, self.K, self.R, offs)
+
+    def host_y(self):
+        return self.y.cpu().numpy()
+
+    def psums(self, m0, mc, n0, nc):
+        torch = _torch()
+        out = torch.zeros((mc, nc, self.K // 64), dtype=torch.int32, device="cuda")
+        W.w4a4_debug_group_psums(self.M, self.N, self.K, self.R, self.act, self.wblob, m0, mc, n0, nc, out)
+        torch.cuda.synchronize()
+        return out.cpu().numpy()
+
+
+def _check_y(y_gpu, y_ref, what):
+    yg = y_gpu.astype(np.float64)
+    yr = y_ref.astype(np.float64)
+    assert np.all(np.isfinite(yg)), f"{what}: non-finite output"
+    rms = np.sqrt(np.mean(yr ** 2))
+    err = np.abs(yg - yr)
+    _say(f"{what}: rms={rms:.4g} max|dY|/rms={err.max() / rms:.3g} mean|dY|/rms={err.mean() / rms:.3g}")
+    assert err.max() <= MAX_TOL * rms, f"{what}: max err {err.max()} > {MAX_TOL}*{rms}"
+    assert err.mean() <= MEAN_TOL * rms, f"{what}: mean err {err.mean()} > {MEAN_TOL}*{rms}"
+
+
+def _check_quant(run, case, ref_qx, ref_sx):
+    a = run.host_act()
+    M = run.M
+    assert np.array_equal(a["qx"][:M], ref_qx), "X codes differ"
+    assert np.array_equal(a["sx"][:M].view(np.uint16), ref_sx.view(np.uint16)), "X scales differ"
+    assert not np.any(a["qx"][M:]) and not np.any(a["sx"][M:].view(np.uint16)), "padding rows not zero"
+    return a
+
+
+def _check_weights(run, case, ref_qw, ref_sw):
+    w = run.host_weights()
+    assert np.array_equal(w["qw"], ref_qw), "W codes differ"
+    assert np.array_equal(w["sw"].view(np.uint16), ref_sw.view(np.uint16)), "W scales differ"
+    if run.R:
+        assert np.array_equal(w["lora_down"].view(np.uint16), case["lora_down"].view(np.uint16))
+        assert np.array_equal(w["lora_up"].view(np.uint16), case["lora_up"].view(np.uint16))
+    a_ref = case["col_scale"] if case.get("col_scale") is not None else np.ones(run.N, np.float32)
+    b_ref = case["bias"] if case.get("bias") is not None else np.zeros(run.N, np.float32)
+    assert np.array_equal(w["a"], a_ref) and np.array_equal(w["b"], b_ref)
+    return w
+
+
+def _check_lora_act(a, ref_la, M):
+    if ref_la is None or ref_la.shape[1] == 0:
+        return
+    got = a["lora_act"][:M].astype(np.float64)
+    rms = np.sqrt(np.mean(ref_la ** 2)) + 1e-30
+    d = np.abs(got - ref_la).max()
+    _say(f"lora_act max|d|/rms = {d / rms:.3g}")
+    assert d <= 1e-4 * rms
+    assert not np.any(a["lora_act"][M:]), "padding lora_act rows not zero"
+
+
+# ---------------------------------------------------------------------------
+def test_quantizer_golden_groups_on_gpu():
+    cases = json.load(open(os.path.join(GOLDEN, "quantize_cases.json")))["groups"]
+    K = 128
+    x = np.zeros((len(cases), K), np.float16)
+    want_q = np.zeros((len(cases), K), np.int8)
+    for i, c in enumerate(cases):
+        x[i, : len(c["x"])] = c["x"]
+        want_q[i, : len(c["q"])] = c["q"]
+        # second group: the same values negated
+        x[i, 64: 64 + len(c["x"])] = -np.array(c["x"], np.float16)
+    torch = _torch()
+    M = len(cases)
+    act = W.alloc_act_blob(M, K, 0)
+    W.w4a4_quantize_act(M, K, 0, _to_dev(x), None, act)
+    torch.cuda.synchronize()
+    _, offs = W.w4a4_act_layout(M, K, 0)
+    a = split_act_blob(act.cpu().numpy(), M, K, 0, offs)
+    for i, c in enumerate(cases):
+        assert a["qx"][i, :64].tolist() == want_q[i, :64].tolist(), c["name"]
+        assert int(a["sx"][i, 0].view(np.uint16)) == c["s_bits"], c["name"]
+        assert int(a["sx"][i, 1].view(np.uint16)) == c["s_bits"], c["name"]
+    # the negated group matches the oracle (the clamp makes -x asymmetric at +-8.5)
+    qx, sx = O.quantize_groups(x)
+    assert np.array_equal(a["qx"][:M], qx)
+
+
+WORKLOAD_CASES = ["small", "mlp_up", "mlp_down", "decode-1", "decode-4", "decode-16"]
+
+
+def _workload(name):
+    if name.startswith("decode-"):
+        return workloads.generate("decode", M=int(name.split("-")[1]))
+    return workloads.generate(name)
+
+
+@pytest.mark.parametrize("name", WORKLOAD_CASES)
+def test_workload_parity_full_output(name):
+    case = _workload(name)
+    _say(f"[parity] {name} M={case['M']} K={case['K']} N={case['N']} R={case['R']}")
+    run = GpuRun(case)
+    ref = O.linear(case["x"], case["lora_down"], case["lora_up"], case["col_scale"], case["bias"], w16=case["w"])
+    a = _check_quant(run, case, ref["qx"], ref["sx"])
+    _check_weights(run, case, ref["qw"], ref["sw"])
+    _check_lora_act(a, ref["lora_act"], run.M)
+    _check_y(run.host_y()[: run.M, : run.N], ref["y"], name)
+    # exact per-group integer sums: whole output for the small case, windows otherwise
+    Mp = (run.M + 15) // 16 * 16
+    if name == "small":
+        wins = [(0, Mp, 0, run.N)]
+    else:
+        wins = [(0, 16, 0, 32), (Mp - 16, 16, run.N - 48, 48), (Mp // 32 * 16, 16, run.N // 32 * 16, 64)]
+    for m0, mc, n0, nc in wins:
+        got = run.psums(m0, mc, n0, nc)
+        rows = np.arange(m0, min(m0 + mc, run.M))
+        P = O.group_psums(ref["qx"][rows], ref["qw"][n0: n0 + nc])
+        assert np.array_equal(got[: len(rows)], P), (name, m0, n0)
+        assert not np.any(got[len(rows):]), "psums of padding rows must be 0"
+
+
+def test_prefill_parity_sampled():
+    case = workloads.generate("prefill")
+    M, K, N = case["M"], case["K"], case["N"]
+    _say(f"[parity] prefill M={M} K={K} N={N} R={case['R']}")
+    run = GpuRun(case)
+    # bit-exact codes and scales over the whole of X and W
+    qx, sx = O.quantize_groups(case["x"])
+    qw, sw = O.quantize_groups(case["w"])
+    a = _check_quant(run, case, qx, sx)
+    _check_weights(run, case, qw, sw)
+    rng = np.random.default_rng(99)
+    rows = np.unique(np.concatenate([rng.choice(M - 16, 48, replace=False), np.arange(M - 16, M)]))
+    cols = np.unique(np.concatenate([rng.choice(N - 16, 48, replace=False), np.arange(N - 16, N)]))
+    ref = O.linear(case["x"], case["lora_down"], case["lora_up"], case["col_scale"], case["bias"],
+                   w16=case["w"], rows=rows, cols=cols)
+    _check_lora_act(dict(lora_act=a["lora_act"][rows]), ref["lora_act"], len(rows))
+    y = run.host_y()
+    _check_y(y[np.ix_(rows, cols)], ref["y"], "prefill (sampled 64x64)")
+    for m0, n0 in [(0, 0), (M - 64, N - 64), (4096, 2048)]:
+        got = run.psums(m0, 64, n0, 64)
+        assert np.array_equal(got, O.group_psums(qx[m0: m0 + 64], qw[n0: n0 + 64])), (m0, n0)
+
+
+@pytest.mark.parametrize("M,K,N,R", [(1, 128, 16, 16), (17, 128, 48, 0), (33, 256, 64, 64),
+                                     (5, 384, 32, 48), (130, 512, 80, 32)])
+def test_ragged_and_rank_edges(M, K, N, R):
+    case = workloads.random_case(M, K, N, R, seed=1000 + M + K + R)
+    _say(f"[edge] M={M} K={K} N={N} R={R}")
+    run = GpuRun(case)
+    ref = O.linear(case["x"], case["lora_down"] if R else None, case["lora_up"] if R else None,
+                   case["col_scale"], case["bias"], w16=case["w"])
+    a = _check_quant(run, case, ref["qx"], ref["sx"])
+    _check_weights(run, case, ref["qw"], ref["sw"])
+    _check_lora_act(a, ref["lora_act"], M)
+    _check_y(run.host_y()[:M, :N], ref["y"], f"edge M={M} R={R}")
+    Mp = (M + 15) // 16 * 16
+    got = run.psums(0, Mp, 0, N)
+    assert np.array_equal(got[:M], O.group_psums(ref["qx"], ref["qw"]))
+    # rows >= M of y are never written
+    assert np.all(np.isnan(run.host_y()[M:].astype(np.float64)))
+
+
+def test_strided_x_and_y():
+    M, K, N, R = 40, 256, 64, 32
+    case = workloads.random_case(M, K, N, R, seed=7)
+    run = GpuRun(case, ldx=K + 64, ldy=N + 24)
+    ref = O.linear(case["x"], case["lora_down"], case["lora_up"], case["col_scale"], case["bias"], w16=case["w"])
+    _check_quant(run, case, ref["qx"], ref["sx"])
+    y = run.host_y()
+    _check_y(y[:, :N], ref["y"], "strided")
+    assert np.all(np.isnan(y[:, N:].astype(np.float64))), "columns beyond N were written"
+
+
+def test_checkpoint_codes_with_minus_eight():
+    """qweight/w_scales input (checkpoint layout), codes spanning -8..7."""
+    M, K, N, R = 24, 256, 32, 16
+    case = workloads.random_case(M, K, N, R, seed=11)
+    rng = np.random.default_rng(12)
+    q = rng.integers(-8, 8, size=(N, K))
+    q[0, :] = -8
+    nib = (q & 0xF).astype(np.uint8)
+    case["qweight"] = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    case["w_scales"] = (rng.uniform(0.001, 0.01, size=(N, K // 64))).astype(np.float16)
+    run = GpuRun(case, use_qweight=True)
+    ref = O.linear(case["x"], case["lora_down"], case["lora_up"], case["col_scale"], case["bias"],
+                   qweight=case["qweight"], w_scales=case["w_scales"])
+    assert np.array_equal(ref["qw"], q.astype(np.int8))
+    _check_weights(run, case, ref["qw"], ref["sw"])
+    _check_y(run.host_y()[:M], ref["y"], "checkpoint codes")
+    got = run.psums(0, 32, 0, N)
+    assert np.array_equal(got[:M], O.group_psums(ref["qx"], ref["qw"]))
+
+
+def test_extreme_rows_and_determinism():
+    """Zero rows, huge-magnitude rows, subnormal rows; two runs bit-identical."""
+    M, K, N, R = 48, 256, 64, 16
+    case = workloads.random_case(M, K, N, R, seed=13)
+    x = case["x"].astype(np.float64)
+    x[3] = 0.0
+    x[4] *= 8000.0
+    x[5] *= 2.0 ** -20
+    x[6, :64] = 0.0
+    x[7] = np.where(np.arange(K) % 64 == 0, 60000.0, x[7])
+    case["x"] = np.clip(x, -65504, 65504).astype(np.float16)
+    case["lora_down"] = (case["lora_down"].astype(np.float64) * 1e-3).astype(np.float16)
+    run = GpuRun(case)
+    ref = O.linear(case["x"], case["lora_down"], case["lora_up"], case["col_scale"], case["bias"], w16=case["w"])
+    _check_quant(run, case, ref["qx"], ref["sx"])
+    y1 = run.host_y().copy()
+    W.w4a4_quantize_act(M, K, R, run.x, run.wblob, run.act)
+    W.w4a4_linear(M, N, K, R, run.act, run.wblob, run.y)
+    _torch().cuda.synchronize()
+    assert np.array_equal(y1.view(np.uint16), run.host_y().view(np.uint16))
+    ok = np.ones(M, bool)
+    ok[4] = ok[7] = False    # outliers dominate the rms; checked separately below
+    _check_y(y1[ok], ref["y"][ok], "extreme rows (ordinary)")
+    for r in (4, 7):
+        _check_y(y1[r: r + 1], ref["y"][r: r + 1], f"extreme row {r}")
+
+
+def test_zero_rows_is_noop():
+    torch = _torch()
+    W.w4a4_quantize_act(0, 128, 16, None, None, None)
+    W.w4a4_linear(0, 16, 128, 16, None, None, None)
+    torch.cuda.synchronize()

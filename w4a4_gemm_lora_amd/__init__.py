@@ -1,0 +1,197 @@
+"""Python binding of libw4a4 (W4A4 linear layer with fused LoRA, gfx950).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+``libw4a4.so``.  PyTorch supplies device memory and the current stream.
+There is no fallback: if the library is missing, importing the binding's
+entry points raises.
+
+Names follow the C ABI in ``include/w4a4.h``::
+
+    w4a4_weight_layout(N, K, R)          -> (total_bytes, offsets[6])
+    w4a4_act_layout(M, K, R)             -> (total_bytes, offsets[3])
+    w4a4_pack_weights(N, K, R, wblob, w_fp16=..., or qweight=..., w_scales=...,
+                      lora_down=..., lora_up=..., col_scale=..., bias=...)
+    w4a4_quantize_act(M, K, R, x, wblob, act)
+    w4a4_linear(M, N, K, R, act, wblob, y)
+    w4a4_query_variant(M, N, K, R)
+    w4a4_debug_group_psums(M, N, K, R, act, wblob, m0, mc, n0, nc, out)
+
+plus helpers that allocate the blobs as uint8 CUDA tensors.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "W4A4Error", "lib_path", "load_library", "w4a4_status_string",
+    "w4a4_weight_layout", "w4a4_act_layout", "w4a4_pack_weights",
+    "w4a4_quantize_act", "w4a4_linear", "w4a4_query_variant",
+    "w4a4_debug_group_psums", "alloc_weight_blob", "alloc_act_blob",
+    "PackedLinear", "EXPORTED_SYMBOLS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+EXPORTED_SYMBOLS = (
+    "w4a4_status_string", "w4a4_weight_layout", "w4a4_act_layout",
+    "w4a4_pack_weights", "w4a4_quantize_act", "w4a4_linear",
+    "w4a4_query_variant", "w4a4_debug_group_psums",
+)
+
+
+class W4A4Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {w4a4_status_string(status)} (status {status})")
+        self.status = status
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "libw4a4.so")
+
+
+_LIB = None
+
+_i64, _i32, _vp, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libw4a4.so from the package directory (raises if it is not built)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = lib_path()
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -m w4a4_gemm_lora_amd.build`")
+    lib = ctypes.CDLL(path)
+    lib.w4a4_status_string.restype = ctypes.c_char_p
+    lib.w4a4_status_string.argtypes = [ctypes.c_int]
+    lib.w4a4_weight_layout.argtypes = [_i64, _i64, _i32, ctypes.POINTER(_sz), ctypes.POINTER(_sz)]
+    lib.w4a4_act_layout.argtypes = [_i64, _i64, _i32, ctypes.POINTER(_sz), ctypes.POINTER(_sz)]
+    lib.w4a4_pack_weights.argtypes = [_i64, _i64, _i32] + [_vp] * 9
+    lib.w4a4_quantize_act.argtypes = [_i64, _i64, _i32, _vp, _i64, _vp, _vp, _vp]
+    lib.w4a4_linear.argtypes = [_i64, _i64, _i64, _i32, _vp, _vp, _vp, _i64, _vp]
+    lib.w4a4_query_variant.argtypes = [_i64, _i64, _i64, _i32]
+    lib.w4a4_debug_group_psums.argtypes = [_i64, _i64, _i64, _i32, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp]
+    for name in EXPORTED_SYMBOLS:
+        if name != "w4a4_status_string":
+            getattr(lib, name).restype = ctypes.c_int
+    _LIB = lib
+    return lib
+
+
+def w4a4_status_string(status: int) -> str:
+    return load_library().w4a4_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise W4A4Error(status, what)
+
+
+def _ptr(t):
+    """Device pointer of a tensor (or None)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("device tensors are required")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+# ---- host-only queries -------------------------------------------------------
+def w4a4_weight_layout(N: int, K: int, R: int):
+    lib = load_library()
+    tot = _sz()
+    offs = (_sz * 6)()
+    _check(lib.w4a4_weight_layout(N, K, R, ctypes.byref(tot), offs), "w4a4_weight_layout")
+    return tot.value, list(offs)
+
+
+def w4a4_act_layout(M: int, K: int, R: int):
+    lib = load_library()
+    tot = _sz()
+    offs = (_sz * 3)()
+    _check(lib.w4a4_act_layout(M, K, R, ctypes.byref(tot), offs), "w4a4_act_layout")
+    return tot.value, list(offs)
+
+
+def w4a4_query_variant(M: int, N: int, K: int, R: int) -> int:
+    v = load_library().w4a4_query_variant(M, N, K, R)
+    if v < 0:
+        raise W4A4Error(-v, "w4a4_query_variant")
+    return v
+
+
+# ---- device calls -------------------------------------------------------------
+def w4a4_pack_weights(N, K, R, wblob, w_fp16=None, qweight=None, w_scales=None,
+                      lora_down=None, lora_up=None, col_scale=None, bias=None, stream=None):
+    st = load_library().w4a4_pack_weights(
+        N, K, R, _ptr(w_fp16), _ptr(qweight), _ptr(w_scales), _ptr(lora_down),
+        _ptr(lora_up), _ptr(col_scale), _ptr(bias), _ptr(wblob), _stream(stream))
+    _check(st, "w4a4_pack_weights")
+
+
+def w4a4_quantize_act(M, K, R, x, wblob, act, ldx=None, stream=None):
+    ldx = K if ldx is None else ldx
+    st = load_library().w4a4_quantize_act(M, K, R, _ptr(x), ldx, _ptr(wblob), _ptr(act), _stream(stream))
+    _check(st, "w4a4_quantize_act")
+
+
+def w4a4_linear(M, N, K, R, act, wblob, y, ldy=None, stream=None):
+    ldy = N if ldy is None else ldy
+    st = load_library().w4a4_linear(M, N, K, R, _ptr(act), _ptr(wblob), _ptr(y), ldy, _stream(stream))
+    _check(st, "w4a4_linear")
+
+
+def w4a4_debug_group_psums(M, N, K, R, act, wblob, m0, mc, n0, nc, out, stream=None):
+    st = load_library().w4a4_debug_group_psums(M, N, K, R, _ptr(act), _ptr(wblob), m0, mc, n0, nc,
+                                               _ptr(out), _stream(stream))
+    _check(st, "w4a4_debug_group_psums")
+
+
+# ---- allocation helpers (torch owns the memory) ------------------------------
+def alloc_weight_blob(N, K, R, device="cuda"):
+    import torch
+    total, _ = w4a4_weight_layout(N, K, R)
+    return torch.empty(total, dtype=torch.uint8, device=device)
+
+
+def alloc_act_blob(M, K, R, device="cuda"):
+    import torch
+    total, _ = w4a4_act_layout(M, K, R)
+    return torch.empty(total, dtype=torch.uint8, device=device)
+
+
+class PackedLinear:
+    """One packed layer: holds the weight blob and runs the two forward calls
+    (quantize_act, then linear) on the current stream."""
+
+    def __init__(self, N, K, R, w_fp16=None, qweight=None, w_scales=None,
+                 lora_down=None, lora_up=None, col_scale=None, bias=None):
+        self.N, self.K, self.R = int(N), int(K), int(R)
+        self.wblob = alloc_weight_blob(self.N, self.K, self.R, device=(
+            w_fp16 if w_fp16 is not None else qweight).device)
+        w4a4_pack_weights(self.N, self.K, self.R, self.wblob, w_fp16=w_fp16, qweight=qweight,
+                          w_scales=w_scales, lora_down=lora_down, lora_up=lora_up,
+                          col_scale=col_scale, bias=bias)
+
+    def forward(self, x, act=None, y=None):
+        import torch
+        M = x.shape[0]
+        if act is None:
+            act = alloc_act_blob(M, self.K, self.R, device=x.device)
+        if y is None:
+            y = torch.empty((M, self.N), dtype=torch.float16, device=x.device)
+        w4a4_quantize_act(M, self.K, self.R, x, self.wblob, act)
+        w4a4_linear(M, self.N, self.K, self.R, act, self.wblob, y)
+        return y

@@ -1,0 +1,233 @@
+// C ABI of libw4a4 (declared in include/w4a4.h): argument validation on the
+// host, blob geometry, kernel selection and launches on the caller's stream.
+// Validation runs before any HIP call, so every error path is testable
+// without a GPU, and nothing is enqueued when a call fails.
+#include "w4a4.h"
+
+#include <cstdio>
+#include <cstdlib>
+
+#include "w4a4_internal.hpp"
+
+using namespace w4a4;
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_nkr(int64_t N, int64_t K, int32_t R) {
+  if (K < kKPair || K % kKPair != 0) return W4A4_ERR_SHAPE;
+  if (N < 16 || N % 16 != 0) return W4A4_ERR_SHAPE;
+  if (R < 0 || R > kMaxRank || R % 16 != 0) return W4A4_ERR_SHAPE;
+  // 32-bit grid dimensions and code tile counts
+  if (N / 16 > (int64_t)1 << 30 || K > (int64_t)1 << 24) return W4A4_ERR_SHAPE;
+  return W4A4_OK;
+}
+
+int check_m(int64_t M) {
+  if (M < 0 || M > ((int64_t)1 << 30)) return W4A4_ERR_SHAPE;
+  return W4A4_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? W4A4_OK : W4A4_ERR_HIP; }
+
+bool log_enabled() {
+  static const bool on = [] {
+    const char* v = std::getenv("W4A4_LOG");
+    return v && v[0] && v[0] != '0';
+  }();
+  return on;
+}
+
+const char* variant_name(int v) {
+  switch (v) {
+    case kDecode: return "decode";
+    case kPrefill: return "prefill";
+    default: return "generic";
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* w4a4_status_string(int status) {
+  switch (status) {
+    case W4A4_OK: return "W4A4_OK";
+    case W4A4_ERR_NULL: return "W4A4_ERR_NULL: a required pointer is NULL";
+    case W4A4_ERR_SHAPE: return "W4A4_ERR_SHAPE: unsupported shape";
+    case W4A4_ERR_ALIGN: return "W4A4_ERR_ALIGN: misaligned pointer or leading dimension";
+    case W4A4_ERR_ARG: return "W4A4_ERR_ARG: inconsistent arguments";
+    case W4A4_ERR_HIP: return "W4A4_ERR_HIP: HIP runtime error";
+    default: return "W4A4: unknown status";
+  }
+}
+
+int w4a4_weight_layout(int64_t N, int64_t K, int32_t R, size_t* total_bytes, size_t* offsets) {
+  if (!total_bytes) return W4A4_ERR_NULL;
+  int st = check_nkr(N, K, R);
+  if (st) return st;
+  WeightGeom g = weight_geom(N, K, R);
+  *total_bytes = g.total;
+  if (offsets) {
+    offsets[0] = g.off_ldown;
+    offsets[1] = g.off_wq;
+    offsets[2] = g.off_sw;
+    offsets[3] = g.off_lup;
+    offsets[4] = g.off_a;
+    offsets[5] = g.off_b;
+  }
+  return W4A4_OK;
+}
+
+int w4a4_act_layout(int64_t M, int64_t K, int32_t R, size_t* total_bytes, size_t* offsets) {
+  if (!total_bytes) return W4A4_ERR_NULL;
+  int st = check_nkr(16, K, R);
+  if (st) return st;
+  if ((st = check_m(M))) return st;
+  ActGeom g = act_geom(M, K, R);
+  *total_bytes = g.total;
+  if (offsets) {
+    offsets[0] = g.off_xq;
+    offsets[1] = g.off_sx;
+    offsets[2] = g.off_la;
+  }
+  return W4A4_OK;
+}
+
+int w4a4_pack_weights(int64_t N, int64_t K, int32_t R, const uint16_t* w_fp16,
+                      const uint8_t* qweight, const uint16_t* w_scales,
+                      const uint16_t* lora_down, const uint16_t* lora_up,
+                      const float* col_scale, const float* bias, void* wblob,
+                      void* stream) {
+  int st = check_nkr(N, K, R);
+  if (st) return st;
+  if (!wblob) return W4A4_ERR_NULL;
+  const bool have_w = w_fp16 != nullptr;
+  const bool have_q = qweight != nullptr || w_scales != nullptr;
+  if (have_w == have_q) return W4A4_ERR_ARG;
+  if (have_q && (!qweight || !w_scales)) return W4A4_ERR_NULL;
+  if (R > 0 && (!lora_down || !lora_up)) return W4A4_ERR_NULL;
+  if (!aligned(wblob, 256)) return W4A4_ERR_ALIGN;
+  if (have_w && !aligned(w_fp16, 16)) return W4A4_ERR_ALIGN;
+  if (have_q && !aligned(w_scales, 2)) return W4A4_ERR_ALIGN;
+  if (R > 0 && (!aligned(lora_down, 2) || !aligned(lora_up, 2))) return W4A4_ERR_ALIGN;
+  if ((col_scale && !aligned(col_scale, 4)) || (bias && !aligned(bias, 4))) return W4A4_ERR_ALIGN;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  WeightGeom g = weight_geom(N, K, R);
+  uint8_t* base = static_cast<uint8_t*>(wblob);
+  uint8_t* wq = base + g.off_wq;
+  uint16_t* sw = reinterpret_cast<uint16_t*>(base + g.off_sw);
+  hipError_t e;
+  if (have_w)
+    e = launch_quantize_rows(w_fp16, K, N, N, K, 0, nullptr, wq, sw, nullptr, s);
+  else
+    e = launch_repack_qweight(qweight, w_scales, N, K, wq, sw, s);
+  if (e != hipSuccess) return W4A4_ERR_HIP;
+  e = launch_pack_lora(lora_down, lora_up, N, K, R,
+                       reinterpret_cast<uint16_t*>(base + g.off_ldown),
+                       reinterpret_cast<uint16_t*>(base + g.off_lup), s);
+  if (e != hipSuccess) return W4A4_ERR_HIP;
+  e = launch_pack_affine(col_scale, bias, N, reinterpret_cast<float*>(base + g.off_a),
+                         reinterpret_cast<float*>(base + g.off_b), s);
+  return hip_status(e);
+}
+
+int w4a4_quantize_act(int64_t M, int64_t K, int32_t R, const uint16_t* x, int64_t ldx,
+                      const void* wblob, void* act, void* stream) {
+  int st = check_nkr(16, K, R);
+  if (st) return st;
+  if ((st = check_m(M))) return st;
+  if (M == 0) return W4A4_OK;
+  if (!x || !act || (R > 0 && !wblob)) return W4A4_ERR_NULL;
+  if (ldx < K) return W4A4_ERR_SHAPE;
+  if (ldx % 8 != 0 || !aligned(x, 16) || !aligned(act, 256) || (wblob && !aligned(wblob, 256)))
+    return W4A4_ERR_ALIGN;
+  ActGeom g = act_geom(M, K, R);
+  uint8_t* base = static_cast<uint8_t*>(act);
+  const uint16_t* ldown = R > 0 ? reinterpret_cast<const uint16_t*>(
+                                      static_cast<const uint8_t*>(wblob) + weight_geom(16, K, R).off_ldown)
+                                : nullptr;
+  hipError_t e = launch_quantize_rows(x, ldx, M, g.Mp, K, R, ldown, base + g.off_xq,
+                                      reinterpret_cast<uint16_t*>(base + g.off_sx),
+                                      reinterpret_cast<float*>(base + g.off_la),
+                                      reinterpret_cast<hipStream_t>(stream));
+  return hip_status(e);
+}
+
+static int make_gemm_args(int64_t M, int64_t N, int64_t K, int32_t R, const void* act,
+                          const void* wblob, uint16_t* y, int64_t ldy, GemmArgs* a) {
+  int st = check_nkr(N, K, R);
+  if (st) return st;
+  if ((st = check_m(M))) return st;
+  if (!act || !wblob) return W4A4_ERR_NULL;
+  if (!aligned(act, 256) || !aligned(wblob, 256)) return W4A4_ERR_ALIGN;
+  ActGeom ag = act_geom(M, K, R);
+  WeightGeom wg = weight_geom(N, K, R);
+  const uint8_t* ab = static_cast<const uint8_t*>(act);
+  const uint8_t* wb = static_cast<const uint8_t*>(wblob);
+  a->xq = ab + ag.off_xq;
+  a->sx = reinterpret_cast<const uint16_t*>(ab + ag.off_sx);
+  a->la = reinterpret_cast<const float*>(ab + ag.off_la);
+  a->wq = wb + wg.off_wq;
+  a->sw = reinterpret_cast<const uint16_t*>(wb + wg.off_sw);
+  a->lup = reinterpret_cast<const uint16_t*>(wb + wg.off_lup);
+  a->ca = reinterpret_cast<const float*>(wb + wg.off_a);
+  a->cb = reinterpret_cast<const float*>(wb + wg.off_b);
+  a->y = y;
+  a->ldy = ldy;
+  a->M = M;
+  a->N = N;
+  a->K = K;
+  a->R = R;
+  // y must not overlap either blob
+  if (y) {
+    const uint8_t* yb = reinterpret_cast<const uint8_t*>(y);
+    const uint8_t* ye = yb + (size_t)(M > 0 ? (M - 1) * ldy + N : 0) * 2;
+    if ((yb < ab + ag.total && ab < ye) || (yb < wb + wg.total && wb < ye)) return W4A4_ERR_ARG;
+  }
+  return W4A4_OK;
+}
+
+int w4a4_linear(int64_t M, int64_t N, int64_t K, int32_t R, const void* act,
+                const void* wblob, uint16_t* y, int64_t ldy, void* stream) {
+  int st = check_nkr(N, K, R);
+  if (st) return st;
+  if ((st = check_m(M))) return st;
+  if (M == 0) return W4A4_OK;
+  if (!y) return W4A4_ERR_NULL;
+  if (ldy < N) return W4A4_ERR_SHAPE;
+  if (ldy % 8 != 0 || !aligned(y, 16)) return W4A4_ERR_ALIGN;
+  GemmArgs a;
+  if ((st = make_gemm_args(M, N, K, R, act, wblob, y, ldy, &a))) return st;
+  const int v = choose_variant(M, N, K, R);
+  if (log_enabled())
+    std::fprintf(stderr, "w4a4_linear M=%lld N=%lld K=%lld R=%d -> %s\n", (long long)M,
+                 (long long)N, (long long)K, R, variant_name(v));
+  return hip_status(launch_gemm(a, v, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int w4a4_query_variant(int64_t M, int64_t N, int64_t K, int32_t R) {
+  if (check_nkr(N, K, R) || check_m(M)) return -W4A4_ERR_SHAPE;
+  return choose_variant(M, N, K, R);
+}
+
+int w4a4_debug_group_psums(int64_t M, int64_t N, int64_t K, int32_t R, const void* act,
+                           const void* wblob, int64_t m0, int64_t mc, int64_t n0,
+                           int64_t nc, int32_t* out, void* stream) {
+  int st = check_nkr(N, K, R);
+  if (st) return st;
+  if ((st = check_m(M))) return st;
+  if (!out) return W4A4_ERR_NULL;
+  const int64_t Mp = round_up16(M);
+  if (m0 < 0 || n0 < 0 || mc <= 0 || nc <= 0 || m0 % 16 || n0 % 16 || mc % 16 || nc % 16 ||
+      m0 + mc > Mp || n0 + nc > N)
+    return W4A4_ERR_SHAPE;
+  if (!aligned(out, 4)) return W4A4_ERR_ALIGN;
+  GemmArgs a;
+  if ((st = make_gemm_args(M, N, K, R, act, wblob, nullptr, N, &a))) return st;
+  return hip_status(launch_group_psums(a, m0, mc, n0, nc, out, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

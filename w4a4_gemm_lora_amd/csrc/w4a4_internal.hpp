@@ -1,0 +1,106 @@
+// Internal definitions of libw4a4: blob geometry and kernel launchers.
+// The packed formats themselves are specified in include/w4a4.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace w4a4 {
+
+constexpr int kGroup = 64;        // quantization group along K
+constexpr int kKPair = 128;       // two groups: the unit of one 128-bit lane load
+constexpr int kTileRows = 16;     // rows per MFMA tile
+constexpr int kTileBytes = 1024;  // 16 rows x 128 k nibbles
+constexpr int kMaxRank = 64;
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+inline int64_t round_up16(int64_t x) { return (x + 15) / 16 * 16; }
+
+struct WeightGeom {
+  int64_t N, K;
+  int R;
+  size_t off_ldown, off_wq, off_sw, off_lup, off_a, off_b, total;
+};
+
+struct ActGeom {
+  int64_t M, Mp, K;
+  int R;
+  size_t off_xq, off_sx, off_la, total;
+};
+
+inline WeightGeom weight_geom(int64_t N, int64_t K, int R) {
+  WeightGeom g{};
+  g.N = N;
+  g.K = K;
+  g.R = R;
+  size_t o = 0;
+  g.off_ldown = o; o = align256(o + size_t(K) * R * 2);
+  g.off_wq = o;    o = align256(o + size_t(N) * K / 2);
+  g.off_sw = o;    o = align256(o + size_t(N) * (K / kGroup) * 2);
+  g.off_lup = o;   o = align256(o + size_t(N) * R * 2);
+  g.off_a = o;     o = align256(o + size_t(N) * 4);
+  g.off_b = o;     o = align256(o + size_t(N) * 4);
+  g.total = o;
+  return g;
+}
+
+inline ActGeom act_geom(int64_t M, int64_t K, int R) {
+  ActGeom g{};
+  g.M = M;
+  g.Mp = round_up16(M);
+  g.K = K;
+  g.R = R;
+  size_t o = 0;
+  g.off_xq = o; o = align256(o + size_t(g.Mp) * K / 2);
+  g.off_sx = o; o = align256(o + size_t(g.Mp) * (K / kGroup) * 2);
+  g.off_la = o; o = align256(o + size_t(g.Mp) * R * 4);
+  g.total = o;
+  return g;
+}
+
+// ---- launchers (defined in the .hip files; return hipError_t of the launch)
+// Quantize `rows` rows (padded up to a multiple of 16 with q=0, s=0) of an
+// fp16 matrix into codes/scales tiles; with R > 0 also lora_act = src L_down.
+hipError_t launch_quantize_rows(const uint16_t* src, int64_t ld, int64_t rows,
+                                int64_t rows_padded, int64_t K, int R,
+                                const uint16_t* ldown_packed, uint8_t* codes,
+                                uint16_t* scales, float* lora_act,
+                                hipStream_t stream);
+
+hipError_t launch_repack_qweight(const uint8_t* qweight, const uint16_t* w_scales,
+                                 int64_t N, int64_t K, uint8_t* codes,
+                                 uint16_t* scales, hipStream_t stream);
+
+hipError_t launch_pack_lora(const uint16_t* lora_down, const uint16_t* lora_up,
+                            int64_t N, int64_t K, int R, uint16_t* ldown_packed,
+                            uint16_t* lup_packed, hipStream_t stream);
+
+hipError_t launch_pack_affine(const float* col_scale, const float* bias, int64_t N,
+                              float* a, float* b, hipStream_t stream);
+
+struct GemmArgs {
+  const uint8_t* xq;
+  const uint16_t* sx;
+  const float* la;
+  const uint8_t* wq;
+  const uint16_t* sw;
+  const uint16_t* lup;
+  const float* ca;
+  const float* cb;
+  uint16_t* y;
+  int64_t ldy;
+  int64_t M, N, K;
+  int R;
+};
+
+enum Variant { kGeneric = 0, kDecode = 1, kPrefill = 2 };
+
+int choose_variant(int64_t M, int64_t N, int64_t K, int R);
+
+hipError_t launch_gemm(const GemmArgs& a, int variant, hipStream_t stream);
+
+hipError_t launch_group_psums(const GemmArgs& a, int64_t m0, int64_t mc, int64_t n0,
+                              int64_t nc, int32_t* out, hipStream_t stream);
+
+}  // namespace w4a4

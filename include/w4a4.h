@@ -56,7 +56,11 @@
  * Activation blob (w4a4_quantize_act writes it; offsets from w4a4_act_layout):
  *   [0] X_q:      [Mp/16][KP] tiles of 1024 bytes (rows = m)
  *   [1] s_x:      fp16, [Mp/16][KP][16][2]: entry (mt, p, i, h) = s_x[16mt+i][2p+h]
- *   [2] lora_act: fp32 [Mp][R], row-major
+ *   [2] lora_act: fp32 [S][Mp][R] row-major partial sums: partial j covers the
+ *       k-pairs [j*KP/S, (j+1)*KP/S) (integer division) and lora_act is their
+ *       sum taken in order j = 0..S-1.  S ("lora splits") depends only on
+ *       (M, K) and is reported by w4a4_act_layout: S = 1 for M > 16, else
+ *       S = clamp(KP / 4, 1, 8).
  */
 #ifndef W4A4_H_
 #define W4A4_H_
@@ -87,10 +91,11 @@ const char* w4a4_status_string(int status);
 int w4a4_weight_layout(int64_t N, int64_t K, int32_t R,
                        size_t* total_bytes, size_t* offsets);
 
-/* Sizes of the activation blob for M rows (host-only).  offsets[3] as above;
- * offsets may be NULL.  Errors as for w4a4_weight_layout. */
+/* Sizes of the activation blob for M rows (host-only).  offsets[3] as above
+ * and the number S of LoRA-down partial sums; offsets and lora_splits may be
+ * NULL.  Errors as for w4a4_weight_layout. */
 int w4a4_act_layout(int64_t M, int64_t K, int32_t R,
-                    size_t* total_bytes, size_t* offsets);
+                    size_t* total_bytes, size_t* offsets, int32_t* lora_splits);
 
 /* Offline weight preparation, once per layer ("W4A4 CUDA Kernel for Voice
  * Clone", section 2.3: repack the checkpoint into the kernel's layout once at

@@ -56,14 +56,20 @@ def split_weight_blob(blob, N, K, R, offsets):
     )
 
 
-def split_act_blob(blob, M, K, R, offsets):
+def split_act_blob(blob, M, K, R, offsets, splits=1):
+    """Sections of an activation blob; lora_act is the in-order sum of the
+    `splits` fp32 partials [splits][Mp][R]."""
     b = np.asarray(blob, np.uint8)
     o = offsets
     Mp = (M + 15) // 16 * 16
     G = K // 64
+    parts = b[o[2]: o[2] + splits * Mp * R * 4].view(np.float32).reshape(splits, Mp, R)
+    la = np.zeros((Mp, R), np.float32)
+    for j in range(splits):
+        la = (la + parts[j]).astype(np.float32)
     return dict(
         qx=unpack_codes(b[o[0]: o[0] + Mp * K // 2], Mp, K),
         sx=unpack_scales(b[o[1]: o[1] + Mp * G * 2], Mp, K),
-        lora_act=b[o[2]: o[2] + Mp * R * 4].view(np.float32).reshape(Mp, R),
+        lora_act=la, lora_parts=parts,
         Mp=Mp,
     )

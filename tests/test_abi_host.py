@@ -40,11 +40,24 @@ def test_layout_sizes():
     assert offs[3] - offs[2] >= N * (K // 64) * 2
     assert offs[4] - offs[3] >= N * R * 2
     assert tot >= offs[5] + 4 * N
-    tot, offs = W.w4a4_act_layout(700, K, R)
+    tot, offs, ks = W.w4a4_act_layout(700, K, R, with_splits=True)
     Mp = 704
     assert offs[1] - offs[0] >= Mp * K // 2
     assert offs[2] - offs[1] >= Mp * (K // 64) * 2
-    assert tot >= offs[2] + Mp * R * 4
+    assert ks == 1
+    assert tot >= offs[2] + ks * Mp * R * 4
+
+
+def test_lora_split_rule():
+    """S = 1 for M > 16, else clamp((K/128)/4, 1, 8) (the header's rule)."""
+    def rule(M, K):
+        if M > 16:
+            return 1
+        return min(max(1, (K // 128) // 4), 8)
+    for M in (1, 4, 16, 17, 100, 700, 4096, 8192):
+        for K in (128, 256, 512, 1024, 3072, 4096):
+            _, _, ks = W.w4a4_act_layout(M, K, 32, with_splits=True)
+            assert ks == rule(M, K), (M, K, ks)
 
 
 @pytest.mark.parametrize("N,K,R", [(16, 64, 16), (16, 192, 16), (8, 128, 16), (24, 128, 16),

@@ -74,8 +74,8 @@ class GpuRun:
         torch.cuda.synchronize()
 
     def host_act(self):
-        _, offs = W.w4a4_act_layout(self.M, self.K, self.R)
-        return split_act_blob(self.act.cpu().numpy(), self.M, self.K, self.R, offs)
+        _, offs, ks = W.w4a4_act_layout(self.M, self.K, self.R, with_splits=True)
+        return split_act_blob(self.act.cpu().numpy(), self.M, self.K, self.R, offs, ks)
 
     def host_weights(self):
         _, offs = W.w4a4_weight_layout(self.N, self.K, self.R)
@@ -126,14 +126,16 @@ def _check_weights(run, case, ref_qw, ref_sw):
 
 
 def _check_lora_act(a, ref_la, M):
+    """lora_act (the in-order sum of the partials) within 1e-4 * rms of the
+    oracle; every partial's padding rows are zero."""
     if ref_la is None or ref_la.shape[1] == 0:
         return
     got = a["lora_act"][:M].astype(np.float64)
     rms = np.sqrt(np.mean(ref_la ** 2)) + 1e-30
     d = np.abs(got - ref_la).max()
-    _say(f"lora_act max|d|/rms = {d / rms:.3g}")
+    _say(f"lora_act max|d|/rms = {d / rms:.3g} (partials: {a['lora_parts'].shape[0]})")
     assert d <= 1e-4 * rms
-    assert not np.any(a["lora_act"][M:]), "padding lora_act rows not zero"
+    assert not np.any(a["lora_parts"][:, M:]), "padding lora_act rows not zero"
 
 
 # ---------------------------------------------------------------------------
@@ -211,7 +213,8 @@ def test_prefill_parity_sampled():
     cols = np.unique(np.concatenate([rng.choice(N - 16, 48, replace=False), np.arange(N - 16, N)]))
     ref = O.linear(case["x"], case["lora_down"], case["lora_up"], case["col_scale"], case["bias"],
                    w16=case["w"], rows=rows, cols=cols)
-    _check_lora_act(dict(lora_act=a["lora_act"][rows]), ref["lora_act"], len(rows))
+    _check_lora_act(dict(lora_act=a["lora_act"][rows], lora_parts=a["lora_parts"][:, rows]),
+                    ref["lora_act"], len(rows))
     y = run.host_y()
     _check_y(y[np.ix_(rows, cols)], ref["y"], "prefill (sampled 64x64)")
     for m0, n0 in [(0, 0), (M - 64, N - 64), (4096, 2048)]:

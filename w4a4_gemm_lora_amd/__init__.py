@@ -8,7 +8,7 @@ entry points raises.
 Names follow the C ABI in ``include/w4a4.h``::
 
     w4a4_weight_layout(N, K, R)          -> (total_bytes, offsets[6])
-    w4a4_act_layout(M, K, R)             -> (total_bytes, offsets[3])
+    w4a4_act_layout(M, K, R)             -> (total_bytes, offsets[3][, lora splits])
     w4a4_pack_weights(N, K, R, wblob, w_fp16=..., or qweight=..., w_scales=...,
                       lora_down=..., lora_up=..., col_scale=..., bias=...)
     w4a4_quantize_act(M, K, R, x, wblob, act)
@@ -66,7 +66,8 @@ def load_library() -> ctypes.CDLL:
     lib.w4a4_status_string.restype = ctypes.c_char_p
     lib.w4a4_status_string.argtypes = [ctypes.c_int]
     lib.w4a4_weight_layout.argtypes = [_i64, _i64, _i32, ctypes.POINTER(_sz), ctypes.POINTER(_sz)]
-    lib.w4a4_act_layout.argtypes = [_i64, _i64, _i32, ctypes.POINTER(_sz), ctypes.POINTER(_sz)]
+    lib.w4a4_act_layout.argtypes = [_i64, _i64, _i32, ctypes.POINTER(_sz), ctypes.POINTER(_sz),
+                                    ctypes.POINTER(ctypes.c_int32)]
     lib.w4a4_pack_weights.argtypes = [_i64, _i64, _i32] + [_vp] * 9
     lib.w4a4_quantize_act.argtypes = [_i64, _i64, _i32, _vp, _i64, _vp, _vp, _vp]
     lib.w4a4_linear.argtypes = [_i64, _i64, _i64, _i32, _vp, _vp, _vp, _i64, _vp]
@@ -117,11 +118,16 @@ def w4a4_weight_layout(N: int, K: int, R: int):
     return tot.value, list(offs)
 
 
-def w4a4_act_layout(M: int, K: int, R: int):
+def w4a4_act_layout(M: int, K: int, R: int, with_splits: bool = False):
+    """(total_bytes, offsets[3]) or, with_splits=True, (total, offsets, S)
+    where S is the number of LoRA-down partial sums in section [2]."""
     lib = load_library()
     tot = _sz()
     offs = (_sz * 3)()
-    _check(lib.w4a4_act_layout(M, K, R, ctypes.byref(tot), offs), "w4a4_act_layout")
+    ks = ctypes.c_int32()
+    _check(lib.w4a4_act_layout(M, K, R, ctypes.byref(tot), offs, ctypes.byref(ks)), "w4a4_act_layout")
+    if with_splits:
+        return tot.value, list(offs), ks.value
     return tot.value, list(offs)
 
 

@@ -80,7 +80,8 @@ int w4a4_weight_layout(int64_t N, int64_t K, int32_t R, size_t* total_bytes, siz
   return W4A4_OK;
 }
 
-int w4a4_act_layout(int64_t M, int64_t K, int32_t R, size_t* total_bytes, size_t* offsets) {
+int w4a4_act_layout(int64_t M, int64_t K, int32_t R, size_t* total_bytes, size_t* offsets,
+                    int32_t* lora_splits) {
   if (!total_bytes) return W4A4_ERR_NULL;
   int st = check_nkr(16, K, R);
   if (st) return st;
@@ -92,6 +93,7 @@ int w4a4_act_layout(int64_t M, int64_t K, int32_t R, size_t* total_bytes, size_t
     offsets[1] = g.off_sx;
     offsets[2] = g.off_la;
   }
+  if (lora_splits) *lora_splits = g.ks;
   return W4A4_OK;
 }
 
@@ -121,7 +123,7 @@ int w4a4_pack_weights(int64_t N, int64_t K, int32_t R, const uint16_t* w_fp16,
   uint16_t* sw = reinterpret_cast<uint16_t*>(base + g.off_sw);
   hipError_t e;
   if (have_w)
-    e = launch_quantize_rows(w_fp16, K, N, N, K, 0, nullptr, wq, sw, nullptr, s);
+    e = launch_quantize_rows(w_fp16, K, N, N, K, 0, 1, nullptr, wq, sw, nullptr, s);
   else
     e = launch_repack_qweight(qweight, w_scales, N, K, wq, sw, s);
   if (e != hipSuccess) return W4A4_ERR_HIP;
@@ -149,7 +151,7 @@ int w4a4_quantize_act(int64_t M, int64_t K, int32_t R, const uint16_t* x, int64_
   const uint16_t* ldown = R > 0 ? reinterpret_cast<const uint16_t*>(
                                       static_cast<const uint8_t*>(wblob) + weight_geom(16, K, R).off_ldown)
                                 : nullptr;
-  hipError_t e = launch_quantize_rows(x, ldx, M, g.Mp, K, R, ldown, base + g.off_xq,
+  hipError_t e = launch_quantize_rows(x, ldx, M, g.Mp, K, R, g.ks, ldown, base + g.off_xq,
                                       reinterpret_cast<uint16_t*>(base + g.off_sx),
                                       reinterpret_cast<float*>(base + g.off_la),
                                       reinterpret_cast<hipStream_t>(stream));
@@ -181,6 +183,7 @@ static int make_gemm_args(int64_t M, int64_t N, int64_t K, int32_t R, const void
   a->N = N;
   a->K = K;
   a->R = R;
+  a->ks = ag.ks;
   // y must not overlap either blob
   if (y) {
     const uint8_t* yb = reinterpret_cast<const uint8_t*>(y);

@@ -12,8 +12,15 @@
 // v_mfma_i32_16x16x64_i8 once per (16x16 output tile, group) with a zero C,
 // which yields 256*P exactly.  The fp32 epilogue per group folds the 1/256
 // into the weight scale.  LoRA-up runs on v_mfma_f32_16x16x16_f16 with the
-// fp32 lora_act split into fp16 hi + lo parts, accumulating straight into the
-// main accumulator; the affine and the fp16 rounding follow in registers.
+// fp32 lora_act (the in-order sum of its partials) split into fp16 hi + lo
+// parts, accumulating straight into the main accumulator; the affine and the
+// fp16 rounding follow in registers.
+//
+// Cost model measured on MI355X: one v_mfma_i32_16x16x64_i8 occupies a SIMD
+// for ~16.5 cycles and a wave64 fp32 VALU op for ~2.6-2.9 cycles, and the two
+// barely overlap, so the per-group epilogue (convert, scale product, fma on
+// four accumulators per lane) costs about twice the MFMA itself.  Large-M
+// kernels are therefore bound by issue of MFMA + VALU, not by HBM.
 #include "device_common.hpp"
 #include "w4a4_internal.hpp"
 
@@ -120,7 +127,11 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         v4f la = v4f{0.f, 0.f, 0.f, 0.f};
-        if (mv[i]) la = *reinterpret_cast<const v4f*>(g.la + ((size_t)((mt0 + i) * 16 + col_l)) * R + t * 16 + c * 4);
+        if (mv[i]) {
+          const size_t mp = (size_t)round_up16(g.M);
+          for (int j = 0; j < g.ks; ++j)
+            la += *reinterpret_cast<const v4f*>(g.la + (j * mp + (size_t)((mt0 + i) * 16 + col_l)) * R + t * 16 + c * 4);
+        }
         split_f16(la, ahi[i], alo[i]);
       }
 #pragma unroll
@@ -159,6 +170,473 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Shared epilogue pieces
+// ---------------------------------------------------------------------------
+
+// lora_act fragment of one 16-row tile for rank tile t: lane (r, c) gets
+// lora_act[row0 + r][16t + 4c .. 16t + 4c + 3], the sum of the ks partials
+// taken in order.
+__device__ __forceinline__ v4f lora_frag(const GemmArgs& g, int64_t row0, int t, int lane) {
+  const int c = lane >> 4, r = lane & 15;
+  const size_t mp = (size_t)round_up16(g.M);
+  v4f l4 = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < g.ks; ++j)
+    l4 += *reinterpret_cast<const v4f*>(g.la + (j * mp + (size_t)(row0 + r)) * g.R + t * 16 + c * 4);
+  return l4;
+}
+
+// acc (one 16x16 output tile; lane holds rows 4c+ii, column lane&15) +=
+// lora_act (fp16 hi + lo) x L_up^T over RT rank tiles.
+template <int RT>
+__device__ __forceinline__ v4f lora_up_tile(v4f acc, const GemmArgs& g, int64_t row0, int64_t nt,
+                                            int lane) {
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    v4h hi, lo;
+    split_f16(lora_frag(g, row0, t, lane), hi, lo);
+    const v4h b = *reinterpret_cast<const v4h*>(g.lup + (((size_t)nt * RT + t) * 64 + lane) * 4);
+    acc = mfma_f16_16x16x16(hi, b, acc);
+    acc = mfma_f16_16x16x16(lo, b, acc);
+  }
+  return acc;
+}
+
+// Y[row, col] = fp16(a * acc + b) for the MV leading rows of each lane's four
+// (rows 4c + ii), column col0 + (lane & 15).
+template <int MV>
+__device__ __forceinline__ void store_tile(const GemmArgs& g, v4f acc, int64_t row0,
+                                           int64_t col0, float af, float bf, int lane) {
+  const int c = lane >> 4, r = lane & 15;
+  const int64_t col = col0 + r;
+#pragma unroll
+  for (int ii = 0; ii < MV; ++ii) {
+    const int64_t row = row0 + c * 4 + ii;
+    if (row < g.M) {
+      const _Float16 v = (_Float16)fmaf(af, acc[ii], bf);
+      g.y[row * g.ldy + col] = __builtin_bit_cast(uint16_t, v);
+    }
+  }
+}
+
+// One 64-group of one 16x16 tile: an i8 MFMA with a zero C (256 P exactly)
+// followed by acc += P * s_x * s_w / 256 for the MV leading accumulator rows.
+template <int MV>
+__device__ __forceinline__ v4f group_tile(v4f acc, uint32_t a0, uint32_t a1, uint32_t b0,
+                                          uint32_t b1, const float* sxf, float swf) {
+  const v4i P = mfma_i8_16x16x64(expand_group(a0, a1), expand_group(b0, b1), v4i{0, 0, 0, 0});
+#pragma unroll
+  for (int ii = 0; ii < MV; ++ii) acc[ii] = fmaf((float)P[ii], sxf[ii] * swf, acc[ii]);
+  return acc;
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits [3:0] and [15:14], expcnt [6:4] and lgkmcnt [11:8] left at
+// their maxima).
+#define W4A4_WAIT_VMCNT(n) \
+  __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
+
+// ---------------------------------------------------------------------------
+// Decode kernel (M <= 16): weight-streaming, HBM-bound.
+// One workgroup per 16-column tile; its 4 waves split K into contiguous
+// ranges of up to kDecodeBatch k-pairs at a time.  Per batch a wave first
+// copies the activation codes and scales of its range into LDS
+// (global_load_lds; they are shared by every workgroup and come from L2) and
+// then issues its weight and weight-scale loads (non-temporal: every weight
+// byte is used once).  A vmcnt wait that leaves the weight loads in flight
+// publishes the activation copies; the compiler's own waits then let k-pair u
+// start as soon as its weights arrive.  Everything the epilogue needs (LoRA
+// partial sums, L_up, a, b) is loaded before the stream, so the tail costs no
+// extra memory round trip.  Partial accumulators are summed in LDS in wave
+// order (deterministic).  MV = accumulator rows per lane that
+// hold valid output (for M <= 4 every valid row sits in lanes 0..15).
+// ---------------------------------------------------------------------------
+constexpr int kDecodeWaves = 4;
+constexpr int kDecodeBatch = 8;
+
+template <int MV, int RT>
+__global__ __launch_bounds__(256, 4) void gemm_decode_kernel(GemmArgs g) {
+  constexpr int RTL = RT > 0 ? RT : 1;
+  __shared__ __attribute__((aligned(1024))) uint8_t a_lds[kDecodeWaves][kDecodeBatch][kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_lds[kDecodeWaves][kTileBytes];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t nt = blockIdx.x;
+  const int64_t KP = g.K / kKPair;
+  const int64_t per = (KP + kDecodeWaves - 1) / kDecodeWaves;
+  const int64_t p0 = wave * per;
+  const int64_t p1 = p0 + per < KP ? p0 + per : KP;
+  const int c = lane >> 4, r = lane & 15;
+
+  // Epilogue prefetch, issued before the weight stream: wave w sums the LoRA
+  // partials j = w, w+4, ... (fixed order) of rows 0..15; wave 0 also takes
+  // the L_up fragments and the affine of its columns.
+  v4f lsum[RTL];
+  v4h lup[RTL];
+#pragma unroll
+  for (int t = 0; t < RTL; ++t) lsum[t] = v4f{0.f, 0.f, 0.f, 0.f};
+  float af = 0.f, bf = 0.f;
+  if constexpr (RT > 0) {
+    for (int j = wave; j < g.ks; j += kDecodeWaves)
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+        lsum[t] += *reinterpret_cast<const v4f*>(g.la + ((size_t)j * 16 + r) * g.R + t * 16 + c * 4);
+    if (wave == 0) {
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+        lup[t] = *reinterpret_cast<const v4h*>(g.lup + (((size_t)nt * RT + t) * 64 + lane) * 4);
+    }
+  }
+  if (wave == 0) {
+    af = g.ca[nt * 16 + r];
+    bf = g.cb[nt * 16 + r];
+  }
+
+  v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+  const uint8_t* wq = g.wq + (size_t)nt * KP * kTileBytes + lane * 16;
+  const uint16_t* sw = g.sw + (size_t)nt * KP * 32 + r * 2;
+  for (int64_t pb = p0; pb < p1; pb += kDecodeBatch) {
+#pragma unroll
+    for (int u = 0; u < kDecodeBatch; ++u) {
+      const int64_t p = pb + u < p1 ? pb + u : p1 - 1;
+      __builtin_amdgcn_global_load_lds(g.xq + (size_t)p * kTileBytes + lane * 16,
+                                       (lds_void*)&a_lds[wave][u][0], 16, 0, 0);
+    }
+    {
+      // activation scales: 64 B per k-pair; lane l fetches part (l & 3) of k-pair l / 4
+      int64_t p = pb + (lane >> 2);
+      p = p < p1 ? p : p1 - 1;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(g.sx) + (size_t)p * 64 + (lane & 3) * 16,
+                                       (lds_void*)&s_lds[wave][0], 16, 0, 0);
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    v4u braw[kDecodeBatch];
+    uint32_t swv[kDecodeBatch];
+#pragma unroll
+    for (int u = 0; u < kDecodeBatch; ++u) {
+      const int64_t p = pb + u < p1 ? pb + u : p1 - 1;   // clamped duplicates are skipped below
+      braw[u] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(wq + (size_t)p * kTileBytes));
+      swv[u] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(sw + (size_t)p * 32));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    W4A4_WAIT_VMCNT(2 * kDecodeBatch);   // everything older than the weight loads has landed
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int u = 0; u < kDecodeBatch; ++u) {
+      if (pb + u < p1) {
+        const v4u araw = *reinterpret_cast<const v4u*>(&a_lds[wave][u][lane * 16]);
+        const v8h sxv = *reinterpret_cast<const v8h*>(&s_lds[wave][u * 64 + c * 16]);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          float sxf[MV];
+#pragma unroll
+          for (int ii = 0; ii < MV; ++ii) sxf[ii] = (float)sxv[ii * 2 + h];
+          const float swf = half_bits_to_float((uint16_t)(swv[u] >> (16 * h))) * (1.0f / 256.0f);
+          acc = group_tile<MV>(acc, araw[2 * h], araw[2 * h + 1], braw[u][2 * h], braw[u][2 * h + 1], sxf, swf);
+        }
+      }
+    }
+  }
+
+  // cross-wave sums in LDS (reusing a_lds), added by wave 0 in wave order
+  __syncthreads();
+  v4f* red = reinterpret_cast<v4f*>(&a_lds[0][0][0]);   // [1 + RTL][waves][64]
+  red[wave * 64 + lane] = acc;
+#pragma unroll
+  for (int t = 0; t < RTL; ++t) red[((1 + t) * kDecodeWaves + wave) * 64 + lane] = lsum[t];
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w = 1; w < kDecodeWaves; ++w) acc += red[w * 64 + lane];
+  if constexpr (RT > 0) {
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      v4f l4 = red[((1 + t) * kDecodeWaves) * 64 + lane];
+#pragma unroll
+      for (int w = 1; w < kDecodeWaves; ++w) l4 += red[((1 + t) * kDecodeWaves + w) * 64 + lane];
+      v4h hi, lo;
+      split_f16(l4, hi, lo);
+      acc = mfma_f16_16x16x16(hi, lup[t], acc);
+      acc = mfma_f16_16x16x16(lo, lup[t], acc);
+    }
+  }
+  store_tile<MV>(g, acc, 0, nt * 16, af, bf, lane);
+}
+
+// ---------------------------------------------------------------------------
+// Tiled kernel (M > 16).  Workgroup tile (WM*TM*16) x (WN*TN*16); wave (wm,
+// wn) owns TM x TN tiles of 16x16.  Per k-pair, the packed 16x128 operand
+// tiles (1 KB each) and the scales of the workgroup's rows and columns (64 B
+// per tile) are copied HBM -> LDS with global_load_lds_dwordx4 (each lane
+// moves 16 bytes; no VGPRs involved) into an NS-deep ring: the copy of
+// k-pair p+NS-1 is issued right after the barrier that publishes k-pair p
+// and overlaps the arithmetic on p..p+NS-2.  Every wave issues the same
+// number of copies per stage, so an exact vmcnt wait publishes stage p while
+// later stages stay in flight.  Fragments are read back with conflict-free LDS
+// reads (lane l reads bytes [16l, 16l+16) of a tile).  Workgroups are
+// renumbered so that the workgroups of one XCD cover a contiguous range of
+// the row-major tile order (their A operand stays in that XCD's L2).
+// ---------------------------------------------------------------------------
+template <int WM, int WN, int TM, int TN, int RT, int NS>
+__global__ __launch_bounds__(WM * WN * 64, 2) void gemm_tiled_kernel(GemmArgs g, int64_t mt_count,
+                                                                 int64_t nt_count) {
+  constexpr int NW = WM * WN;
+  constexpr int BMT = WM * TM, BNT = WN * TN;            // tiles per workgroup
+  constexpr int CHUNKS = BMT + BNT;                      // 1 KB operand tiles per stage
+  constexpr int CPW = (CHUNKS + NW - 1) / NW;            // operand copies per wave per stage
+  constexpr int SLOTS = CPW * NW;                        // >= CHUNKS; extra slots take dummy copies
+  static_assert(SLOTS <= 16, "the scale copy covers at most 16 tiles");
+  constexpr int OPS = CPW + 1;                           // + one scale copy
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NS][SLOTS + 1][kTileBytes];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int c = lane >> 4;
+
+  const int64_t nbm = (mt_count + BMT - 1) / BMT, nbn = (nt_count + BNT - 1) / BNT;
+  const int64_t nblk = nbm * nbn;
+  int64_t b = blockIdx.x;
+  {
+    // dispatch places workgroup b on XCD b % 8; give each XCD a contiguous range
+    const int64_t per_xcd = nblk / 8, extra = nblk % 8;
+    const int64_t xcd = b % 8, local = b / 8;
+    b = xcd * per_xcd + (xcd < extra ? xcd : extra) + local;
+  }
+  const int64_t bm = b / nbn, bn = b % nbn;
+  const int64_t mt0 = bm * BMT, nt0 = bn * BNT;
+  const int64_t KP = g.K / kKPair;
+
+  // operand tile q of a stage: q < BMT -> A tile mt0+q; else B tile nt0+q-BMT.
+  // Tiles past the edge re-read the last valid tile (never stored); slots
+  // q >= CHUNKS (padding so that every wave issues the same number of
+  // copies) re-read tile CHUNKS-1.
+  auto tile_index = [&](int q) -> int64_t {
+    q = q < CHUNKS ? q : CHUNKS - 1;
+    if (q < BMT) {
+      const int64_t t = mt0 + q;
+      return t < mt_count ? t : mt_count - 1;
+    }
+    const int64_t t = nt0 + (q - BMT);
+    return t < nt_count ? t : nt_count - 1;
+  };
+  auto issue_copy = [&](int stage, int64_t p) {
+#pragma unroll
+    for (int u = 0; u < CPW; ++u) {
+      const int q = wave * CPW + u;
+      const uint8_t* base = (q < CHUNKS ? q : CHUNKS - 1) < BMT ? g.xq : g.wq;
+      __builtin_amdgcn_global_load_lds(base + ((size_t)tile_index(q) * KP + p) * kTileBytes + lane * 16,
+                                       (lds_void*)&lds[stage][q][0], 16, 0, 0);
+    }
+    // scales of this wave's tiles: 64 B (16 rows x 2 groups fp16) per tile,
+    // lane l < 4*CPW copies 16 B of tile wave*CPW + l/4
+    if (lane < 4 * CPW) {
+      const int q = wave * CPW + (lane >> 2);
+      const uint16_t* sbase = (q < CHUNKS ? q : CHUNKS - 1) < BMT ? g.sx : g.sw;
+      __builtin_amdgcn_global_load_lds(
+          reinterpret_cast<const uint8_t*>(sbase) + ((size_t)tile_index(q) * KP + p) * 64 + (lane & 3) * 16,
+          (lds_void*)&lds[stage][SLOTS][wave * CPW * 64], 16, 0, 0);
+    }
+  };
+
+  v4f acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < KP) issue_copy(s, s);
+
+  // Epilogue operands, loaded now so that they arrive during the main loop:
+  // lora_act fragments (sum of the partials) of the wave's row tiles, L_up
+  // fragments and the affine of its columns.  Tiles past the edge read the
+  // last valid tile (never stored).
+  constexpr int RTL = RT > 0 ? RT : 1;
+  v4f la_f[TM][RTL];
+  v4h lu_f[TN][RTL];
+  float af[TN], bf[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int64_t nt = tile_index(BMT + wn * TN + j);
+    af[j] = g.ca[nt * 16 + (lane & 15)];
+    bf[j] = g.cb[nt * 16 + (lane & 15)];
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+      lu_f[j][t] = *reinterpret_cast<const v4h*>(g.lup + (((size_t)nt * RT + t) * 64 + lane) * 4);
+  }
+  if constexpr (RT > 0) {
+    // for M > 16 lora_act is a single partial (one k range)
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int64_t mt = tile_index(wm * TM + i);
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+        la_f[i][t] = *reinterpret_cast<const v4f*>(g.la + (size_t)(mt * 16 + (lane & 15)) * g.R + t * 16 + c * 4);
+    }
+  }
+  int st = 0;                      // == p % NS
+  int st_next = (NS - 1) % NS;     // == (p + NS - 1) % NS
+  for (int64_t p = 0; p < KP; ++p) {
+    // stages issued after p and still allowed in flight
+    const int64_t after = (KP - 1 - p) < (NS - 2) ? (KP - 1 - p) : (NS - 2);
+    asm volatile("" ::: "memory");
+    if constexpr (NS >= 4) {
+      if (after >= 2) W4A4_WAIT_VMCNT(2 * OPS);
+      else if (after == 1) W4A4_WAIT_VMCNT(OPS);
+      else W4A4_WAIT_VMCNT(0);
+    } else if constexpr (NS == 3) {
+      if (after >= 1) W4A4_WAIT_VMCNT(OPS);
+      else W4A4_WAIT_VMCNT(0);
+    } else {
+      W4A4_WAIT_VMCNT(0);
+    }
+    // Every wave's copies of stage st have landed (each wave waited for its
+    // own above); after this barrier stage (p-1)%NS is no longer read by
+    // anyone.  A bare s_barrier is used: __syncthreads() would add a
+    // vmcnt(0) wait and drain the copies of later stages.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (p + NS - 1 < KP) issue_copy(st_next, p + NS - 1);
+    // Scales of this k-pair: lane l needs s_x of row 4(l/16) + l%4 of each of
+    // its row tiles and s_w of column l%16 of each of its column tiles (both
+    // groups in one dword).  The 4x4x4 f16 MFMA turns them into the exact
+    // fp32 tile S[m][n] = s_x[m] * s_w[n] in the accumulator layout.
+    const uint8_t* sl = &lds[st][SLOTS][0];
+    uint32_t sxw[TM], sww[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      sxw[i] = *reinterpret_cast<const uint32_t*>(sl + (wm * TM + i) * 64 + (4 * c + (lane & 3)) * 4);
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      sww[j] = *reinterpret_cast<const uint32_t*>(sl + (BMT + wn * TN + j) * 64 + (lane & 15) * 4);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      v4i Ae[TM], Be[TN];
+      v4h xs[TM], ws[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const v2u r2 = *reinterpret_cast<const v2u*>(&lds[st][wm * TM + i][lane * 16 + h * 8]);
+        Ae[i] = expand_group(r2[0], r2[1]);
+        xs[i] = __builtin_bit_cast(v4h, v2u{h ? (sxw[i] >> 16) : (sxw[i] & 0xFFFFu), 0u});
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const v2u r2 = *reinterpret_cast<const v2u*>(&lds[st][BMT + wn * TN + j][lane * 16 + h * 8]);
+        Be[j] = expand_group(r2[0], r2[1]);
+        ws[j] = __builtin_bit_cast(v4h, v2u{h ? (sww[j] >> 16) : (sww[j] & 0xFFFFu), 0u});
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const v4f S = __builtin_amdgcn_mfma_f32_4x4x4f16(xs[i], ws[j], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          const v4i P = mfma_i8_16x16x64(Ae[i], Be[j], v4i{0, 0, 0, 0});
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) acc[i][j][ii] = fmaf((float)P[ii], S[ii], acc[i][j][ii]);
+        }
+    }
+    st = st + 1 == NS ? 0 : st + 1;
+    st_next = st_next + 1 == NS ? 0 : st_next + 1;
+  }
+
+  // acc holds 256 * main (the int8 operands carry 16 q each)
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] *= (1.0f / 256.0f);
+
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int64_t nt = nt0 + wn * TN + j;
+    if (nt >= nt_count) continue;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int64_t mt = mt0 + wm * TM + i;
+      if (mt >= mt_count) continue;
+      v4f a = acc[i][j];
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        v4h hi, lo;
+        split_f16(la_f[i][t], hi, lo);
+        a = mfma_f16_16x16x16(hi, lu_f[j][t], a);
+        a = mfma_f16_16x16x16(lo, lu_f[j][t], a);
+      }
+      store_tile<4>(g, a, mt * 16, nt * 16, af[j], bf[j], lane);
+    }
+  }
+}
+
+template <int MV>
+static hipError_t launch_decode_mv(const GemmArgs& a, hipStream_t stream) {
+  dim3 grid((unsigned)(a.N / 16)), block(64 * kDecodeWaves);
+  switch (a.R / 16) {
+    case 0: gemm_decode_kernel<MV, 0><<<grid, block, 0, stream>>>(a); break;
+    case 1: gemm_decode_kernel<MV, 1><<<grid, block, 0, stream>>>(a); break;
+    case 2: gemm_decode_kernel<MV, 2><<<grid, block, 0, stream>>>(a); break;
+    case 3: gemm_decode_kernel<MV, 3><<<grid, block, 0, stream>>>(a); break;
+    case 4: gemm_decode_kernel<MV, 4><<<grid, block, 0, stream>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+static hipError_t launch_decode(const GemmArgs& a, hipStream_t stream) {
+  switch (a.M) {
+    case 1: return launch_decode_mv<1>(a, stream);
+    case 2: return launch_decode_mv<2>(a, stream);
+    case 3: return launch_decode_mv<3>(a, stream);
+    default: return launch_decode_mv<4>(a, stream);
+  }
+}
+
+constexpr int kTiledStages = 4;
+
+template <int WM, int WN, int TM, int TN>
+static hipError_t launch_tiled_cfg(const GemmArgs& a, hipStream_t stream) {
+  const int64_t mt = round_up16(a.M) / 16, nt = a.N / 16;
+  const int64_t nblk = ((mt + WM * TM - 1) / (WM * TM)) * ((nt + WN * TN - 1) / (WN * TN));
+  dim3 grid((unsigned)nblk), block(64 * WM * WN);
+  constexpr int NS = kTiledStages;
+  switch (a.R / 16) {
+    case 0: gemm_tiled_kernel<WM, WN, TM, TN, 0, NS><<<grid, block, 0, stream>>>(a, mt, nt); break;
+    case 1: gemm_tiled_kernel<WM, WN, TM, TN, 1, NS><<<grid, block, 0, stream>>>(a, mt, nt); break;
+    case 2: gemm_tiled_kernel<WM, WN, TM, TN, 2, NS><<<grid, block, 0, stream>>>(a, mt, nt); break;
+    case 3: gemm_tiled_kernel<WM, WN, TM, TN, 3, NS><<<grid, block, 0, stream>>>(a, mt, nt); break;
+    case 4: gemm_tiled_kernel<WM, WN, TM, TN, 4, NS><<<grid, block, 0, stream>>>(a, mt, nt); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// Tile shapes for M > 16, largest first: (rows x cols) of a workgroup.
+struct TiledCfg {
+  int bm, bn;
+};
+constexpr TiledCfg kTiledCfgs[] = {{128, 128}, {64, 128}, {128, 64}, {64, 64}, {32, 64}};
+constexpr int64_t kTiledMinWorkgroups = 256;   // one per CU
+
+static int pick_tiled(int64_t M, int64_t N) {
+  const int64_t mt = round_up16(M) / 16, nt = N / 16;
+  int best = 0;
+  int64_t best_n = -1;
+  for (int i = 0; i < (int)(sizeof(kTiledCfgs) / sizeof(kTiledCfgs[0])); ++i) {
+    const int64_t n = ((mt + kTiledCfgs[i].bm / 16 - 1) / (kTiledCfgs[i].bm / 16)) *
+                      ((nt + kTiledCfgs[i].bn / 16 - 1) / (kTiledCfgs[i].bn / 16));
+    if (n >= kTiledMinWorkgroups) return i;
+    if (n > best_n) {
+      best_n = n;
+      best = i;
+    }
+  }
+  return best;
+}
+
 template <int TM, int TN, bool PSUM>
 static hipError_t launch_generic_rt(const GemmArgs& a, int64_t mt_base, int64_t mt_end,
                                     int64_t nt_base, int64_t nt_end, int32_t* psum,
@@ -177,13 +655,24 @@ static hipError_t launch_generic_rt(const GemmArgs& a, int64_t mt_base, int64_t 
 }
 
 int choose_variant(int64_t M, int64_t N, int64_t K, int R) {
-  (void)M; (void)N; (void)K; (void)R;
-  return kGeneric;
+  (void)N; (void)K; (void)R;
+  return M <= 16 ? kDecode : kPrefill;
 }
 
 hipError_t launch_gemm(const GemmArgs& a, int variant, hipStream_t stream) {
   const int64_t mt = round_up16(a.M) / 16, nt = a.N / 16;
   switch (variant) {
+    case kDecode:
+      return launch_decode(a, stream);
+    case kPrefill:
+      if (a.ks != 1) return hipErrorInvalidValue;   // lora_splits() is 1 for M > 16
+      switch (pick_tiled(a.M, a.N)) {
+        case 0: return launch_tiled_cfg<2, 2, 4, 4>(a, stream);
+        case 1: return launch_tiled_cfg<2, 2, 2, 4>(a, stream);
+        case 2: return launch_tiled_cfg<2, 2, 4, 2>(a, stream);
+        case 3: return launch_tiled_cfg<2, 2, 2, 2>(a, stream);
+        default: return launch_tiled_cfg<2, 2, 1, 2>(a, stream);
+      }
     default:
       return launch_generic_rt<2, 2, false>(a, 0, mt, 0, nt, nullptr, 0, stream);
   }

@@ -6,8 +6,8 @@
 // LoRA down-projection lora_act = X L_down on the fp16 values.  Section 2.3 /
 // 3.10: weights are repacked once at load into the kernel's layout.
 //
-// gfx950 design: one workgroup per 16-row tile, W = min(16, K/128) waves; a
-// wave owns whole 16 x 128 k-pairs.  Lane l = r + 16c loads the 32 fp16 values
+// gfx950 design: one workgroup of 4 or 16 waves per (16-row tile, k-pair
+// range); a wave owns whole 16 x 128 k-pairs.  Lane l = r + 16c loads the 32 fp16 values
 // of row r at k = 128p + 64j + 16c + [0,16) (j = group in the pair) with four
 // 128-bit loads, and those registers serve three purposes without any LDS
 // staging: the absmax (reduced over the four lanes of a row with two xor
@@ -22,16 +22,30 @@
 
 namespace w4a4 {
 
-// Codes for 8 values (one dword) with scale `sf`, per the quantizer rule.
-// The fp32 division is IEEE (correctly rounded); rintf rounds half to even.
-__device__ __forceinline__ uint32_t quantize8(v8h v, float sf) {
+// Codes for 8 values (one dword): q = clamp(rint(fl32(x / s)), -8, 7) with
+// round-half-to-even, where s is the group's fp16 scale (sf, exact in fp32)
+// and rs ~ 1/s (v_rcp_f32, ~1 ulp).
+//
+// No IEEE division is needed.  x and s are fp16 values, so x/s is a ratio of
+// two integers of at most 11 bits times a power of two; unless it is exactly
+// a half-integer, it lies at least 2^-13 away from every half-integer, far
+// beyond the error of t = x * rs (< 2^-19 for |x/s| <= 8.5), so rint(t) is the
+// nearest integer to x/s -- the same as the nearest integer to fl32(x/s).  When x/s is exactly a half-integer, fl32(x/s)
+// is that half-integer and the rule rounds it to the even neighbour.  The
+// residual f = x - n*s is computed exactly by one fma (n*s has <= 15
+// significant bits and |f| <= s/2, so f needs <= 12 bits), and x/s is a
+// half-integer exactly when |f| == s/2; then n is moved to the even side.
+__device__ __forceinline__ uint32_t quantize8(v8h v, float sf, float rs) {
   uint32_t out = 0;
+  const float half_s = 0.5f * sf;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    float t = rintf((float)v[i] / sf);
-    t = fminf(fmaxf(t, -8.0f), 7.0f);
-    int q = (int)t;
-    out |= (uint32_t(q) & 0xFu) << (4 * i);
+    const float x = (float)v[i];
+    float n = __builtin_rintf(x * rs);
+    const float f = __builtin_fmaf(-n, sf, x);
+    if (__builtin_fabsf(f) == half_s && (((int)n) & 1)) n += __builtin_copysignf(1.0f, f);
+    n = __builtin_amdgcn_fmed3f(n, -8.0f, 7.0f);
+    out |= (uint32_t((int)n) & 0xFu) << (4 * i);
   }
   return out;
 }
@@ -42,7 +56,8 @@ __device__ __forceinline__ float absmax8(v8h v, float m) {
   return m;
 }
 
-// Scale of a group from its absmax: fp16(fp32(amax / 7)); 0 -> 2^-24.
+// Scale of a group from its absmax: fp16(fp32(amax / 7)) with the IEEE fp32
+// division (one per group); a zero scale becomes 2^-24.
 __device__ __forceinline__ _Float16 group_scale(float amax) {
   float s32 = amax / 7.0f;
   _Float16 s = (_Float16)s32;
@@ -50,55 +65,69 @@ __device__ __forceinline__ _Float16 group_scale(float amax) {
   return s;
 }
 
-template <int RT>  // RT = R / 16 (0 = no LoRA)
-__global__ __launch_bounds__(1024) void quantize_rows_kernel(
-    const uint16_t* __restrict__ src, int64_t ld, int64_t rows, int64_t K,
+// Grid (rows_padded/16, ks) x NW waves.  Workgroup (rt, j) handles the 16-row
+// tile rt and the k-pairs [j*KP/ks, (j+1)*KP/ks); its waves take every NW-th
+// k-pair.  The next k-pair's X loads are issued before the current one is
+// processed.  NW = 16 when there are few row tiles (more loads in flight per
+// tile), else 4.
+template <int RT, int NW>  // RT = R / 16 (0 = no LoRA)
+__global__ __launch_bounds__(NW * 64) void quantize_rows_kernel(
+    const uint16_t* __restrict__ src, int64_t ld, int64_t rows, int64_t rows_padded, int64_t K,
     const uint16_t* __restrict__ ldown, uint8_t* __restrict__ codes,
-    uint16_t* __restrict__ scales, float* __restrict__ lora_act) {
+    uint16_t* __restrict__ scales, float* __restrict__ lora_part) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int nwaves = blockDim.x >> 6;
   const int r = lane & 15, c = lane >> 4;
   const int64_t rt = blockIdx.x;
   const int64_t row = rt * 16 + r;
   const bool valid = row < rows;
   const int64_t KP = K / kKPair;
+  const int64_t ks = gridDim.y, j = blockIdx.y;
+  const int64_t pbeg = j * KP / ks, pend = (j + 1) * KP / ks;
   const _Float16* xrow = reinterpret_cast<const _Float16*>(src) + (valid ? row * ld : 0);
 
   v4f acc[RT > 0 ? RT : 1];
 #pragma unroll
   for (int t = 0; t < (RT > 0 ? RT : 1); ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  for (int64_t p = wave; p < KP; p += nwaves) {
-    v8h v[4];  // v[2j + h]: group j, k = 16c + 8h + [0,8)
+  auto load_x = [&](int64_t p, v8h* v) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       if (valid) {
         const int64_t k = p * kKPair + (s >> 1) * kGroup + c * 16 + (s & 1) * 8;
-        v[s] = *reinterpret_cast<const v8h*>(xrow + k);
+        v[s] = __builtin_nontemporal_load(reinterpret_cast<const v8h*>(xrow + k));
       } else {
         v[s] = v8h{0, 0, 0, 0, 0, 0, 0, 0};
       }
     }
+  };
+
+  v8h v[4], vn[4];
+  int64_t p = pbeg + wave;
+  if (p < pend) load_x(p, v);
+  for (; p < pend; p += NW) {
+    const bool more = p + NW < pend;
+    if (more) load_x(p + NW, vn);
     uint32_t d[4];
     _Float16 sc[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      float am = absmax8(v[2 * j + 1], absmax8(v[2 * j], 0.0f));
+    for (int h = 0; h < 2; ++h) {
+      float am = absmax8(v[2 * h + 1], absmax8(v[2 * h], 0.0f));
       am = fmaxf(am, __shfl_xor(am, 16));
       am = fmaxf(am, __shfl_xor(am, 32));
-      _Float16 s = group_scale(am);
+      const _Float16 s = group_scale(am);
       const float sf = (float)s;
-      d[2 * j] = quantize8(v[2 * j], sf);
-      d[2 * j + 1] = quantize8(v[2 * j + 1], sf);
-      sc[j] = valid ? s : (_Float16)0.0f;
+      const float rs = __builtin_amdgcn_rcpf(sf);
+      d[2 * h] = quantize8(v[2 * h], sf, rs);
+      d[2 * h + 1] = quantize8(v[2 * h + 1], sf, rs);
+      sc[h] = valid ? s : (_Float16)0.0f;
     }
     uint8_t* tile = codes + (size_t)(rt * KP + p) * kTileBytes;
     *reinterpret_cast<v4u*>(tile + lane * 16) = v4u{d[0], d[1], d[2], d[3]};
     if (c == 0) {
       _Float16* sp = reinterpret_cast<_Float16*>(scales) + ((size_t)(rt * KP + p) * 16 + r) * 2;
-      sp[0] = sc[0];
-      sp[1] = sc[1];
+      *reinterpret_cast<uint32_t*>(sp) =
+          uint32_t(__builtin_bit_cast(uint16_t, sc[0])) | (uint32_t(__builtin_bit_cast(uint16_t, sc[1])) << 16);
     }
     if constexpr (RT > 0) {
       const _Float16* lp = reinterpret_cast<const _Float16*>(ldown) + (size_t)p * RT * 4 * 64 * 8;
@@ -111,45 +140,62 @@ __global__ __launch_bounds__(1024) void quantize_rows_kernel(
         }
       }
     }
+    if (more) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) v[s] = vn[s];
+    }
   }
 
   if constexpr (RT > 0) {
-    // red[w][t*4 + i][lane]: partial of rows 4c+i, rank 16t + (lane & 15)
-    __shared__ float red[16][RT * 4][64];
+    // red[w][t*4 + i][lane]: partial of rows 4c+i, rank 16t + (lane & 15);
+    // summed over the waves in order (deterministic)
+    __shared__ float red[NW][RT * 4][64];
 #pragma unroll
     for (int t = 0; t < RT; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) red[wave][t * 4 + i][lane] = acc[t][i];
     __syncthreads();
     const int R = RT * 16;
+    float* out = lora_part + (size_t)j * rows_padded * R;
     for (int e = threadIdx.x; e < RT * 4 * 64; e += blockDim.x) {
       const int ti = e >> 6, l = e & 63;
       float s = 0.0f;
-      for (int w = 0; w < nwaves; ++w) s += red[w][ti][l];
+#pragma unroll
+      for (int w = 0; w < NW; ++w) s += red[w][ti][l];
       const int t = ti >> 2, i = ti & 3;
       const int64_t orow = rt * 16 + (l >> 4) * 4 + i;
-      lora_act[orow * R + t * 16 + (l & 15)] = s;
+      out[orow * R + t * 16 + (l & 15)] = s;
     }
   }
 }
 
-hipError_t launch_quantize_rows(const uint16_t* src, int64_t ld, int64_t rows,
-                                int64_t rows_padded, int64_t K, int R,
-                                const uint16_t* ldown_packed, uint8_t* codes,
-                                uint16_t* scales, float* lora_act,
-                                hipStream_t stream) {
-  const int64_t KP = K / kKPair;
-  const int waves = (int)(KP < 16 ? KP : 16);
-  dim3 grid((unsigned)(rows_padded / 16)), block(64 * waves);
+template <int NW>
+static hipError_t launch_quantize_nw(const uint16_t* src, int64_t ld, int64_t rows,
+                                     int64_t rows_padded, int64_t K, int R, int ks,
+                                     const uint16_t* ldown_packed, uint8_t* codes,
+                                     uint16_t* scales, float* lora_part, hipStream_t stream) {
+  dim3 grid((unsigned)(rows_padded / 16), (unsigned)ks), block(64 * NW);
   switch (R / 16) {
-    case 0: quantize_rows_kernel<0><<<grid, block, 0, stream>>>(src, ld, rows, K, ldown_packed, codes, scales, lora_act); break;
-    case 1: quantize_rows_kernel<1><<<grid, block, 0, stream>>>(src, ld, rows, K, ldown_packed, codes, scales, lora_act); break;
-    case 2: quantize_rows_kernel<2><<<grid, block, 0, stream>>>(src, ld, rows, K, ldown_packed, codes, scales, lora_act); break;
-    case 3: quantize_rows_kernel<3><<<grid, block, 0, stream>>>(src, ld, rows, K, ldown_packed, codes, scales, lora_act); break;
-    case 4: quantize_rows_kernel<4><<<grid, block, 0, stream>>>(src, ld, rows, K, ldown_packed, codes, scales, lora_act); break;
+    case 0: quantize_rows_kernel<0, NW><<<grid, block, 0, stream>>>(src, ld, rows, rows_padded, K, ldown_packed, codes, scales, lora_part); break;
+    case 1: quantize_rows_kernel<1, NW><<<grid, block, 0, stream>>>(src, ld, rows, rows_padded, K, ldown_packed, codes, scales, lora_part); break;
+    case 2: quantize_rows_kernel<2, NW><<<grid, block, 0, stream>>>(src, ld, rows, rows_padded, K, ldown_packed, codes, scales, lora_part); break;
+    case 3: quantize_rows_kernel<3, NW><<<grid, block, 0, stream>>>(src, ld, rows, rows_padded, K, ldown_packed, codes, scales, lora_part); break;
+    case 4: quantize_rows_kernel<4, NW><<<grid, block, 0, stream>>>(src, ld, rows, rows_padded, K, ldown_packed, codes, scales, lora_part); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_quantize_rows(const uint16_t* src, int64_t ld, int64_t rows,
+                                int64_t rows_padded, int64_t K, int R, int ks,
+                                const uint16_t* ldown_packed, uint8_t* codes,
+                                uint16_t* scales, float* lora_part,
+                                hipStream_t stream) {
+  const int64_t wgs = rows_padded / 16 * ks;
+  const int64_t kp_per_wg = (K / kKPair + ks - 1) / ks;
+  if (wgs < 256 && kp_per_wg >= 8)
+    return launch_quantize_nw<16>(src, ld, rows, rows_padded, K, R, ks, ldown_packed, codes, scales, lora_part, stream);
+  return launch_quantize_nw<4>(src, ld, rows, rows_padded, K, R, ks, ldown_packed, codes, scales, lora_part, stream);
 }
 
 // ---------------------------------------------------------------------------

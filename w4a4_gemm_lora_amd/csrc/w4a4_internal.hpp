@@ -15,7 +15,7 @@ constexpr int kTileBytes = 1024;  // 16 rows x 128 k nibbles
 constexpr int kMaxRank = 64;
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
-inline int64_t round_up16(int64_t x) { return (x + 15) / 16 * 16; }
+__host__ __device__ inline int64_t round_up16(int64_t x) { return (x + 15) / 16 * 16; }
 
 struct WeightGeom {
   int64_t N, K;
@@ -25,9 +25,20 @@ struct WeightGeom {
 
 struct ActGeom {
   int64_t M, Mp, K;
-  int R;
+  int R, ks;
   size_t off_xq, off_sx, off_la, total;
 };
+
+// The activation pass splits K into `ks` contiguous ranges of k-pairs when M
+// fits one 16-row tile (decode): each range writes its own LoRA-down partial
+// sum and the GEMM adds the partials.  For M > 16 there is one range.
+constexpr int kMaxLoraSplits = 8;
+
+inline int lora_splits(int64_t M, int64_t K) {
+  if (M > 16) return 1;
+  const int64_t ks = (K / kKPair) / 4;
+  return ks < 1 ? 1 : (ks > kMaxLoraSplits ? kMaxLoraSplits : (int)ks);
+}
 
 inline WeightGeom weight_geom(int64_t N, int64_t K, int R) {
   WeightGeom g{};
@@ -51,21 +62,23 @@ inline ActGeom act_geom(int64_t M, int64_t K, int R) {
   g.Mp = round_up16(M);
   g.K = K;
   g.R = R;
+  g.ks = lora_splits(M, K);
   size_t o = 0;
   g.off_xq = o; o = align256(o + size_t(g.Mp) * K / 2);
   g.off_sx = o; o = align256(o + size_t(g.Mp) * (K / kGroup) * 2);
-  g.off_la = o; o = align256(o + size_t(g.Mp) * R * 4);
+  g.off_la = o; o = align256(o + size_t(g.ks) * g.Mp * R * 4);
   g.total = o;
   return g;
 }
 
 // ---- launchers (defined in the .hip files; return hipError_t of the launch)
 // Quantize `rows` rows (padded up to a multiple of 16 with q=0, s=0) of an
-// fp16 matrix into codes/scales tiles; with R > 0 also lora_act = src L_down.
+// fp16 matrix into codes/scales tiles.  With R > 0 also the LoRA-down partial sums lora_part[ks][rows_padded][R]
+// over `ks` k-pair ranges (ks = 1: the full sum).
 hipError_t launch_quantize_rows(const uint16_t* src, int64_t ld, int64_t rows,
-                                int64_t rows_padded, int64_t K, int R,
+                                int64_t rows_padded, int64_t K, int R, int ks,
                                 const uint16_t* ldown_packed, uint8_t* codes,
-                                uint16_t* scales, float* lora_act,
+                                uint16_t* scales, float* lora_part,
                                 hipStream_t stream);
 
 hipError_t launch_repack_qweight(const uint8_t* qweight, const uint16_t* w_scales,
@@ -92,6 +105,7 @@ struct GemmArgs {
   int64_t ldy;
   int64_t M, N, K;
   int R;
+  int ks;   // LoRA-down partials in la: [ks][Mp][R]
 };
 
 enum Variant { kGeneric = 0, kDecode = 1, kPrefill = 2 };

@@ -159,8 +159,32 @@ def main(argv=None):
         W.w4a4_linear(M, N, K, R, act, wb, y, stream=sh)
         ev[i][2].record(stream)
     torch.cuda.synchronize()
-    q_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    l_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    q_ms_ev = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    l_ms_ev = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+
+    # Kernel-only figures: a graph of `nk_g` back-to-back launches of one
+    # kernel, bracketed by two events on the launch stream; the average
+    # launch duration is (elapsed) / nk_g.
+    def graph_avg_ms(fn, n):
+        gk = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gk):
+            cs2 = torch.cuda.current_stream().cuda_stream
+            for i in range(n):
+                fn(i, cs2)
+        gk.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s2 = torch.cuda.current_stream()
+        e0.record(s2)
+        for _ in range(3):
+            gk.replay()
+        e1.record(s2)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (3 * n)
+
+    nk_g = 50
+    l_ms = graph_avg_ms(lambda i, cs2: W.w4a4_linear(M, N, K, R, act, blobs[i % len(blobs)], y, stream=cs2), nk_g)
+    q_ms = graph_avg_ms(lambda i, cs2: W.w4a4_quantize_act(M, K, R, x, blobs[i % len(blobs)], act, stream=cs2), nk_g)
 
     c = algorithmic_counts(M, N, K, R)
     value = c["layer_ops"] / (ms_per_step * 1e-3) / 1e12
@@ -184,9 +208,11 @@ def main(argv=None):
         "hbm_gbps_step": round((c["lin_bytes"] + c["q_bytes"]) / (ms_per_step * 1e-3) / 1e9, 1),
         "kernels": {
             "w4a4_linear": {"avg_us": round(l_ms * 1e3, 3), "TOPS": round(lin_tops, 2),
-                             "GBps": round(c["lin_bytes"] / (l_ms * 1e-3) / 1e9, 1)},
+                             "GBps": round(c["lin_bytes"] / (l_ms * 1e-3) / 1e9, 1),
+                             "event_bracketed_us": round(l_ms_ev * 1e3, 3)},
             "w4a4_quantize_act": {"avg_us": round(q_ms * 1e3, 3),
-                                   "GBps": round(c["q_bytes"] / (q_ms * 1e-3) / 1e9, 1)},
+                                   "GBps": round(c["q_bytes"] / (q_ms * 1e-3) / 1e9, 1),
+                                   "event_bracketed_us": round(q_ms_ev * 1e3, 3)},
         },
         "roofline": {"bound": "mfma", "achieved": round(lin_tops, 2), "peak": PEAK_INT8_TOPS,
                      "unit": "TFLOP/s", "frac": round(lin_tops / PEAK_INT8_TOPS, 4), "traffic": None},

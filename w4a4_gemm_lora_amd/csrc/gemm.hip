@@ -21,6 +21,8 @@
 // barely overlap, so the per-group epilogue (convert, scale product, fma on
 // four accumulators per lane) costs about twice the MFMA itself.  Large-M
 // kernels are therefore bound by issue of MFMA + VALU, not by HBM.
+#include <cstdlib>
+
 #include "device_common.hpp"
 #include "w4a4_internal.hpp"
 
@@ -219,6 +221,22 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, v4f acc, int64_t r
   }
 }
 
+// Same for a tile known to start at a row < M: one 64-bit address per lane,
+// then the four rows at a stride of ldy; only a ragged last tile pays a
+// per-row check.
+__device__ __forceinline__ void store_tile4(const GemmArgs& g, v4f acc, int64_t row0, int64_t col0,
+                                            float af, float bf, int lane) {
+  const int c = lane >> 4, r = lane & 15;
+  const int64_t row = row0 + c * 4;
+  uint16_t* p = g.y + row * g.ldy + col0 + r;
+  const int64_t rows_left = g.M - row;
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii) {
+    const _Float16 v = (_Float16)fmaf(af, acc[ii], bf);
+    if (rows_left > ii) p[ii * g.ldy] = __builtin_bit_cast(uint16_t, v);
+  }
+}
+
 // One 64-group of one 16x16 tile: an i8 MFMA with a zero C (256 P exactly)
 // followed by acc += P * s_x * s_w / 256 for the MV leading accumulator rows.
 template <int MV>
@@ -298,11 +316,16 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_kernel(GemmArgs g) {
   const uint8_t* wq = g.wq + (size_t)nt * KP * kTileBytes + lane * 16;
   const uint16_t* sw = g.sw + (size_t)nt * KP * 32 + r * 2;
   for (int64_t pb = p0; pb < p1; pb += kDecodeBatch) {
+    // Only lanes holding rows < M carry data (row r = lane & 15); the other
+    // LDS slots keep stale bytes, which only reach accumulator rows >= M
+    // (never stored).
+    if (r < g.M) {
 #pragma unroll
-    for (int u = 0; u < kDecodeBatch; ++u) {
-      const int64_t p = pb + u < p1 ? pb + u : p1 - 1;
-      __builtin_amdgcn_global_load_lds(g.xq + (size_t)p * kTileBytes + lane * 16,
-                                       (lds_void*)&a_lds[wave][u][0], 16, 0, 0);
+      for (int u = 0; u < kDecodeBatch; ++u) {
+        const int64_t p = pb + u < p1 ? pb + u : p1 - 1;
+        __builtin_amdgcn_global_load_lds(g.xq + (size_t)p * kTileBytes + lane * 16,
+                                         (lds_void*)&a_lds[wave][u][0], 16, 0, 0);
+      }
     }
     {
       // activation scales: 64 B per k-pair; lane l fetches part (l & 3) of k-pair l / 4
@@ -378,8 +401,11 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_kernel(GemmArgs g) {
 // later stages stay in flight.  Fragments are read back with conflict-free LDS
 // reads (lane l reads bytes [16l, 16l+16) of a tile).  Workgroups are
 // renumbered so that the workgroups of one XCD cover a contiguous range of
-// the row-major tile order (their A operand stays in that XCD's L2).
+// a grouped tile order (groups of 8 row bands, column tiles outer), which
+// keeps both operands' working set of an XCD inside its L2.
 // ---------------------------------------------------------------------------
+constexpr int kTileGroupRows = 8;
+
 template <int WM, int WN, int TM, int TN, int RT, int NS>
 __global__ __launch_bounds__(WM * WN * 64, 2) void gemm_tiled_kernel(GemmArgs g, int64_t mt_count,
                                                                  int64_t nt_count) {
@@ -406,7 +432,18 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void gemm_tiled_kernel(GemmArgs g,
     const int64_t xcd = b % 8, local = b / 8;
     b = xcd * per_xcd + (xcd < extra ? xcd : extra) + local;
   }
-  const int64_t bm = b / nbn, bn = b % nbn;
+  // Grouped order inside each XCD's range: kTileGroupRows row bands advance
+  // together and column tiles are the outer index, so a B column tile is
+  // reused by the whole group while the group's A band stays in L2.
+  int64_t bm, bn;
+  {
+    const int64_t group_size = (int64_t)kTileGroupRows * nbn;
+    const int64_t first_bm = (b / group_size) * kTileGroupRows;
+    const int64_t gm = nbm - first_bm < kTileGroupRows ? nbm - first_bm : kTileGroupRows;
+    const int64_t in_g = b % group_size;
+    bm = first_bm + in_g % gm;
+    bn = in_g / gm;
+  }
   const int64_t mt0 = bm * BMT, nt0 = bn * BNT;
   const int64_t KP = g.K / kKPair;
 
@@ -457,7 +494,7 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void gemm_tiled_kernel(GemmArgs g,
   // fragments and the affine of its columns.  Tiles past the edge read the
   // last valid tile (never stored).
   constexpr int RTL = RT > 0 ? RT : 1;
-  v4f la_f[TM][RTL];
+  v4h la_hi[TM][RTL], la_lo[TM][RTL];
   v4h lu_f[TN][RTL];
   float af[TN], bf[TN];
 #pragma unroll
@@ -475,8 +512,10 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void gemm_tiled_kernel(GemmArgs g,
     for (int i = 0; i < TM; ++i) {
       const int64_t mt = tile_index(wm * TM + i);
 #pragma unroll
-      for (int t = 0; t < RT; ++t)
-        la_f[i][t] = *reinterpret_cast<const v4f*>(g.la + (size_t)(mt * 16 + (lane & 15)) * g.R + t * 16 + c * 4);
+      for (int t = 0; t < RT; ++t) {
+        const v4f l4 = *reinterpret_cast<const v4f*>(g.la + (size_t)(mt * 16 + (lane & 15)) * g.R + t * 16 + c * 4);
+        split_f16(l4, la_hi[i][t], la_lo[i][t]);
+      }
     }
   }
   int st = 0;                      // == p % NS
@@ -562,12 +601,10 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void gemm_tiled_kernel(GemmArgs g,
       v4f a = acc[i][j];
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
-        v4h hi, lo;
-        split_f16(la_f[i][t], hi, lo);
-        a = mfma_f16_16x16x16(hi, lu_f[j][t], a);
-        a = mfma_f16_16x16x16(lo, lu_f[j][t], a);
+        a = mfma_f16_16x16x16(la_hi[i][t], lu_f[j][t], a);
+        a = mfma_f16_16x16x16(la_lo[i][t], lu_f[j][t], a);
       }
-      store_tile<4>(g, a, mt * 16, nt * 16, af[j], bf[j], lane);
+      store_tile4(g, a, mt * 16, nt * 16, af[j], bf[j], lane);
     }
   }
 }
@@ -619,13 +656,26 @@ struct TiledCfg {
   int bm, bn;
 };
 constexpr TiledCfg kTiledCfgs[] = {{128, 128}, {64, 128}, {128, 64}, {64, 64}, {32, 64}};
-constexpr int64_t kTiledMinWorkgroups = 256;   // one per CU
+constexpr int kNumTiledCfgs = (int)(sizeof(kTiledCfgs) / sizeof(kTiledCfgs[0]));
+constexpr int64_t kTiledMinWorkgroups = 512;   // two per CU (latency hiding beats tile reuse here)
+
+// W4A4_TILED_CFG=<index into kTiledCfgs> forces a tile shape (tuning aid).
+static int tiled_override() {
+  static const int v = [] {
+    const char* e = std::getenv("W4A4_TILED_CFG");
+    if (!e || !e[0]) return -1;
+    const int i = std::atoi(e);
+    return (i >= 0 && i < kNumTiledCfgs) ? i : -1;
+  }();
+  return v;
+}
 
 static int pick_tiled(int64_t M, int64_t N) {
+  if (tiled_override() >= 0) return tiled_override();
   const int64_t mt = round_up16(M) / 16, nt = N / 16;
   int best = 0;
   int64_t best_n = -1;
-  for (int i = 0; i < (int)(sizeof(kTiledCfgs) / sizeof(kTiledCfgs[0])); ++i) {
+  for (int i = 0; i < kNumTiledCfgs; ++i) {
     const int64_t n = ((mt + kTiledCfgs[i].bm / 16 - 1) / (kTiledCfgs[i].bm / 16)) *
                       ((nt + kTiledCfgs[i].bn / 16 - 1) / (kTiledCfgs[i].bn / 16));
     if (n >= kTiledMinWorkgroups) return i;

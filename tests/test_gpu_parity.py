@@ -165,7 +165,7 @@ def test_quantizer_golden_groups_on_gpu():
     assert np.array_equal(a["qx"][:M], qx)
 
 
-WORKLOAD_CASES = ["small", "mlp_up", "mlp_down", "decode-1", "decode-4", "decode-16"]
+WORKLOAD_CASES = ["small", "mlp_up", "mlp_down", "decode-1", "decode-2", "decode-4", "decode-16"]
 
 
 def _workload(name):
@@ -238,6 +238,32 @@ def test_ragged_and_rank_edges(M, K, N, R):
     got = run.psums(0, Mp, 0, N)
     assert np.array_equal(got[:M], O.group_psums(ref["qx"], ref["qw"]))
     # rows >= M of y are never written
+    assert np.all(np.isnan(run.host_y()[M:].astype(np.float64)))
+
+
+@pytest.mark.parametrize("M,K,N,R", [(1, 128, 48, 0), (2, 384, 32, 64), (1, 1664, 64, 48),
+                                     (2, 4864, 48, 32), (1, 4864, 16, 64), (2, 1664, 48, 16),
+                                     (3, 1664, 32, 32)])
+def test_small_m_decode_shapes(M, K, N, R):
+    """M <= 16 kernels over uneven per-wave k-pair ranges (a wave with no
+    k-pairs, ranges that are not a multiple of the batch), every rank, and
+    groups whose scales differ by 16x between odd and even groups, so a
+    group / scale mispairing cannot hide inside the tolerance."""
+    case = workloads.random_case(M, K, N, R, seed=2000 + M + K + R)
+    x = case["x"].astype(np.float64)
+    x[:, (np.arange(K) // 64) % 2 == 1] *= 16.0
+    case["x"] = x.astype(np.float16)
+    w = case["w"].astype(np.float64)
+    w[:, (np.arange(K) // 64) % 3 == 2] *= 0.125
+    case["w"] = w.astype(np.float16)
+    _say(f"[decode-shape] M={M} K={K} N={N} R={R}")
+    assert W.w4a4_query_variant(M, N, K, R) == 1
+    run = GpuRun(case)
+    ref = O.linear(case["x"], case["lora_down"] if R else None, case["lora_up"] if R else None,
+                   case["col_scale"], case["bias"], w16=case["w"])
+    a = _check_quant(run, case, ref["qx"], ref["sx"])
+    _check_lora_act(a, ref["lora_act"], M)
+    _check_y(run.host_y()[:M, :N], ref["y"], f"decode shape M={M} K={K} R={R}")
     assert np.all(np.isnan(run.host_y()[M:].astype(np.float64)))
 
 

@@ -289,7 +289,7 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_kernel(GemmArgs g) {
   const int c = lane >> 4, r = lane & 15;
 
   // Epilogue prefetch, issued before the weight stream: wave w sums the LoRA
-  // partials j = w, w+4, ... (fixed order) of rows 0..15; wave 0 also takes
+  // partials j = w, w+4, ... (fixed order) of rows 0..M-1; wave 0 also takes
   // the L_up fragments and the affine of its columns.
   v4f lsum[RTL];
   v4h lup[RTL];
@@ -297,10 +297,11 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_kernel(GemmArgs g) {
   for (int t = 0; t < RTL; ++t) lsum[t] = v4f{0.f, 0.f, 0.f, 0.f};
   float af = 0.f, bf = 0.f;
   if constexpr (RT > 0) {
-    for (int j = wave; j < g.ks; j += kDecodeWaves)
+    if (r < g.M)   // rows >= M stay 0 and are never stored
+      for (int j = wave; j < g.ks; j += kDecodeWaves)
 #pragma unroll
-      for (int t = 0; t < RT; ++t)
-        lsum[t] += *reinterpret_cast<const v4f*>(g.la + ((size_t)j * 16 + r) * g.R + t * 16 + c * 4);
+        for (int t = 0; t < RT; ++t)
+          lsum[t] += *reinterpret_cast<const v4f*>(g.la + ((size_t)j * 16 + r) * g.R + t * 16 + c * 4);
     if (wave == 0) {
 #pragma unroll
       for (int t = 0; t < RT; ++t)
@@ -387,6 +388,171 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_kernel(GemmArgs g) {
     }
   }
   store_tile<MV>(g, acc, 0, nt * 16, af, bf, lane);
+}
+
+// ---------------------------------------------------------------------------
+// Decode kernel for M <= 2: no nibble expansion and no MFMA in the K loop.
+// v_dot8_i32_i4 multiplies the 8 signed nibbles of a weight dword with the
+// 8 nibbles of the matching activation dword (the packed layouts pair the
+// same k in the same nibble position), so lane (column r = lane & 15, k
+// segment c = lane >> 4) forms the integer sum of its 16 k per group with two
+// instructions and adds P * s_x * s_w to a per-lane fp32 partial.  The four
+// segment partials of a column are summed once after the K loop (shuffles),
+// the four waves' partials in LDS in wave order, and the result is laid into
+// the MFMA accumulator layout for the LoRA-up and the store.  Workgroup and
+// wave decomposition are those of gemm_decode_kernel.
+// ---------------------------------------------------------------------------
+template <int MR, int KB>
+struct DotBatch {
+  v4u w[KB];          // weight codes, 16 B per lane per k-pair
+  v4u x[KB][MR];      // activation codes of the lane's k segment, per row
+  uint32_t sw[KB];    // s_w of the lane's column, both groups
+  uint32_t sx[KB][MR];
+};
+
+// Bases and the k-pair index are wave-uniform, per-lane offsets 32-bit (one
+// column tile of codes is at most 2^24 / 2 bytes): the weight and activation
+// codes load with a scalar base and an immediate offset, s_x with scalar loads.
+// TAIL batches clamp the k-pair to the last valid one and weight it 0.
+template <int MR, int KB, bool TAIL>
+__device__ __forceinline__ void dot_load(DotBatch<MR, KB>& d, const uint8_t* wq, const uint8_t* sw,
+                                         const uint8_t* xq, const uint8_t* sx, uint32_t lane_w,
+                                         uint32_t lane_sw, uint32_t lane_x, int pb, int p1) {
+  // batch bases are wave-uniform (scalar registers); the per-k-pair step is an
+  // immediate offset on top of the lane's 32-bit offset
+  const uint8_t* wb = wq + (size_t)pb * kTileBytes;
+  const uint8_t* swb = sw + (size_t)pb * 64u;
+  const uint8_t* xb = xq + (size_t)pb * kTileBytes;
+  const uint8_t* sxb = sx + (size_t)pb * 64u;
+#pragma unroll
+  for (int u = 0; u < KB; ++u) {
+    const uint32_t q = (uint32_t)(TAIL && pb + u >= p1 ? p1 - 1 - pb : u);
+    d.w[u] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(wb + (lane_w + q * kTileBytes)));
+    d.sw[u] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(swb + (lane_sw + q * 64u)));
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      d.x[u][m] = *reinterpret_cast<const v4u*>(xb + (lane_x + q * kTileBytes + m * 16u));
+      d.sx[u][m] = *reinterpret_cast<const uint32_t*>(sxb + (q * 64u + m * 4u));
+    }
+  }
+  // keep every load of the batch ahead of the arithmetic that consumes it
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int MR, int KB, bool TAIL>
+__device__ __forceinline__ void dot_accumulate(const DotBatch<MR, KB>& d, float (&acc)[MR], int pb, int p1) {
+#pragma unroll
+  for (int u = 0; u < KB; ++u) {
+    if (TAIL && pb + u >= p1) break;   // wave-uniform
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float swf = half_bits_to_float((uint16_t)(d.sw[u] >> (16 * h)));
+#pragma unroll
+      for (int m = 0; m < MR; ++m) {
+        int P = __builtin_amdgcn_sdot8((int)d.w[u][2 * h], (int)d.x[u][m][2 * h], 0, false);
+        P = __builtin_amdgcn_sdot8((int)d.w[u][2 * h + 1], (int)d.x[u][m][2 * h + 1], P, false);
+        // s_x * s_w is exact in fp32; fma with +0 keeps it one mixed-precision op
+        const float s = __builtin_fmaf(half_bits_to_float((uint16_t)(d.sx[u][m] >> (16 * h))), swf, 0.f);
+        acc[m] = fmaf((float)P, s, acc[m]);
+      }
+    }
+  }
+}
+
+template <int MR, int RT, int KB>
+__global__ __launch_bounds__(256, 4) void gemm_decode_dot_kernel(GemmArgs g) {
+  constexpr int RTL = RT > 0 ? RT : 1;
+  __shared__ float red[kDecodeWaves][MR][16];
+  __shared__ v4f lred[RTL][kDecodeWaves][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t nt = blockIdx.x;
+  const int KP = (int)(g.K / kKPair);
+  const int per = (KP + kDecodeWaves - 1) / kDecodeWaves;
+  const int p0 = wave * per;
+  const int p1 = p0 + per < KP ? p0 + per : KP;
+  const int c = lane >> 4, r = lane & 15;
+  const uint8_t* wq = g.wq + (size_t)nt * KP * kTileBytes;
+  const uint8_t* sw = reinterpret_cast<const uint8_t*>(g.sw + (size_t)nt * KP * 32);
+  const uint8_t* sx = reinterpret_cast<const uint8_t*>(g.sx);
+  // row m of k segment c sits at lane m + 16c of an activation tile
+  const uint32_t lane_w = lane * 16u, lane_sw = r * 4u, lane_x = c * 256u;
+
+  v4f lsum[RTL];
+  v4h lup[RTL];
+#pragma unroll
+  for (int t = 0; t < RTL; ++t) lsum[t] = v4f{0.f, 0.f, 0.f, 0.f};
+  float af = 0.f, bf = 0.f;
+  if constexpr (RT > 0) {
+    if (r < g.M)   // rows >= M stay 0 and are never stored
+      for (int j = wave; j < g.ks; j += kDecodeWaves)
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+          lsum[t] += *reinterpret_cast<const v4f*>(g.la + ((size_t)j * 16 + r) * g.R + t * 16 + c * 4);
+    if (wave == 0) {
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+        lup[t] = *reinterpret_cast<const v4h*>(g.lup + (((size_t)nt * RT + t) * 64 + lane) * 4);
+    }
+  }
+  if (wave == 0) {
+    af = g.ca[nt * 16 + r];
+    bf = g.cb[nt * 16 + r];
+  }
+
+  float acc[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) acc[m] = 0.f;
+  int pb = p0;
+  for (; pb + KB <= p1; pb += KB) {
+    DotBatch<MR, KB> d;
+    dot_load<MR, KB, false>(d, wq, sw, g.xq, sx, lane_w, lane_sw, lane_x, pb, p1);
+    dot_accumulate<MR, KB, false>(d, acc, pb, p1);
+  }
+  if (pb < p1) {
+    DotBatch<MR, KB> d;
+    dot_load<MR, KB, true>(d, wq, sw, g.xq, sx, lane_w, lane_sw, lane_x, pb, p1);
+    dot_accumulate<MR, KB, true>(d, acc, pb, p1);
+  }
+
+  // sum the four k segments of each column (lanes r, r+16, r+32, r+48)
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+    acc[m] += __shfl_xor(acc[m], 16);
+    acc[m] += __shfl_xor(acc[m], 32);
+  }
+  if (c == 0) {
+#pragma unroll
+    for (int m = 0; m < MR; ++m) red[wave][m][r] = acc[m];
+  }
+#pragma unroll
+  for (int t = 0; t < RTL; ++t) lred[t][wave][lane] = lsum[t];
+  __syncthreads();
+  if (wave != 0) return;
+  // accumulator layout of a 16x16 tile: lane (c, r) holds rows 4c + ii of column r
+  v4f a = v4f{0.f, 0.f, 0.f, 0.f};
+  if (c == 0) {
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      float v = red[0][m][r];
+#pragma unroll
+      for (int w = 1; w < kDecodeWaves; ++w) v += red[w][m][r];
+      a[m] = v;
+    }
+  }
+  if constexpr (RT > 0) {
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      v4f l4 = lred[t][0][lane];
+#pragma unroll
+      for (int w = 1; w < kDecodeWaves; ++w) l4 += lred[t][w][lane];
+      v4h hi, lo;
+      split_f16(l4, hi, lo);
+      a = mfma_f16_16x16x16(hi, lup[t], a);
+      a = mfma_f16_16x16x16(lo, lup[t], a);
+    }
+  }
+  store_tile<MR>(g, a, 0, nt * 16, af, bf, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -623,10 +789,25 @@ static hipError_t launch_decode_mv(const GemmArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int MR>
+static hipError_t launch_decode_dot(const GemmArgs& a, hipStream_t stream) {
+  dim3 grid((unsigned)(a.N / 16)), block(64 * kDecodeWaves);
+  switch (a.R / 16) {
+    // k-pairs in flight per wave: as many as fit in 128 VGPRs without spills
+    case 0: gemm_decode_dot_kernel<MR, 0, 8><<<grid, block, 0, stream>>>(a); break;
+    case 1: gemm_decode_dot_kernel<MR, 1, 8><<<grid, block, 0, stream>>>(a); break;
+    case 2: gemm_decode_dot_kernel<MR, 2, MR == 1 ? 8 : 6><<<grid, block, 0, stream>>>(a); break;
+    case 3: gemm_decode_dot_kernel<MR, 3, MR == 1 ? 8 : 6><<<grid, block, 0, stream>>>(a); break;
+    case 4: gemm_decode_dot_kernel<MR, 4, MR == 1 ? 8 : 6><<<grid, block, 0, stream>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 static hipError_t launch_decode(const GemmArgs& a, hipStream_t stream) {
   switch (a.M) {
-    case 1: return launch_decode_mv<1>(a, stream);
-    case 2: return launch_decode_mv<2>(a, stream);
+    case 1: return launch_decode_dot<1>(a, stream);
+    case 2: return launch_decode_dot<2>(a, stream);
     case 3: return launch_decode_mv<3>(a, stream);
     default: return launch_decode_mv<4>(a, stream);
   }

@@ -6,7 +6,7 @@
 // LoRA down-projection lora_act = X L_down on the fp16 values.  Section 2.3 /
 // 3.10: weights are repacked once at load into the kernel's layout.
 //
-// gfx950 design: one workgroup of 4 or 16 waves per (16-row tile, k-pair
+// gfx950 design: one workgroup of 4, 8 or 16 waves per (16-row tile, k-pair
 // range); a wave owns whole 16 x 128 k-pairs.  Lane l = r + 16c loads the 32 fp16 values
 // of row r at k = 128p + 64j + 16c + [0,16) (j = group in the pair) with four
 // 128-bit loads, and those registers serve three purposes without any LDS
@@ -30,29 +30,58 @@ namespace w4a4 {
 // two integers of at most 11 bits times a power of two; unless it is exactly
 // a half-integer, it lies at least 2^-13 away from every half-integer, far
 // beyond the error of t = x * rs (< 2^-19 for |x/s| <= 8.5), so rint(t) is the
-// nearest integer to x/s -- the same as the nearest integer to fl32(x/s).  When x/s is exactly a half-integer, fl32(x/s)
-// is that half-integer and the rule rounds it to the even neighbour.  The
-// residual f = x - n*s is computed exactly by one fma (n*s has <= 15
-// significant bits and |f| <= s/2, so f needs <= 12 bits), and x/s is a
-// half-integer exactly when |f| == s/2; then n is moved to the even side.
+// nearest integer to x/s -- the same as the nearest integer to fl32(x/s).
+// When x/s is exactly a half-integer, fl32(x/s) is that half-integer and the
+// rule rounds it to the even neighbour.  The residual f = x - n*s is exact
+// (n*s has <= 15 significant bits and |f| <= s/2, so f needs <= 12 bits), and
+// x/s is a half-integer exactly when |f| == s/2.  Such ties are rare, so the
+// fix-up runs on a wave-uniform branch taken only when some lane has one.
+//
+// Packing: for an integer n in [-8, 7] and j < 4, n + 1.5 * 2^(23 - 4j) is
+// exact and its bit pattern holds n << 4j (two's complement) in bits
+// [4j, 4j + 4), so one and-or puts a code in place within a 16-bit half.
 __device__ __forceinline__ uint32_t quantize8(v8h v, float sf, float rs) {
-  uint32_t out = 0;
+  float n[8], f[8];
+  bool tie = false;
   const float half_s = 0.5f * sf;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const float x = (float)v[i];
-    float n = __builtin_rintf(x * rs);
-    const float f = __builtin_fmaf(-n, sf, x);
-    if (__builtin_fabsf(f) == half_s && (((int)n) & 1)) n += __builtin_copysignf(1.0f, f);
-    n = __builtin_amdgcn_fmed3f(n, -8.0f, 7.0f);
-    out |= (uint32_t((int)n) & 0xFu) << (4 * i);
+    n[i] = __builtin_rintf(x * rs);
+    f[i] = __builtin_fmaf(-n[i], sf, x);
+    tie |= __builtin_fabsf(f[i]) == half_s;
   }
-  return out;
+  if (__builtin_amdgcn_ballot_w64(tie) != 0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bool fix = (__builtin_fabsf(f[i]) == half_s) & ((((int)n[i]) & 1) != 0);
+      n[i] = fix ? n[i] + __builtin_copysignf(1.0f, f[i]) : n[i];
+    }
+  }
+  // two 16-bit halves, each built with the biases 1.5 * 2^(23 - 4j), j < 4,
+  // whose own set bits (22 and up) stay clear of bits [0, 16)
+  uint32_t half[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int j = i & 3;
+    const float q = __builtin_amdgcn_fmed3f(n[i], -8.0f, 7.0f);
+    const float biased = q + __builtin_ldexpf(1.5f, 23 - 4 * j);   // constant per i
+    half[i >> 2] |= __builtin_bit_cast(uint32_t, biased) & (0xFu << (4 * j));
+  }
+  return half[0] | (half[1] << 16);
 }
 
-__device__ __forceinline__ float absmax8(v8h v, float m) {
+// max |x| over 8 fp16 values: for fp16, |x| orders like (bits & 0x7fff) as
+// unsigned integers, so the max is taken on the bit patterns.
+__device__ __forceinline__ uint32_t absmax8_bits(v8h v, uint32_t m) {
+  const v4u w = __builtin_bit_cast(v4u, v);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf((float)v[i]));
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t a = w[i] & 0x7FFF7FFFu;
+    const uint32_t lo = a & 0xFFFFu, hi = a >> 16;
+    m = m > lo ? m : lo;
+    m = m > hi ? m : hi;
+  }
   return m;
 }
 
@@ -68,8 +97,8 @@ __device__ __forceinline__ _Float16 group_scale(float amax) {
 // Grid (rows_padded/16, ks) x NW waves.  Workgroup (rt, j) handles the 16-row
 // tile rt and the k-pairs [j*KP/ks, (j+1)*KP/ks); its waves take every NW-th
 // k-pair.  The next k-pair's X loads are issued before the current one is
-// processed.  NW = 16 when there are few row tiles (more loads in flight per
-// tile), else 4.
+// processed.  NW (4, 8 or 16) follows the number of k-pairs per workgroup so
+// that few row tiles still give many waves.
 template <int RT, int NW>  // RT = R / 16 (0 = no LoRA)
 __global__ __launch_bounds__(NW * 64) void quantize_rows_kernel(
     const uint16_t* __restrict__ src, int64_t ld, int64_t rows, int64_t rows_padded, int64_t K,
@@ -112,9 +141,14 @@ __global__ __launch_bounds__(NW * 64) void quantize_rows_kernel(
     _Float16 sc[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      float am = absmax8(v[2 * h + 1], absmax8(v[2 * h], 0.0f));
-      am = fmaxf(am, __shfl_xor(am, 16));
-      am = fmaxf(am, __shfl_xor(am, 32));
+      uint32_t amb = absmax8_bits(v[2 * h + 1], absmax8_bits(v[2 * h], 0u));
+      // each shuffle is taken once, by every lane (a shuffle under a lane
+      // mask reads 0 from inactive source lanes)
+      const uint32_t o16 = (uint32_t)__shfl_xor((int)amb, 16);
+      amb = amb > o16 ? amb : o16;
+      const uint32_t o32 = (uint32_t)__shfl_xor((int)amb, 32);
+      amb = amb > o32 ? amb : o32;
+      const float am = half_bits_to_float((uint16_t)amb);
       const _Float16 s = group_scale(am);
       const float sf = (float)s;
       const float rs = __builtin_amdgcn_rcpf(sf);
@@ -191,10 +225,14 @@ hipError_t launch_quantize_rows(const uint16_t* src, int64_t ld, int64_t rows,
                                 const uint16_t* ldown_packed, uint8_t* codes,
                                 uint16_t* scales, float* lora_part,
                                 hipStream_t stream) {
+  // waves per workgroup: as many as the k-pairs of a workgroup allow (<= 16),
+  // but 8 when there are enough row tiles to fill the GPU anyway
   const int64_t wgs = rows_padded / 16 * ks;
-  const int64_t kp_per_wg = (K / kKPair + ks - 1) / ks;
-  if (wgs < 256 && kp_per_wg >= 8)
+  const int64_t kp_per_wg = (K / kKPair) / ks;
+  if (kp_per_wg >= 16 && wgs < 256)
     return launch_quantize_nw<16>(src, ld, rows, rows_padded, K, R, ks, ldown_packed, codes, scales, lora_part, stream);
+  if (kp_per_wg >= 8)
+    return launch_quantize_nw<8>(src, ld, rows, rows_padded, K, R, ks, ldown_packed, codes, scales, lora_part, stream);
   return launch_quantize_nw<4>(src, ld, rows, rows_padded, K, R, ks, ldown_packed, codes, scales, lora_part, stream);
 }
 

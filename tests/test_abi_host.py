@@ -31,6 +31,20 @@ def test_exports_every_declared_symbol():
     assert "SHAPE" in W.w4a4_status_string(2)
 
 
+def test_no_unresolved_library_symbols():
+    """Every kernel launch stub the library references is defined in it (a
+    stub the compiler fails to emit only shows up as an unresolved symbol)."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--undefined-only", W.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    bad = [l for l in out.splitlines() if "w4a4" in l]
+    assert not bad, bad
+
+
 def test_layout_sizes():
     N, K, R = 3072, 1024, 32
     tot, offs = W.w4a4_weight_layout(N, K, R)

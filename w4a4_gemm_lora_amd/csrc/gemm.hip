@@ -280,7 +280,7 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) uint8_t a_lds[kDecodeWaves][kDecodeBatch][kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t s_lds[kDecodeWaves][kTileBytes];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nt = blockIdx.x;
   const int64_t KP = g.K / kKPair;
   const int64_t per = (KP + kDecodeWaves - 1) / kDecodeWaves;
@@ -585,7 +585,7 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void gemm_tiled_kernel(GemmArgs g,
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NS][SLOTS + 1][kTileBytes];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int wm = wave / WN, wn = wave % WN;
   const int c = lane >> 4;
 
@@ -626,23 +626,35 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void gemm_tiled_kernel(GemmArgs g,
     const int64_t t = nt0 + (q - BMT);
     return t < nt_count ? t : nt_count - 1;
   };
+  // Copy sources at k-pair 0: the wave's operand tiles (wave-uniform
+  // pointers) and, for lanes l < 4*CPW, 16 B of the scales of tile
+  // wave*CPW + l/4 (64 B per tile: 16 rows x 2 groups fp16).
+  const uint8_t* src[CPW];
+#pragma unroll
+  for (int u = 0; u < CPW; ++u) {
+    const int q = wave * CPW + u;
+    const uint8_t* base = (q < CHUNKS ? q : CHUNKS - 1) < BMT ? g.xq : g.wq;
+    src[u] = base + (size_t)tile_index(q) * KP * kTileBytes;
+  }
+  const uint8_t* ssrc;
+  {
+    const int q = wave * CPW + ((lane >> 2) < CPW ? (lane >> 2) : CPW - 1);
+    const uint16_t* sbase = (q < CHUNKS ? q : CHUNKS - 1) < BMT ? g.sx : g.sw;
+    ssrc = reinterpret_cast<const uint8_t*>(sbase) + (size_t)tile_index(q) * KP * 64 + (lane & 3) * 16;
+  }
+  const uint32_t lane_off = lane * 16u;
   auto issue_copy = [&](int stage, int64_t p) {
 #pragma unroll
     for (int u = 0; u < CPW; ++u) {
-      const int q = wave * CPW + u;
-      const uint8_t* base = (q < CHUNKS ? q : CHUNKS - 1) < BMT ? g.xq : g.wq;
-      __builtin_amdgcn_global_load_lds(base + ((size_t)tile_index(q) * KP + p) * kTileBytes + lane * 16,
-                                       (lds_void*)&lds[stage][q][0], 16, 0, 0);
+      // (a local copy: clang's host pass drops the launch stub when the
+      // captured array element feeds the builtin directly)
+      const uint8_t* sp = src[u];
+      __builtin_amdgcn_global_load_lds(sp + (size_t)p * kTileBytes + lane_off,
+                                       (lds_void*)&lds[stage][wave * CPW + u][0], 16, 0, 0);
     }
-    // scales of this wave's tiles: 64 B (16 rows x 2 groups fp16) per tile,
-    // lane l < 4*CPW copies 16 B of tile wave*CPW + l/4
-    if (lane < 4 * CPW) {
-      const int q = wave * CPW + (lane >> 2);
-      const uint16_t* sbase = (q < CHUNKS ? q : CHUNKS - 1) < BMT ? g.sx : g.sw;
-      __builtin_amdgcn_global_load_lds(
-          reinterpret_cast<const uint8_t*>(sbase) + ((size_t)tile_index(q) * KP + p) * 64 + (lane & 3) * 16,
-          (lds_void*)&lds[stage][SLOTS][wave * CPW * 64], 16, 0, 0);
-    }
+    if (lane < 4 * CPW)
+      __builtin_amdgcn_global_load_lds(ssrc + (size_t)p * 64, (lds_void*)&lds[stage][SLOTS][wave * CPW * 64],
+                                       16, 0, 0);
   };
 
   v4f acc[TM][TN];

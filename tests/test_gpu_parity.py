@@ -267,6 +267,20 @@ def test_small_m_decode_shapes(M, K, N, R):
     assert np.all(np.isnan(run.host_y()[M:].astype(np.float64)))
 
 
+@pytest.mark.parametrize("cfg", range(7))
+def test_every_tile_shape(cfg, monkeypatch):
+    """Each M > 16 tile shape (forced) on a shape with ragged row and column
+    edges for all of them: M = 130 (9 row tiles), N = 208 (13 column tiles)."""
+    M, K, N, R = 130, 512, 208, 32
+    monkeypatch.setenv("W4A4_TILED_CFG", str(cfg))
+    case = workloads.random_case(M, K, N, R, seed=3000 + cfg)
+    _say(f"[tile shape {cfg}] M={M} K={K} N={N} R={R}")
+    run = GpuRun(case)
+    ref = O.linear(case["x"], case["lora_down"], case["lora_up"], case["col_scale"], case["bias"], w16=case["w"])
+    _check_y(run.host_y()[:M, :N], ref["y"], f"tile shape {cfg}")
+    assert np.all(np.isnan(run.host_y()[M:].astype(np.float64)))
+
+
 def test_strided_x_and_y():
     M, K, N, R = 40, 256, 64, 32
     case = workloads.random_case(M, K, N, R, seed=7)

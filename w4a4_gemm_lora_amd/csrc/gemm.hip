@@ -256,6 +256,19 @@ typedef __attribute__((address_space(3))) void lds_void;
 #define W4A4_WAIT_VMCNT(n) \
   __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
 
+// Exact fp32 scale products of one 16 x 16 tile and group h in the MFMA
+// accumulator layout, S[ii] = s_x[row 4c + ii] * s_w[col lane & 15], from one
+// v_mfma_f32_4x4x4_16b_f16.  sx_pair: the fp16 s_x of both groups of row
+// 4(lane / 16) + (lane & 3); sw_pair: the fp16 s_w of both groups of column
+// lane & 15.  The product sums over k = 0..3: A carries (s_x g0, s_x g1, 0, 0)
+// and B (s_w g0, 0, 0, 0) or (0, s_w g1, 0, 0), so only group h survives and
+// the product of two fp16 values is exact in fp32.
+__device__ __forceinline__ v4f scale_tile(uint32_t sx_pair, uint32_t sw_pair, int h) {
+  const v4h a = __builtin_bit_cast(v4h, v2u{sx_pair, 0u});
+  const v4h b = __builtin_bit_cast(v4h, v2u{sw_pair & (h ? 0xFFFF0000u : 0x0000FFFFu), 0u});
+  return __builtin_amdgcn_mfma_f32_4x4x4f16(a, b, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+}
+
 // ---------------------------------------------------------------------------
 // Decode kernel (M <= 16): weight-streaming, HBM-bound.
 // One workgroup per 16-column tile; its 4 waves split K into contiguous
@@ -352,18 +365,21 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_kernel(GemmArgs g) {
     for (int u = 0; u < kDecodeBatch; ++u) {
       if (pb + u < p1) {
         const v4u araw = *reinterpret_cast<const v4u*>(&a_lds[wave][u][lane * 16]);
-        const v8h sxv = *reinterpret_cast<const v8h*>(&s_lds[wave][u * 64 + c * 16]);
+        // s_x of row 4c + (lane & 3), both groups: the A operand of the scale MFMA
+        const uint32_t sxw = *reinterpret_cast<const uint32_t*>(&s_lds[wave][u * 64 + (4 * c + (lane & 3)) * 4]);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          float sxf[MV];
+          const v4f S = scale_tile(sxw, swv[u], h);
+          const v4i P = mfma_i8_16x16x64(expand_group(araw[2 * h], araw[2 * h + 1]),
+                                         expand_group(braw[u][2 * h], braw[u][2 * h + 1]), v4i{0, 0, 0, 0});
 #pragma unroll
-          for (int ii = 0; ii < MV; ++ii) sxf[ii] = (float)sxv[ii * 2 + h];
-          const float swf = half_bits_to_float((uint16_t)(swv[u] >> (16 * h))) * (1.0f / 256.0f);
-          acc = group_tile<MV>(acc, araw[2 * h], araw[2 * h + 1], braw[u][2 * h], braw[u][2 * h + 1], sxf, swf);
+          for (int ii = 0; ii < MV; ++ii) acc[ii] = fmaf((float)P[ii], S[ii], acc[ii]);
         }
       }
     }
   }
+
+  acc *= (1.0f / 256.0f);   // the int8 operands carry 16 q each
 
   // cross-wave sums in LDS (reusing a_lds), added by wave 0 in wave order
   __syncthreads();
@@ -589,26 +605,32 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void gemm_tiled_kernel(GemmArgs g,
   const int wm = wave / WN, wn = wave % WN;
   const int c = lane >> 4;
 
-  const int64_t nbm = (mt_count + BMT - 1) / BMT, nbn = (nt_count + BNT - 1) / BNT;
-  const int64_t nblk = nbm * nbn;
-  int64_t b = blockIdx.x;
+  // 32-bit tile arithmetic: the launcher guarantees nblk < 2^31.
+  const uint32_t nbm = (uint32_t)((mt_count + BMT - 1) / BMT), nbn = (uint32_t)((nt_count + BNT - 1) / BNT);
+  const uint32_t nblk = nbm * nbn;
+  uint32_t b = blockIdx.x;
   {
     // dispatch places workgroup b on XCD b % 8; give each XCD a contiguous range
-    const int64_t per_xcd = nblk / 8, extra = nblk % 8;
-    const int64_t xcd = b % 8, local = b / 8;
+    const uint32_t per_xcd = nblk >> 3, extra = nblk & 7;
+    const uint32_t xcd = b & 7, local = b >> 3;
     b = xcd * per_xcd + (xcd < extra ? xcd : extra) + local;
   }
   // Grouped order inside each XCD's range: kTileGroupRows row bands advance
   // together and column tiles are the outer index, so a B column tile is
-  // reused by the whole group while the group's A band stays in L2.
-  int64_t bm, bn;
+  // reused by the whole group while the group's A band stays in L2.  (With
+  // nbm > kTileGroupRows, nbn < nblk / kTileGroupRows, so group_size fits.)
+  uint32_t bm, bn;
   {
-    const int64_t group_size = (int64_t)kTileGroupRows * nbn;
-    const int64_t first_bm = (b / group_size) * kTileGroupRows;
-    const int64_t gm = nbm - first_bm < kTileGroupRows ? nbm - first_bm : kTileGroupRows;
-    const int64_t in_g = b % group_size;
-    bm = first_bm + in_g % gm;
+    uint32_t first_bm = 0, in_g = b, gm = nbm;
+    if (nbm > (uint32_t)kTileGroupRows) {
+      const uint32_t group_size = (uint32_t)kTileGroupRows * nbn;
+      const uint32_t grp = b / group_size;
+      first_bm = grp * kTileGroupRows;
+      in_g = b - grp * group_size;
+      gm = nbm - first_bm < (uint32_t)kTileGroupRows ? nbm - first_bm : (uint32_t)kTileGroupRows;
+    }
     bn = in_g / gm;
+    bm = first_bm + (in_g - bn * gm);
   }
   const int64_t mt0 = bm * BMT, nt0 = bn * BNT;
   const int64_t KP = g.K / kKPair;
@@ -663,16 +685,13 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void gemm_tiled_kernel(GemmArgs g,
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-#pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
-    if (s < KP) issue_copy(s, s);
-
-  // Epilogue operands, loaded now so that they arrive during the main loop:
-  // lora_act fragments (sum of the partials) of the wave's row tiles, L_up
-  // fragments and the affine of its columns.  Tiles past the edge read the
-  // last valid tile (never stored).
+  // Epilogue operands, loaded first so that they arrive during the main loop
+  // and the exact vmcnt waits below count only stage copies after them:
+  // lora_act fragments of the wave's row tiles (fp32; split into fp16 hi +
+  // lo after the loop), L_up fragments and the affine of its columns.  Tiles
+  // past the edge read the last valid tile (never stored).
   constexpr int RTL = RT > 0 ? RT : 1;
-  v4h la_hi[TM][RTL], la_lo[TM][RTL];
+  v4f la_f[TM][RTL];
   v4h lu_f[TN][RTL];
   float af[TN], bf[TN];
 #pragma unroll
@@ -690,12 +709,15 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void gemm_tiled_kernel(GemmArgs g,
     for (int i = 0; i < TM; ++i) {
       const int64_t mt = tile_index(wm * TM + i);
 #pragma unroll
-      for (int t = 0; t < RT; ++t) {
-        const v4f l4 = *reinterpret_cast<const v4f*>(g.la + (size_t)(mt * 16 + (lane & 15)) * g.R + t * 16 + c * 4);
-        split_f16(l4, la_hi[i][t], la_lo[i][t]);
-      }
+      for (int t = 0; t < RT; ++t)
+        la_f[i][t] = *reinterpret_cast<const v4f*>(g.la + (size_t)(mt * 16 + (lane & 15)) * g.R + t * 16 + c * 4);
     }
   }
+
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < KP) issue_copy(s, s);
+
   int st = 0;                      // == p % NS
   int st_next = (NS - 1) % NS;     // == (p + NS - 1) % NS
   for (int64_t p = 0; p < KP; ++p) {
@@ -735,24 +757,21 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void gemm_tiled_kernel(GemmArgs g,
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       v4i Ae[TM], Be[TN];
-      v4h xs[TM], ws[TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const v2u r2 = *reinterpret_cast<const v2u*>(&lds[st][wm * TM + i][lane * 16 + h * 8]);
         Ae[i] = expand_group(r2[0], r2[1]);
-        xs[i] = __builtin_bit_cast(v4h, v2u{h ? (sxw[i] >> 16) : (sxw[i] & 0xFFFFu), 0u});
       }
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const v2u r2 = *reinterpret_cast<const v2u*>(&lds[st][BMT + wn * TN + j][lane * 16 + h * 8]);
         Be[j] = expand_group(r2[0], r2[1]);
-        ws[j] = __builtin_bit_cast(v4h, v2u{h ? (sww[j] >> 16) : (sww[j] & 0xFFFFu), 0u});
       }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-          const v4f S = __builtin_amdgcn_mfma_f32_4x4x4f16(xs[i], ws[j], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          const v4f S = scale_tile(sxw[i], sww[j], h);
           const v4i P = mfma_i8_16x16x64(Ae[i], Be[j], v4i{0, 0, 0, 0});
 #pragma unroll
           for (int ii = 0; ii < 4; ++ii) acc[i][j][ii] = fmaf((float)P[ii], S[ii], acc[i][j][ii]);
@@ -779,8 +798,10 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void gemm_tiled_kernel(GemmArgs g,
       v4f a = acc[i][j];
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
-        a = mfma_f16_16x16x16(la_hi[i][t], lu_f[j][t], a);
-        a = mfma_f16_16x16x16(la_lo[i][t], lu_f[j][t], a);
+        v4h hi, lo;
+        split_f16(la_f[i][t], hi, lo);
+        a = mfma_f16_16x16x16(hi, lu_f[j][t], a);
+        a = mfma_f16_16x16x16(lo, lu_f[j][t], a);
       }
       store_tile4(g, a, mt * 16, nt * 16, af[j], bf[j], lane);
     }
@@ -831,6 +852,7 @@ template <int WM, int WN, int TM, int TN>
 static hipError_t launch_tiled_cfg(const GemmArgs& a, hipStream_t stream) {
   const int64_t mt = round_up16(a.M) / 16, nt = a.N / 16;
   const int64_t nblk = ((mt + WM * TM - 1) / (WM * TM)) * ((nt + WN * TN - 1) / (WN * TN));
+  if (nblk >= ((int64_t)1 << 31)) return hipErrorInvalidValue;   // the kernel's tile math is 32-bit
   dim3 grid((unsigned)nblk), block(64 * WM * WN);
   constexpr int NS = kTiledStages;
   switch (a.R / 16) {
@@ -844,36 +866,60 @@ static hipError_t launch_tiled_cfg(const GemmArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Tile shapes for M > 16, largest first: (rows x cols) of a workgroup.
+// Tile shapes for M > 16: a workgroup of WM x WN waves, each wave TM x TN
+// tiles of 16 x 16.  occ = workgroups one CU holds at once (from the VGPR and
+// LDS use of the instance).
 struct TiledCfg {
-  int bm, bn;
+  int wm, wn, tm, tn, occ;
 };
-constexpr TiledCfg kTiledCfgs[] = {{128, 128}, {64, 128}, {128, 64}, {64, 64}, {32, 64}};
+constexpr TiledCfg kTiledCfgs[] = {
+    {2, 2, 4, 4, 2},   // 128 x 128
+    {2, 2, 2, 4, 3},   //  64 x 128
+    {2, 2, 4, 2, 3},   // 128 x  64
+    {2, 2, 2, 2, 4},   //  64 x  64
+    {2, 2, 1, 2, 4},   //  32 x  64
+    {4, 1, 1, 3, 4},   //  64 x  48
+    {1, 4, 3, 1, 4},   //  48 x  64
+};
 constexpr int kNumTiledCfgs = (int)(sizeof(kTiledCfgs) / sizeof(kTiledCfgs[0]));
-constexpr int64_t kTiledMinWorkgroups = 512;   // two per CU (latency hiding beats tile reuse here)
 
-// W4A4_TILED_CFG=<index into kTiledCfgs> forces a tile shape (tuning aid).
+// W4A4_TILED_CFG=<index into kTiledCfgs> forces a tile shape (tuning and
+// test aid; read at every launch so that one process can cover every shape).
 static int tiled_override() {
-  static const int v = [] {
-    const char* e = std::getenv("W4A4_TILED_CFG");
-    if (!e || !e[0]) return -1;
-    const int i = std::atoi(e);
-    return (i >= 0 && i < kNumTiledCfgs) ? i : -1;
-  }();
-  return v;
+  const char* e = std::getenv("W4A4_TILED_CFG");
+  if (!e || !e[0]) return -1;
+  const int i = std::atoi(e);
+  return (i >= 0 && i < kNumTiledCfgs) ? i : -1;
 }
 
-static int pick_tiled(int64_t M, int64_t N) {
+// Makespan model of a launch on 256 CUs x 4 SIMDs.  Workgroups spread evenly
+// over the CUs, so the busiest SIMD runs ceil(ceil(nblk / 256) * waves / 4)
+// waves one after another or interleaved (the kernel is bound by instruction
+// issue); a wave's cost is its tiles times the per-tile cost of its shape
+// (integer MFMA, scale MFMA and the per-group convert + fma are fixed per
+// tile; the nibble expansion is shared by a wave's row and column tiles),
+// plus a fixed prologue / epilogue share.  Units: SIMD cycles per k-pair.
+static double tiled_cost(const TiledCfg& c, int64_t mt, int64_t nt, int64_t kp) {
+  const int64_t bmt = c.wm * c.tm, bnt = c.wn * c.tn;
+  const int64_t nblk = ((mt + bmt - 1) / bmt) * ((nt + bnt - 1) / bnt);
+  const int64_t per_cu = (nblk + 255) / 256;
+  const int64_t waves_per_simd = (per_cu * c.wm * c.wn + 3) / 4;
+  const double tiles = (double)(c.tm * c.tn);
+  const double per_tile = 2.0 * (16.5 + 8.6 + 8 * 2.8 + 5 * 2.8) +
+                          2.0 * 6 * 2.8 * (double)(c.tm + c.tn) / tiles;
+  const double fixed = 900.0 + 150.0 * tiles;   // prologue, LoRA-up and store per wave
+  return (double)waves_per_simd * (tiles * per_tile * (double)kp + fixed);
+}
+
+static int pick_tiled(int64_t M, int64_t N, int64_t K) {
   if (tiled_override() >= 0) return tiled_override();
-  const int64_t mt = round_up16(M) / 16, nt = N / 16;
+  const int64_t mt = round_up16(M) / 16, nt = N / 16, kp = K / kKPair;
   int best = 0;
-  int64_t best_n = -1;
+  double best_c = 0;
   for (int i = 0; i < kNumTiledCfgs; ++i) {
-    const int64_t n = ((mt + kTiledCfgs[i].bm / 16 - 1) / (kTiledCfgs[i].bm / 16)) *
-                      ((nt + kTiledCfgs[i].bn / 16 - 1) / (kTiledCfgs[i].bn / 16));
-    if (n >= kTiledMinWorkgroups) return i;
-    if (n > best_n) {
-      best_n = n;
+    const double c = tiled_cost(kTiledCfgs[i], mt, nt, kp);
+    if (i == 0 || c < best_c) {
+      best_c = c;
       best = i;
     }
   }
@@ -909,12 +955,14 @@ hipError_t launch_gemm(const GemmArgs& a, int variant, hipStream_t stream) {
       return launch_decode(a, stream);
     case kPrefill:
       if (a.ks != 1) return hipErrorInvalidValue;   // lora_splits() is 1 for M > 16
-      switch (pick_tiled(a.M, a.N)) {
+      switch (pick_tiled(a.M, a.N, a.K)) {
         case 0: return launch_tiled_cfg<2, 2, 4, 4>(a, stream);
         case 1: return launch_tiled_cfg<2, 2, 2, 4>(a, stream);
         case 2: return launch_tiled_cfg<2, 2, 4, 2>(a, stream);
         case 3: return launch_tiled_cfg<2, 2, 2, 2>(a, stream);
-        default: return launch_tiled_cfg<2, 2, 1, 2>(a, stream);
+        case 4: return launch_tiled_cfg<2, 2, 1, 2>(a, stream);
+        case 5: return launch_tiled_cfg<4, 1, 1, 3>(a, stream);
+        default: return launch_tiled_cfg<1, 4, 3, 1>(a, stream);
       }
     default:
       return launch_generic_rt<2, 2, false>(a, 0, mt, 0, nt, nullptr, 0, stream);

@@ -243,7 +243,9 @@ def test_ragged_and_rank_edges(M, K, N, R):
 
 @pytest.mark.parametrize("M,K,N,R", [(1, 128, 48, 0), (2, 384, 32, 64), (1, 1664, 64, 48),
                                      (2, 4864, 48, 32), (1, 4864, 16, 64), (2, 1664, 48, 16),
-                                     (3, 1664, 32, 32)])
+                                     (3, 1664, 32, 32), (3, 4864, 32, 48), (4, 1664, 32, 64),
+                                     (4, 4864, 48, 16), (4, 384, 16, 0), (8, 1664, 32, 32),
+                                     (13, 4864, 48, 64)])
 def test_small_m_decode_shapes(M, K, N, R):
     """M <= 16 kernels over uneven per-wave k-pair ranges (a wave with no
     k-pairs, ranges that are not a multiple of the batch), every rank, and

@@ -272,26 +272,22 @@ __device__ __forceinline__ v4f scale_tile(uint32_t sx_pair, uint32_t sw_pair, in
 // ---------------------------------------------------------------------------
 // Decode kernel (M <= 16): weight-streaming, HBM-bound.
 // One workgroup per 16-column tile; its 4 waves split K into contiguous
-// ranges of up to kDecodeBatch k-pairs at a time.  Per batch a wave first
-// copies the activation codes and scales of its range into LDS
-// (global_load_lds; they are shared by every workgroup and come from L2) and
-// then issues its weight and weight-scale loads (non-temporal: every weight
-// byte is used once).  A vmcnt wait that leaves the weight loads in flight
-// publishes the activation copies; the compiler's own waits then let k-pair u
-// start as soon as its weights arrive.  Everything the epilogue needs (LoRA
-// partial sums, L_up, a, b) is loaded before the stream, so the tail costs no
-// extra memory round trip.  Partial accumulators are summed in LDS in wave
-// order (deterministic).  MV = accumulator rows per lane that
-// hold valid output (for M <= 4 every valid row sits in lanes 0..15).
+// ranges, worked through in batches of KB k-pairs: a wave issues the whole
+// batch of loads -- weight codes and scales (non-temporal: every weight byte
+// is used once) and activation codes and scales (shared by every workgroup,
+// served by L2) -- and then computes k-pair by k-pair as the data lands.  Everything
+// the epilogue needs (LoRA partial sums, L_up, a, b) is loaded before the
+// stream, so the tail costs no extra memory round trip.
+// Partial accumulators are summed in LDS in wave order (deterministic).
+// MV = accumulator rows per lane that hold valid output (for M <= 4 every
+// valid row sits in lanes 0..15).
 // ---------------------------------------------------------------------------
 constexpr int kDecodeWaves = 4;
-constexpr int kDecodeBatch = 8;
 
-template <int MV, int RT>
+template <int MV, int RT, int KB>
 __global__ __launch_bounds__(256, 4) void gemm_decode_kernel(GemmArgs g) {
   constexpr int RTL = RT > 0 ? RT : 1;
-  __shared__ __attribute__((aligned(1024))) uint8_t a_lds[kDecodeWaves][kDecodeBatch][kTileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t s_lds[kDecodeWaves][kTileBytes];
+  __shared__ v4f red_lds[(1 + RTL) * kDecodeWaves * 64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nt = blockIdx.x;
@@ -329,48 +325,33 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_kernel(GemmArgs g) {
   v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
   const uint8_t* wq = g.wq + (size_t)nt * KP * kTileBytes + lane * 16;
   const uint16_t* sw = g.sw + (size_t)nt * KP * 32 + r * 2;
-  for (int64_t pb = p0; pb < p1; pb += kDecodeBatch) {
-    // Only lanes holding rows < M carry data (row r = lane & 15); the other
-    // LDS slots keep stale bytes, which only reach accumulator rows >= M
-    // (never stored).
-    if (r < g.M) {
+  // The activation tile is lane-ordered like the MFMA A operand, so lane l
+  // loads its own 16 bytes; rows >= M are zero codes with zero scales.
+  const uint8_t* xq = g.xq + lane * 16;
+  const uint8_t* sxq = reinterpret_cast<const uint8_t*>(g.sx) + (4 * c + (lane & 3)) * 4;
+  for (int64_t pb = p0; pb < p1; pb += KB) {
+    // All loads of a batch are plain vector loads issued in k-pair order (one
+    // kind of outstanding access keeps the compiler's vmcnt waits
+    // incremental, so k-pair u starts as soon as its own data has landed).
+    // Issuing the whole batch at once keeps the most bytes in flight.
+    v4u braw[KB], araw[KB];
+    uint32_t swv[KB], sxw[KB];
 #pragma unroll
-      for (int u = 0; u < kDecodeBatch; ++u) {
-        const int64_t p = pb + u < p1 ? pb + u : p1 - 1;
-        __builtin_amdgcn_global_load_lds(g.xq + (size_t)p * kTileBytes + lane * 16,
-                                         (lds_void*)&a_lds[wave][u][0], 16, 0, 0);
-      }
-    }
-    {
-      // activation scales: 64 B per k-pair; lane l fetches part (l & 3) of k-pair l / 4
-      int64_t p = pb + (lane >> 2);
-      p = p < p1 ? p : p1 - 1;
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(g.sx) + (size_t)p * 64 + (lane & 3) * 16,
-                                       (lds_void*)&s_lds[wave][0], 16, 0, 0);
-    }
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    v4u braw[kDecodeBatch];
-    uint32_t swv[kDecodeBatch];
-#pragma unroll
-    for (int u = 0; u < kDecodeBatch; ++u) {
+    for (int u = 0; u < KB; ++u) {
       const int64_t p = pb + u < p1 ? pb + u : p1 - 1;   // clamped duplicates are skipped below
       braw[u] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(wq + (size_t)p * kTileBytes));
       swv[u] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(sw + (size_t)p * 32));
+      araw[u] = *reinterpret_cast<const v4u*>(xq + (size_t)p * kTileBytes);
+      sxw[u] = *reinterpret_cast<const uint32_t*>(sxq + (size_t)p * 64);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    W4A4_WAIT_VMCNT(2 * kDecodeBatch);   // everything older than the weight loads has landed
-    asm volatile("" ::: "memory");
 #pragma unroll
-    for (int u = 0; u < kDecodeBatch; ++u) {
+    for (int u = 0; u < KB; ++u) {
       if (pb + u < p1) {
-        const v4u araw = *reinterpret_cast<const v4u*>(&a_lds[wave][u][lane * 16]);
-        // s_x of row 4c + (lane & 3), both groups: the A operand of the scale MFMA
-        const uint32_t sxw = *reinterpret_cast<const uint32_t*>(&s_lds[wave][u * 64 + (4 * c + (lane & 3)) * 4]);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const v4f S = scale_tile(sxw, swv[u], h);
-          const v4i P = mfma_i8_16x16x64(expand_group(araw[2 * h], araw[2 * h + 1]),
+          const v4f S = scale_tile(sxw[u], swv[u], h);
+          const v4i P = mfma_i8_16x16x64(expand_group(araw[u][2 * h], araw[u][2 * h + 1]),
                                          expand_group(braw[u][2 * h], braw[u][2 * h + 1]), v4i{0, 0, 0, 0});
 #pragma unroll
           for (int ii = 0; ii < MV; ++ii) acc[ii] = fmaf((float)P[ii], S[ii], acc[ii]);
@@ -381,9 +362,9 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_kernel(GemmArgs g) {
 
   acc *= (1.0f / 256.0f);   // the int8 operands carry 16 q each
 
-  // cross-wave sums in LDS (reusing a_lds), added by wave 0 in wave order
+  // cross-wave sums in LDS, added by wave 0 in wave order
   __syncthreads();
-  v4f* red = reinterpret_cast<v4f*>(&a_lds[0][0][0]);   // [1 + RTL][waves][64]
+  v4f* red = red_lds;   // [1 + RTL][waves][64]
   red[wave * 64 + lane] = acc;
 #pragma unroll
   for (int t = 0; t < RTL; ++t) red[((1 + t) * kDecodeWaves + wave) * 64 + lane] = lsum[t];
@@ -407,69 +388,102 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_kernel(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------
-// Decode kernel for M <= 2: no nibble expansion and no MFMA in the K loop.
+// Decode kernel for M <= 4: no nibble expansion and no MFMA in the K loop.
 // v_dot8_i32_i4 multiplies the 8 signed nibbles of a weight dword with the
 // 8 nibbles of the matching activation dword (the packed layouts pair the
 // same k in the same nibble position), so lane (column r = lane & 15, k
-// segment c = lane >> 4) forms the integer sum of its 16 k per group with two
-// instructions and adds P * s_x * s_w to a per-lane fp32 partial.  The four
-// segment partials of a column are summed once after the K loop (shuffles),
-// the four waves' partials in LDS in wave order, and the result is laid into
-// the MFMA accumulator layout for the LoRA-up and the store.  Workgroup and
-// wave decomposition are those of gemm_decode_kernel.
+// segment c = lane >> 4) forms the integer sum of its 16 k per group and row
+// with two instructions and adds P * s_x * s_w to a per-lane fp32 partial.
+// Per batch of KB k-pairs a wave issues plain vector loads only: first the
+// activation codes of its k-pairs (rows < MR, 64 B per row and k-pair,
+// served by L2), then the weight codes and scales k-pair by k-pair
+// (non-temporal); s_x comes through scalar loads.  The activation codes are
+// parked in a per-wave LDS slice (read back as 16-lane broadcasts), so the
+// compiler's vmcnt waits stay incremental and k-pair u starts as soon as its
+// own weights have landed.
+// The four segment partials of a column are summed once after the K loop
+// (shuffles), the four waves' partials in LDS in wave order, and the result
+// is laid into the MFMA accumulator layout for the LoRA-up and the store.
+// Workgroup and wave decomposition are those of gemm_decode_kernel.
 // ---------------------------------------------------------------------------
 template <int MR, int KB>
 struct DotBatch {
+  static constexpr int kChunks = KB * MR * 4;          // 16 B activation chunks
+  static constexpr int kXLoads = (kChunks + 63) / 64;  // per-lane loads for them
   v4u w[KB];          // weight codes, 16 B per lane per k-pair
-  v4u x[KB][MR];      // activation codes of the lane's k segment, per row
   uint32_t sw[KB];    // s_w of the lane's column, both groups
   uint32_t sx[KB][MR];
+  v4u x[kXLoads];     // activation chunk(s) of this lane, before they go to LDS
 };
 
 // Bases and the k-pair index are wave-uniform, per-lane offsets 32-bit (one
-// column tile of codes is at most 2^24 / 2 bytes): the weight and activation
-// codes load with a scalar base and an immediate offset, s_x with scalar loads.
-// TAIL batches clamp the k-pair to the last valid one and weight it 0.
+// column tile of codes is at most 2^24 / 2 bytes).  TAIL batches clamp the
+// k-pair to the last valid one (its contribution is skipped).  Chunk q of a
+// batch is (k-pair q / (4 MR), row (q / 4) % MR, segment q % 4).  The
+// activation chunks are issued first and s_x comes through scalar loads, so
+// the wait that parks the chunks in LDS leaves the weight loads in flight.
 template <int MR, int KB, bool TAIL>
 __device__ __forceinline__ void dot_load(DotBatch<MR, KB>& d, const uint8_t* wq, const uint8_t* sw,
-                                         const uint8_t* xq, const uint8_t* sx, uint32_t lane_w,
-                                         uint32_t lane_sw, uint32_t lane_x, int pb, int p1) {
-  // batch bases are wave-uniform (scalar registers); the per-k-pair step is an
-  // immediate offset on top of the lane's 32-bit offset
+                                         const uint8_t* xq, const uint8_t* sx, int lane, int pb, int p1) {
+  using D = DotBatch<MR, KB>;
+  const uint32_t lane_w = lane * 16u, lane_sw = (lane & 15) * 4u;
+  // batch bases are wave-uniform (scalar registers)
   const uint8_t* wb = wq + (size_t)pb * kTileBytes;
   const uint8_t* swb = sw + (size_t)pb * 64u;
   const uint8_t* xb = xq + (size_t)pb * kTileBytes;
   const uint8_t* sxb = sx + (size_t)pb * 64u;
 #pragma unroll
-  for (int u = 0; u < KB; ++u) {
-    const uint32_t q = (uint32_t)(TAIL && pb + u >= p1 ? p1 - 1 - pb : u);
-    d.w[u] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(wb + (lane_w + q * kTileBytes)));
-    d.sw[u] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(swb + (lane_sw + q * 64u)));
-#pragma unroll
-    for (int m = 0; m < MR; ++m) {
-      d.x[u][m] = *reinterpret_cast<const v4u*>(xb + (lane_x + q * kTileBytes + m * 16u));
-      d.sx[u][m] = *reinterpret_cast<const uint32_t*>(sxb + (q * 64u + m * 4u));
-    }
+  for (int i = 0; i < D::kXLoads; ++i) {
+    const int q = lane + 64 * i;
+    const int qc = q < D::kChunks ? q : D::kChunks - 1;
+    const int u = qc / (4 * MR), m = (qc >> 2) % MR, cc = qc & 3;
+    const uint32_t uq = (uint32_t)(TAIL && pb + u >= p1 ? p1 - 1 - pb : u);
+    // row m of k segment cc sits at lane m + 16 cc of an activation tile
+    d.x[i] = *reinterpret_cast<const v4u*>(xb + (uq * kTileBytes + (uint32_t)(m + 16 * cc) * 16u));
   }
-  // keep every load of the batch ahead of the arithmetic that consumes it
   __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int u = 0; u < KB; ++u) {
+    const uint32_t uq = (uint32_t)(TAIL && pb + u >= p1 ? p1 - 1 - pb : u);
+    d.w[u] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(wb + (lane_w + uq * kTileBytes)));
+    d.sw[u] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(swb + (lane_sw + uq * 64u)));
+#pragma unroll
+    for (int m = 0; m < MR; ++m) d.sx[u][m] = *reinterpret_cast<const uint32_t*>(sxb + (uq * 64u + m * 4u));
+    // issue in k-pair order, so that k-pair u waits only for its own loads
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Park the batch's activation chunks in the wave's LDS slice [KB][MR][4].
+template <int MR, int KB>
+__device__ __forceinline__ void dot_stage(const DotBatch<MR, KB>& d, v4u* xs, int lane) {
+  using D = DotBatch<MR, KB>;
+#pragma unroll
+  for (int i = 0; i < D::kXLoads; ++i) {
+    const int q = lane + 64 * i;
+    if (D::kChunks % 64 == 0 || q < D::kChunks) xs[q] = d.x[i];
+  }
 }
 
 template <int MR, int KB, bool TAIL>
-__device__ __forceinline__ void dot_accumulate(const DotBatch<MR, KB>& d, float (&acc)[MR], int pb, int p1) {
+__device__ __forceinline__ void dot_accumulate(const DotBatch<MR, KB>& d, const v4u* xs, float (&acc)[MR],
+                                               int c, int pb, int p1) {
 #pragma unroll
   for (int u = 0; u < KB; ++u) {
     if (TAIL && pb + u >= p1) break;   // wave-uniform
+    v4u xv[MR];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) xv[m] = xs[(u * MR + m) * 4 + c];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const float swf = half_bits_to_float((uint16_t)(d.sw[u] >> (16 * h)));
 #pragma unroll
       for (int m = 0; m < MR; ++m) {
-        int P = __builtin_amdgcn_sdot8((int)d.w[u][2 * h], (int)d.x[u][m][2 * h], 0, false);
-        P = __builtin_amdgcn_sdot8((int)d.w[u][2 * h + 1], (int)d.x[u][m][2 * h + 1], P, false);
+        int P = __builtin_amdgcn_sdot8((int)d.w[u][2 * h], (int)xv[m][2 * h], 0, false);
+        P = __builtin_amdgcn_sdot8((int)d.w[u][2 * h + 1], (int)xv[m][2 * h + 1], P, false);
         // s_x * s_w is exact in fp32; fma with +0 keeps it one mixed-precision op
-        const float s = __builtin_fmaf(half_bits_to_float((uint16_t)(d.sx[u][m] >> (16 * h))), swf, 0.f);
-        acc[m] = fmaf((float)P, s, acc[m]);
+        const float sc = __builtin_fmaf(half_bits_to_float((uint16_t)(d.sx[u][m] >> (16 * h))), swf, 0.f);
+        acc[m] = fmaf((float)P, sc, acc[m]);
       }
     }
   }
@@ -480,6 +494,7 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_dot_kernel(GemmArgs g) {
   constexpr int RTL = RT > 0 ? RT : 1;
   __shared__ float red[kDecodeWaves][MR][16];
   __shared__ v4f lred[RTL][kDecodeWaves][64];
+  __shared__ v4u xs_lds[kDecodeWaves][DotBatch<MR, KB>::kXLoads * 64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nt = blockIdx.x;
@@ -491,8 +506,7 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_dot_kernel(GemmArgs g) {
   const uint8_t* wq = g.wq + (size_t)nt * KP * kTileBytes;
   const uint8_t* sw = reinterpret_cast<const uint8_t*>(g.sw + (size_t)nt * KP * 32);
   const uint8_t* sx = reinterpret_cast<const uint8_t*>(g.sx);
-  // row m of k segment c sits at lane m + 16c of an activation tile
-  const uint32_t lane_w = lane * 16u, lane_sw = r * 4u, lane_x = c * 256u;
+  v4u* xs = &xs_lds[wave][0];
 
   v4f lsum[RTL];
   v4h lup[RTL];
@@ -522,13 +536,15 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_dot_kernel(GemmArgs g) {
   int pb = p0;
   for (; pb + KB <= p1; pb += KB) {
     DotBatch<MR, KB> d;
-    dot_load<MR, KB, false>(d, wq, sw, g.xq, sx, lane_w, lane_sw, lane_x, pb, p1);
-    dot_accumulate<MR, KB, false>(d, acc, pb, p1);
+    dot_load<MR, KB, false>(d, wq, sw, g.xq, sx, lane, pb, p1);
+    dot_stage(d, xs, lane);
+    dot_accumulate<MR, KB, false>(d, xs, acc, c, pb, p1);
   }
   if (pb < p1) {
     DotBatch<MR, KB> d;
-    dot_load<MR, KB, true>(d, wq, sw, g.xq, sx, lane_w, lane_sw, lane_x, pb, p1);
-    dot_accumulate<MR, KB, true>(d, acc, pb, p1);
+    dot_load<MR, KB, true>(d, wq, sw, g.xq, sx, lane, pb, p1);
+    dot_stage(d, xs, lane);
+    dot_accumulate<MR, KB, true>(d, xs, acc, c, pb, p1);
   }
 
   // sum the four k segments of each column (lanes r, r+16, r+32, r+48)
@@ -812,11 +828,12 @@ template <int MV>
 static hipError_t launch_decode_mv(const GemmArgs& a, hipStream_t stream) {
   dim3 grid((unsigned)(a.N / 16)), block(64 * kDecodeWaves);
   switch (a.R / 16) {
-    case 0: gemm_decode_kernel<MV, 0><<<grid, block, 0, stream>>>(a); break;
-    case 1: gemm_decode_kernel<MV, 1><<<grid, block, 0, stream>>>(a); break;
-    case 2: gemm_decode_kernel<MV, 2><<<grid, block, 0, stream>>>(a); break;
-    case 3: gemm_decode_kernel<MV, 3><<<grid, block, 0, stream>>>(a); break;
-    case 4: gemm_decode_kernel<MV, 4><<<grid, block, 0, stream>>>(a); break;
+    // k-pairs in flight per wave: as many as fit in 128 VGPRs without spills
+    case 0: gemm_decode_kernel<MV, 0, 8><<<grid, block, 0, stream>>>(a); break;
+    case 1: gemm_decode_kernel<MV, 1, 8><<<grid, block, 0, stream>>>(a); break;
+    case 2: gemm_decode_kernel<MV, 2, 8><<<grid, block, 0, stream>>>(a); break;
+    case 3: gemm_decode_kernel<MV, 3, 6><<<grid, block, 0, stream>>>(a); break;
+    case 4: gemm_decode_kernel<MV, 4, 6><<<grid, block, 0, stream>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -826,22 +843,25 @@ template <int MR>
 static hipError_t launch_decode_dot(const GemmArgs& a, hipStream_t stream) {
   dim3 grid((unsigned)(a.N / 16)), block(64 * kDecodeWaves);
   switch (a.R / 16) {
-    // k-pairs in flight per wave: as many as fit in 128 VGPRs without spills
     case 0: gemm_decode_dot_kernel<MR, 0, 8><<<grid, block, 0, stream>>>(a); break;
     case 1: gemm_decode_dot_kernel<MR, 1, 8><<<grid, block, 0, stream>>>(a); break;
-    case 2: gemm_decode_dot_kernel<MR, 2, MR == 1 ? 8 : 6><<<grid, block, 0, stream>>>(a); break;
-    case 3: gemm_decode_dot_kernel<MR, 3, MR == 1 ? 8 : 6><<<grid, block, 0, stream>>>(a); break;
-    case 4: gemm_decode_dot_kernel<MR, 4, MR == 1 ? 8 : 6><<<grid, block, 0, stream>>>(a); break;
+    case 2: gemm_decode_dot_kernel<MR, 2, 8><<<grid, block, 0, stream>>>(a); break;
+    // k-pairs in flight per wave: as many as fit in 128 VGPRs without spills
+    case 3: gemm_decode_dot_kernel<MR, 3, MR <= 2 ? 8 : 6><<<grid, block, 0, stream>>>(a); break;
+    case 4: gemm_decode_dot_kernel<MR, 4, MR <= 2 ? 8 : 6><<<grid, block, 0, stream>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+// M <= 4: nibble dot products (about 10 VALU per row and k-pair); larger M:
+// int8 MFMA on expanded nibbles (a fixed ~50 VALU + 4 MFMA per k-pair).
 static hipError_t launch_decode(const GemmArgs& a, hipStream_t stream) {
   switch (a.M) {
     case 1: return launch_decode_dot<1>(a, stream);
     case 2: return launch_decode_dot<2>(a, stream);
-    case 3: return launch_decode_mv<3>(a, stream);
+    case 3: return launch_decode_dot<3>(a, stream);
+    case 4: return launch_decode_dot<4>(a, stream);
     default: return launch_decode_mv<4>(a, stream);
   }
 }

@@ -25,6 +25,74 @@ if ROOT not in sys.path:
 METRIC = "W4A4+LoRA linear TOPS & HBM GB/s at 1 GPU; % of roofline per shape"
 PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA, 10^12 ops/s
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+# sources that define the GEMM kernels: a measured traffic figure is only
+# reported while they are unchanged
+KERNEL_SOURCES = ["w4a4_gemm_lora_amd/csrc/gemm.hip", "w4a4_gemm_lora_amd/csrc/device_common.hpp",
+                  "w4a4_gemm_lora_amd/csrc/w4a4_internal.hpp"]
+COPY_BYTES = 256 << 20      # the calibration copy moves this many bytes each way
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the GEMM kernel from committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE counters (scaled by a plain copy's counters), or
+    None if there are none for this workload or the kernel changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != kernel_source_hash():
+        return None
+    return rec["fetch_kib"] * 1024 * rec["fetch_factor"] + rec["write_kib"] * 1024 * rec["write_factor"]
+
+
+def _pmc_per_dispatch(csv_dir: str, counter: str, name_part: str):
+    """Mean per-dispatch value of one counter for kernels whose name holds name_part."""
+    import csv
+    import glob
+    vals, names = [], set()
+    for path in glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] == counter and name_part in row["Kernel_Name"]:
+                    vals.append(float(row["Counter_Value"]))
+                    names.add(row["Kernel_Name"])
+    if not vals:
+        raise SystemExit(f"no {counter} samples for kernels matching {name_part!r} under {csv_dir}")
+    return sum(vals) / len(vals), sorted(names)
+
+
+def ingest_pmc(workload, gemm_fetch_dir, gemm_write_dir, cal_fetch_dir, cal_write_dir, command):
+    """Write the traffic record of `workload` into profiles/traffic.json."""
+    fetch_kib, names = _pmc_per_dispatch(gemm_fetch_dir, "FETCH_SIZE", "gemm_")
+    write_kib, _ = _pmc_per_dispatch(gemm_write_dir, "WRITE_SIZE", "gemm_")
+    cal_f, _ = _pmc_per_dispatch(cal_fetch_dir, "FETCH_SIZE", "copy")
+    cal_w, _ = _pmc_per_dispatch(cal_write_dir, "WRITE_SIZE", "copy")
+    try:
+        with open(TRAFFIC_FILE) as f:
+            db = json.load(f)
+    except (OSError, ValueError):
+        db = {}
+    db[workload] = {
+        "kernels": names, "fetch_kib": round(fetch_kib, 1), "write_kib": round(write_kib, 1),
+        "fetch_factor": round(COPY_BYTES / 1024 / cal_f, 4), "write_factor": round(COPY_BYTES / 1024 / cal_w, 4),
+        "copy_fetch_kib": round(cal_f, 1), "copy_write_kib": round(cal_w, 1),
+        "source_sha": kernel_source_hash(), "command": command,
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(db, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps(db[workload]))
 
 
 def algorithmic_counts(M, N, K, R):
@@ -79,7 +147,15 @@ def main(argv=None):
     ap.add_argument("--rotate", type=int, default=1,
                     help="distinct weight blobs cycled through (defeat the 256 MB MALL for decode)")
     ap.add_argument("--per-graph", type=int, default=20, help="steps captured per HIP graph")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of a known size (counter calibration)")
+    ap.add_argument("--ingest-pmc", nargs=4, metavar=("GEMM_FETCH", "GEMM_WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="record rocprofv3 FETCH_SIZE / WRITE_SIZE output directories for --workload")
+    ap.add_argument("--pmc-command", default="", help="the profiling command, stored with --ingest-pmc")
     args = ap.parse_args(argv)
+    if args.ingest_pmc:
+        ingest_pmc(args.workload, *args.ingest_pmc, command=args.pmc_command)
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the layer's "
               "multi-GPU sharding is a design note, not a measured path.", file=sys.stderr)
@@ -91,6 +167,14 @@ def main(argv=None):
     from w4a4_gemm_lora_amd import workloads
 
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": COPY_BYTES, "copies": 10}), flush=True)
+        return 0
     case = workloads.generate(args.workload, M=args.m)
     M, K, N, R = case["M"], case["K"], case["N"], case["R"]
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
@@ -214,10 +298,24 @@ def main(argv=None):
                                    "GBps": round(c["q_bytes"] / (q_ms * 1e-3) / 1e9, 1),
                                    "event_bracketed_us": round(q_ms_ev * 1e3, 3)},
         },
-        "roofline": {"bound": "mfma", "achieved": round(lin_tops, 2), "peak": PEAK_INT8_TOPS,
-                     "unit": "TFLOP/s", "frac": round(lin_tops / PEAK_INT8_TOPS, 4), "traffic": None},
+        "roofline": None,
         "cpu_baseline": None,
     }
+    # Roofline of the dominant kernel (w4a4_linear): the decode kernels
+    # (M <= 16) stream the weights and are bound by HBM; the tiled kernel is
+    # bound by int8 MFMA issue.  achieved = algorithmic bytes or ops per
+    # launch / the launch's average duration measured above.
+    traffic = measured_traffic(args.workload if args.m is None else f"{args.workload}-{M}")
+    if out["config"]["variant"] == 1:
+        gbps = c["lin_bytes"] / (l_ms * 1e-3) / 1e9
+        out["roofline"] = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                           "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                           "traffic": None if traffic is None else int(traffic)}
+    else:
+        out["roofline"] = {"bound": "mfma", "achieved": round(lin_tops, 2), "peak": PEAK_INT8_TOPS,
+                           "unit": "TFLOP/s", "frac": round(lin_tops / PEAK_INT8_TOPS, 4),
+                           "traffic": None if traffic is None else int(traffic)}
+    out["roofline"]["algorithmic_bytes"] = c["lin_bytes"]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(case)
     print(json.dumps(out), flush=True)

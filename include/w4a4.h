@@ -59,8 +59,10 @@
  *   [2] lora_act: fp32 [S][Mp][R] row-major partial sums: partial j covers the
  *       k-pairs [j*KP/S, (j+1)*KP/S) (integer division) and lora_act is their
  *       sum taken in order j = 0..S-1.  S ("lora splits") depends only on
- *       (M, K) and is reported by w4a4_act_layout: S = 1 for M > 16, else
- *       S = clamp(KP / 4, 1, 8).
+ *       (M, K) and is reported by w4a4_act_layout: for M <= 16,
+ *       S = clamp(KP / 4, 1, 8); for M > 16, S is the smallest power of two
+ *       with ceil(M/16) * S >= 256, capped at 4 and at KP / 8 (every split
+ *       keeps at least 8 k-pairs; S = 1 when KP < 16 or ceil(M/16) >= 256).
  */
 #ifndef W4A4_H_
 #define W4A4_H_

@@ -58,18 +58,26 @@ def test_layout_sizes():
     Mp = 704
     assert offs[1] - offs[0] >= Mp * K // 2
     assert offs[2] - offs[1] >= Mp * (K // 64) * 2
-    assert ks == 1
+    assert ks == 1   # 8 k-pairs: too short to split
     assert tot >= offs[2] + ks * Mp * R * 4
 
 
 def test_lora_split_rule():
-    """S = 1 for M > 16, else clamp((K/128)/4, 1, 8) (the header's rule)."""
+    """The header's rule: M <= 16: clamp((K/128)/4, 1, 8); M > 16: the
+    smallest power of two S with ceil(M/16)*S >= 256, capped at 4 and KP/8."""
     def rule(M, K):
-        if M > 16:
-            return 1
-        return min(max(1, (K // 128) // 4), 8)
-    for M in (1, 4, 16, 17, 100, 700, 4096, 8192):
-        for K in (128, 256, 512, 1024, 3072, 4096):
+        kp = K // 128
+        if M <= 16:
+            return min(max(1, kp // 4), 8)
+        mt = -(-M // 16)
+        s = 1
+        while s < 4 and mt * s < 256 and 16 * s <= kp:
+            s *= 2
+        return s
+    assert rule(700, 1024) == 1 and rule(700, 3072) == 2 and rule(8192, 4096) == 1 and rule(17, 256) == 1
+    assert rule(130, 2048) == 2 and rule(40, 4096) == 4 and rule(100, 8192) == 4
+    for M in (1, 4, 16, 17, 100, 700, 2048, 4095, 4096, 8192):
+        for K in (128, 256, 512, 1024, 2048, 3072, 4096, 8192):
             _, _, ks = W.w4a4_act_layout(M, K, 32, with_splits=True)
             assert ks == rule(M, K), (M, K, ks)
 

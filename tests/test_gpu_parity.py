@@ -269,14 +269,18 @@ def test_small_m_decode_shapes(M, K, N, R):
     assert np.all(np.isnan(run.host_y()[M:].astype(np.float64)))
 
 
-@pytest.mark.parametrize("cfg", range(7))
-def test_every_tile_shape(cfg, monkeypatch):
+@pytest.mark.parametrize("cfg,K", [(c, 512) for c in range(7)] + [(c, 2048) for c in range(7)])
+def test_every_tile_shape(cfg, K, monkeypatch):
     """Each M > 16 tile shape (forced) on a shape with ragged row and column
-    edges for all of them: M = 130 (9 row tiles), N = 208 (13 column tiles)."""
-    M, K, N, R = 130, 512, 208, 32
+    edges for all of them: M = 130 (9 row tiles), N = 208 (13 column tiles);
+    K = 512 gives one lora_act partial, K = 2048 two (shapes that cannot sum
+    partials fall back to the model's pick)."""
+    M, N, R = 130, 208, 32
+    _, _, ks = W.w4a4_act_layout(M, K, R, with_splits=True)
+    assert ks == (1 if K == 512 else 2)
     monkeypatch.setenv("W4A4_TILED_CFG", str(cfg))
-    case = workloads.random_case(M, K, N, R, seed=3000 + cfg)
-    _say(f"[tile shape {cfg}] M={M} K={K} N={N} R={R}")
+    case = workloads.random_case(M, K, N, R, seed=3000 + cfg + K)
+    _say(f"[tile shape {cfg}] M={M} K={K} N={N} R={R} partials={ks}")
     run = GpuRun(case)
     ref = O.linear(case["x"], case["lora_down"], case["lora_up"], case["col_scale"], case["bias"], w16=case["w"])
     _check_y(run.host_y()[:M, :N], ref["y"], f"tile shape {cfg}")

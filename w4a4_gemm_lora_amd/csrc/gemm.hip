@@ -604,7 +604,7 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_dot_kernel(GemmArgs g) {
 // ---------------------------------------------------------------------------
 constexpr int kTileGroupRows = 8;
 
-template <int WM, int WN, int TM, int TN, int RT, int NS>
+template <int WM, int WN, int TM, int TN, int RT, int NS, int SPL>
 __global__ __launch_bounds__(WM * WN * 64, 2) void gemm_tiled_kernel(GemmArgs g, int64_t mt_count,
                                                                  int64_t nt_count) {
   constexpr int NW = WM * WN;
@@ -707,7 +707,6 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void gemm_tiled_kernel(GemmArgs g,
   // lo after the loop), L_up fragments and the affine of its columns.  Tiles
   // past the edge read the last valid tile (never stored).
   constexpr int RTL = RT > 0 ? RT : 1;
-  v4f la_f[TM][RTL];
   v4h lu_f[TN][RTL];
   float af[TN], bf[TN];
 #pragma unroll
@@ -719,20 +718,30 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void gemm_tiled_kernel(GemmArgs g,
     for (int t = 0; t < RT; ++t)
       lu_f[j][t] = *reinterpret_cast<const v4h*>(g.lup + (((size_t)nt * RT + t) * 64 + lane) * 4);
   }
+  // lora_act comes as g.ks <= SPL K-range partials; all of them are loaded
+  // here and summed in order in the epilogue (no wait before the K loop).
+  v4f la_p[SPL][TM][RTL];
   if constexpr (RT > 0) {
-    // for M > 16 lora_act is a single partial (one k range)
+    const size_t part = (size_t)round_up16(g.M) * g.R;   // floats per partial
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int64_t mt = tile_index(wm * TM + i);
+    for (int j = 0; j < SPL; ++j) {
+      if (j < g.ks) {   // uniform
 #pragma unroll
-      for (int t = 0; t < RT; ++t)
-        la_f[i][t] = *reinterpret_cast<const v4f*>(g.la + (size_t)(mt * 16 + (lane & 15)) * g.R + t * 16 + c * 4);
+        for (int i = 0; i < TM; ++i) {
+          const int64_t mt = tile_index(wm * TM + i);
+#pragma unroll
+          for (int t = 0; t < RT; ++t)
+            la_p[j][i][t] = *reinterpret_cast<const v4f*>(g.la + j * part + (size_t)(mt * 16 + (lane & 15)) * g.R +
+                                                          t * 16 + c * 4);
+        }
+      }
     }
   }
 
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
     if (s < KP) issue_copy(s, s);
+
 
   int st = 0;                      // == p % NS
   int st_next = (NS - 1) % NS;     // == (p + NS - 1) % NS
@@ -814,8 +823,12 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void gemm_tiled_kernel(GemmArgs g,
       v4f a = acc[i][j];
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
+        v4f l4 = la_p[0][i][t];
+#pragma unroll
+        for (int jj = 1; jj < SPL; ++jj)
+          if (jj < g.ks) l4 += la_p[jj][i][t];
         v4h hi, lo;
-        split_f16(la_f[i][t], hi, lo);
+        split_f16(l4, hi, lo);
         a = mfma_f16_16x16x16(hi, lu_f[j][t], a);
         a = mfma_f16_16x16x16(lo, lu_f[j][t], a);
       }
@@ -868,22 +881,44 @@ static hipError_t launch_decode(const GemmArgs& a, hipStream_t stream) {
 
 constexpr int kTiledStages = 4;
 
+template <int WM, int WN, int TM, int TN, int SPL>
+static hipError_t launch_tiled_spl(const GemmArgs& a, int64_t mt, int64_t nt, dim3 grid, dim3 block,
+                                   hipStream_t stream) {
+  constexpr int NS = kTiledStages;
+  switch (a.R / 16) {
+    case 0: gemm_tiled_kernel<WM, WN, TM, TN, 0, NS, SPL><<<grid, block, 0, stream>>>(a, mt, nt); break;
+    case 1: gemm_tiled_kernel<WM, WN, TM, TN, 1, NS, SPL><<<grid, block, 0, stream>>>(a, mt, nt); break;
+    case 2: gemm_tiled_kernel<WM, WN, TM, TN, 2, NS, SPL><<<grid, block, 0, stream>>>(a, mt, nt); break;
+    case 3:
+      if constexpr (SPL == 1 || TM == 1) {
+        gemm_tiled_kernel<WM, WN, TM, TN, 3, NS, SPL><<<grid, block, 0, stream>>>(a, mt, nt);
+        break;
+      } else {
+        return hipErrorInvalidValue;
+      }
+    case 4:
+      if constexpr (SPL == 1 || TM == 1) {
+        gemm_tiled_kernel<WM, WN, TM, TN, 4, NS, SPL><<<grid, block, 0, stream>>>(a, mt, nt);
+        break;
+      } else {
+        return hipErrorInvalidValue;
+      }
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// SPL = number of lora_act partials a wave sums: 1, or up to
+// kMaxTiledLoraSplits for the shapes where TM * (R/16) * 4 <= 16.
 template <int WM, int WN, int TM, int TN>
 static hipError_t launch_tiled_cfg(const GemmArgs& a, hipStream_t stream) {
   const int64_t mt = round_up16(a.M) / 16, nt = a.N / 16;
   const int64_t nblk = ((mt + WM * TM - 1) / (WM * TM)) * ((nt + WN * TN - 1) / (WN * TN));
   if (nblk >= ((int64_t)1 << 31)) return hipErrorInvalidValue;   // the kernel's tile math is 32-bit
   dim3 grid((unsigned)nblk), block(64 * WM * WN);
-  constexpr int NS = kTiledStages;
-  switch (a.R / 16) {
-    case 0: gemm_tiled_kernel<WM, WN, TM, TN, 0, NS><<<grid, block, 0, stream>>>(a, mt, nt); break;
-    case 1: gemm_tiled_kernel<WM, WN, TM, TN, 1, NS><<<grid, block, 0, stream>>>(a, mt, nt); break;
-    case 2: gemm_tiled_kernel<WM, WN, TM, TN, 2, NS><<<grid, block, 0, stream>>>(a, mt, nt); break;
-    case 3: gemm_tiled_kernel<WM, WN, TM, TN, 3, NS><<<grid, block, 0, stream>>>(a, mt, nt); break;
-    case 4: gemm_tiled_kernel<WM, WN, TM, TN, 4, NS><<<grid, block, 0, stream>>>(a, mt, nt); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  if (a.ks == 1) return launch_tiled_spl<WM, WN, TM, TN, 1>(a, mt, nt, grid, block, stream);
+  if constexpr (TM <= 2) return launch_tiled_spl<WM, WN, TM, TN, kMaxTiledLoraSplits>(a, mt, nt, grid, block, stream);
+  return hipErrorInvalidValue;   // pick_tiled never selects this shape with split lora_act
 }
 
 // Tile shapes for M > 16: a workgroup of WM x WN waves, each wave TM x TN
@@ -931,14 +966,23 @@ static double tiled_cost(const TiledCfg& c, int64_t mt, int64_t nt, int64_t kp) 
   return (double)waves_per_simd * (tiles * per_tile * (double)kp + fixed);
 }
 
-static int pick_tiled(int64_t M, int64_t N, int64_t K) {
-  if (tiled_override() >= 0) return tiled_override();
+// With split lora_act a wave holds TM * RT * kMaxTiledLoraSplits fragments
+// (4 VGPRs each) while it sums the partials; shapes that would hold more than
+// 16 are not eligible (the launcher builds no such instance).
+static bool tiled_fits(const TiledCfg& c, int R, int ks) {
+  return ks == 1 || c.tm * (R / 16) * kMaxTiledLoraSplits <= 16;
+}
+
+static int pick_tiled(int64_t M, int64_t N, int64_t K, int R, int ks) {
+  const int ov = tiled_override();
+  if (ov >= 0 && tiled_fits(kTiledCfgs[ov], R, ks)) return ov;
   const int64_t mt = round_up16(M) / 16, nt = N / 16, kp = K / kKPair;
-  int best = 0;
+  int best = -1;
   double best_c = 0;
   for (int i = 0; i < kNumTiledCfgs; ++i) {
+    if (!tiled_fits(kTiledCfgs[i], R, ks)) continue;
     const double c = tiled_cost(kTiledCfgs[i], mt, nt, kp);
-    if (i == 0 || c < best_c) {
+    if (best < 0 || c < best_c) {
       best_c = c;
       best = i;
     }
@@ -974,8 +1018,8 @@ hipError_t launch_gemm(const GemmArgs& a, int variant, hipStream_t stream) {
     case kDecode:
       return launch_decode(a, stream);
     case kPrefill:
-      if (a.ks != 1) return hipErrorInvalidValue;   // lora_splits() is 1 for M > 16
-      switch (pick_tiled(a.M, a.N, a.K)) {
+      if (a.ks < 1 || a.ks > kMaxTiledLoraSplits) return hipErrorInvalidValue;   // lora_splits() for M > 16
+      switch (pick_tiled(a.M, a.N, a.K, a.R, a.ks)) {
         case 0: return launch_tiled_cfg<2, 2, 4, 4>(a, stream);
         case 1: return launch_tiled_cfg<2, 2, 2, 4>(a, stream);
         case 2: return launch_tiled_cfg<2, 2, 4, 2>(a, stream);

@@ -97,8 +97,8 @@ __device__ __forceinline__ _Float16 group_scale(float amax) {
 // Grid (rows_padded/16, ks) x NW waves.  Workgroup (rt, j) handles the 16-row
 // tile rt and the k-pairs [j*KP/ks, (j+1)*KP/ks); its waves take every NW-th
 // k-pair.  The next k-pair's X loads are issued before the current one is
-// processed.  NW (4, 8 or 16) follows the number of k-pairs per workgroup so
-// that few row tiles still give many waves.
+// processed.  NW (2, 4, 8 or 16) follows the number of k-pairs per workgroup
+// so that few row tiles still give many waves.
 template <int RT, int NW>  // RT = R / 16 (0 = no LoRA)
 __global__ __launch_bounds__(NW * 64) void quantize_rows_kernel(
     const uint16_t* __restrict__ src, int64_t ld, int64_t rows, int64_t rows_padded, int64_t K,
@@ -136,6 +136,18 @@ __global__ __launch_bounds__(NW * 64) void quantize_rows_kernel(
   if (p < pend) load_x(p, v);
   for (; p < pend; p += NW) {
     const bool more = p + NW < pend;
+    // this k-pair's L_down fragments first (L2-resident, shared by every row
+    // tile), then the next k-pair's X: the LoRA MFMAs below then wait only
+    // for the former while the quantizer arithmetic covers their latency
+    constexpr int RTL = RT > 0 ? RT : 1;
+    v8h lb[RTL][4];
+    if constexpr (RT > 0) {
+      const _Float16* lp = reinterpret_cast<const _Float16*>(ldown) + (size_t)p * RT * 4 * 64 * 8;
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) lb[t][s] = *reinterpret_cast<const v8h*>(lp + ((size_t)(t * 4 + s) * 64 + lane) * 8);
+    }
     if (more) load_x(p + NW, vn);
     uint32_t d[4];
     _Float16 sc[2];
@@ -164,15 +176,10 @@ __global__ __launch_bounds__(NW * 64) void quantize_rows_kernel(
           uint32_t(__builtin_bit_cast(uint16_t, sc[0])) | (uint32_t(__builtin_bit_cast(uint16_t, sc[1])) << 16);
     }
     if constexpr (RT > 0) {
-      const _Float16* lp = reinterpret_cast<const _Float16*>(ldown) + (size_t)p * RT * 4 * 64 * 8;
 #pragma unroll
-      for (int t = 0; t < RT; ++t) {
+      for (int t = 0; t < RT; ++t)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          v8h b = *reinterpret_cast<const v8h*>(lp + ((size_t)(t * 4 + s) * 64 + lane) * 8);
-          acc[t] = mfma_f16_16x16x32(v[s], b, acc[t]);
-        }
-      }
+        for (int s = 0; s < 4; ++s) acc[t] = mfma_f16_16x16x32(v[s], lb[t][s], acc[t]);
     }
     if (more) {
 #pragma unroll
@@ -233,7 +240,9 @@ hipError_t launch_quantize_rows(const uint16_t* src, int64_t ld, int64_t rows,
     return launch_quantize_nw<16>(src, ld, rows, rows_padded, K, R, ks, ldown_packed, codes, scales, lora_part, stream);
   if (kp_per_wg >= 8)
     return launch_quantize_nw<8>(src, ld, rows, rows_padded, K, R, ks, ldown_packed, codes, scales, lora_part, stream);
-  return launch_quantize_nw<4>(src, ld, rows, rows_padded, K, R, ks, ldown_packed, codes, scales, lora_part, stream);
+  if (kp_per_wg >= 4)
+    return launch_quantize_nw<4>(src, ld, rows, rows_padded, K, R, ks, ldown_packed, codes, scales, lora_part, stream);
+  return launch_quantize_nw<2>(src, ld, rows, rows_padded, K, R, ks, ldown_packed, codes, scales, lora_part, stream);
 }
 
 // ---------------------------------------------------------------------------

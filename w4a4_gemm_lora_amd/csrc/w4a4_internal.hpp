@@ -33,11 +33,23 @@ struct ActGeom {
 // fits one 16-row tile (decode): each range writes its own LoRA-down partial
 // sum and the GEMM adds the partials.  For M > 16 there is one range.
 constexpr int kMaxLoraSplits = 8;
-
+constexpr int kMaxTiledLoraSplits = 4;
+// Number S of K-range partials of lora_act the quantizer writes (each its own
+// workgroup column).  M <= 16: clamp(KP/4, 1, 8), summed by the decode GEMM.
+// M > 16: enough K splits for >= 256 quantizer workgroups (a power of two,
+// at most 4, each split keeping >= 8 k-pairs), 1 once there are >= 256 row
+// tiles; the tiled GEMM loads every partial and sums them in its epilogue
+// (each extra partial costs start-up loads there, so short K is not split).
 inline int lora_splits(int64_t M, int64_t K) {
-  if (M > 16) return 1;
-  const int64_t ks = (K / kKPair) / 4;
-  return ks < 1 ? 1 : (ks > kMaxLoraSplits ? kMaxLoraSplits : (int)ks);
+  const int64_t kp = K / kKPair;
+  if (M <= 16) {
+    const int64_t ks = kp / 4;
+    return ks < 1 ? 1 : (ks > kMaxLoraSplits ? kMaxLoraSplits : (int)ks);
+  }
+  const int64_t mt = (M + 15) / 16;
+  int s = 1;
+  while (s < kMaxTiledLoraSplits && mt * s < 256 && 16 * s <= kp) s *= 2;
+  return s;
 }
 
 inline WeightGeom weight_geom(int64_t N, int64_t K, int R) {

@@ -94,22 +94,29 @@ __device__ __forceinline__ _Float16 group_scale(float amax) {
   return s;
 }
 
-// Grid (rows_padded/16, ks) x NW waves.  Workgroup (rt, j) handles the 16-row
-// tile rt and the k-pairs [j*KP/ks, (j+1)*KP/ks); its waves take every NW-th
-// k-pair.  The next k-pair's X loads are issued before the current one is
+// Grid (rows_padded/16 * 16/rh, ks) x NW waves.  Workgroup (x, j) handles
+// rows [r0, r0 + rh) of the 16-row tile rt = x / (16/rh), r0 = (x % (16/rh)) *
+// rh, and the k-pairs [j*KP/ks, (j+1)*KP/ks); its waves take every NW-th
+// k-pair.  The wave works on whole tiles (lanes of other rows read zeros) but
+// stores only its own rows' codes, scales and lora_act rows, so splitting a
+// tile's rows over 2 workgroups doubles the parallelism of small M without
+// partial sums (every such workgroup reads the whole L_down slice of its K
+// range, which is why tiles are not split further).  The next k-pair's X loads are issued before the current one is
 // processed.  NW (2, 4, 8 or 16) follows the number of k-pairs per workgroup
 // so that few row tiles still give many waves.
 template <int RT, int NW>  // RT = R / 16 (0 = no LoRA)
 __global__ __launch_bounds__(NW * 64) void quantize_rows_kernel(
     const uint16_t* __restrict__ src, int64_t ld, int64_t rows, int64_t rows_padded, int64_t K,
     const uint16_t* __restrict__ ldown, uint8_t* __restrict__ codes,
-    uint16_t* __restrict__ scales, float* __restrict__ lora_part) {
+    uint16_t* __restrict__ scales, float* __restrict__ lora_part, int rh) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r = lane & 15, c = lane >> 4;
-  const int64_t rt = blockIdx.x;
+  const int64_t rt = blockIdx.x / (16 / rh);
+  const int r0 = (int)(blockIdx.x % (16 / rh)) * rh;
   const int64_t row = rt * 16 + r;
-  const bool valid = row < rows;
+  const bool mine = r >= r0 && r < r0 + rh;   // this workgroup stores row r
+  const bool valid = mine && row < rows;
   const int64_t KP = K / kKPair;
   const int64_t ks = gridDim.y, j = blockIdx.y;
   const int64_t pbeg = j * KP / ks, pend = (j + 1) * KP / ks;
@@ -169,8 +176,8 @@ __global__ __launch_bounds__(NW * 64) void quantize_rows_kernel(
       sc[h] = valid ? s : (_Float16)0.0f;
     }
     uint8_t* tile = codes + (size_t)(rt * KP + p) * kTileBytes;
-    *reinterpret_cast<v4u*>(tile + lane * 16) = v4u{d[0], d[1], d[2], d[3]};
-    if (c == 0) {
+    if (mine) *reinterpret_cast<v4u*>(tile + lane * 16) = v4u{d[0], d[1], d[2], d[3]};
+    if (c == 0 && mine) {
       _Float16* sp = reinterpret_cast<_Float16*>(scales) + ((size_t)(rt * KP + p) * 16 + r) * 2;
       *reinterpret_cast<uint32_t*>(sp) =
           uint32_t(__builtin_bit_cast(uint16_t, sc[0])) | (uint32_t(__builtin_bit_cast(uint16_t, sc[1])) << 16);
@@ -200,12 +207,13 @@ __global__ __launch_bounds__(NW * 64) void quantize_rows_kernel(
     float* out = lora_part + (size_t)j * rows_padded * R;
     for (int e = threadIdx.x; e < RT * 4 * 64; e += blockDim.x) {
       const int ti = e >> 6, l = e & 63;
+      const int t = ti >> 2, i = ti & 3;
+      const int lr = (l >> 4) * 4 + i;   // row within the tile
+      if (lr < r0 || lr >= r0 + rh) continue;
       float s = 0.0f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) s += red[w][ti][l];
-      const int t = ti >> 2, i = ti & 3;
-      const int64_t orow = rt * 16 + (l >> 4) * 4 + i;
-      out[orow * R + t * 16 + (l & 15)] = s;
+      out[(rt * 16 + lr) * R + t * 16 + (l & 15)] = s;
     }
   }
 }
@@ -215,13 +223,16 @@ static hipError_t launch_quantize_nw(const uint16_t* src, int64_t ld, int64_t ro
                                      int64_t rows_padded, int64_t K, int R, int ks,
                                      const uint16_t* ldown_packed, uint8_t* codes,
                                      uint16_t* scales, float* lora_part, hipStream_t stream) {
-  dim3 grid((unsigned)(rows_padded / 16), (unsigned)ks), block(64 * NW);
+  // rows per workgroup: 8 (tiles split in two) when there are < 256 workgroups
+  int rh = 16;
+  while (rh > 8 && rows_padded / 16 * (16 / rh) * ks < 256) rh /= 2;
+  dim3 grid((unsigned)(rows_padded / 16 * (16 / rh)), (unsigned)ks), block(64 * NW);
   switch (R / 16) {
-    case 0: quantize_rows_kernel<0, NW><<<grid, block, 0, stream>>>(src, ld, rows, rows_padded, K, ldown_packed, codes, scales, lora_part); break;
-    case 1: quantize_rows_kernel<1, NW><<<grid, block, 0, stream>>>(src, ld, rows, rows_padded, K, ldown_packed, codes, scales, lora_part); break;
-    case 2: quantize_rows_kernel<2, NW><<<grid, block, 0, stream>>>(src, ld, rows, rows_padded, K, ldown_packed, codes, scales, lora_part); break;
-    case 3: quantize_rows_kernel<3, NW><<<grid, block, 0, stream>>>(src, ld, rows, rows_padded, K, ldown_packed, codes, scales, lora_part); break;
-    case 4: quantize_rows_kernel<4, NW><<<grid, block, 0, stream>>>(src, ld, rows, rows_padded, K, ldown_packed, codes, scales, lora_part); break;
+    case 0: quantize_rows_kernel<0, NW><<<grid, block, 0, stream>>>(src, ld, rows, rows_padded, K, ldown_packed, codes, scales, lora_part, rh); break;
+    case 1: quantize_rows_kernel<1, NW><<<grid, block, 0, stream>>>(src, ld, rows, rows_padded, K, ldown_packed, codes, scales, lora_part, rh); break;
+    case 2: quantize_rows_kernel<2, NW><<<grid, block, 0, stream>>>(src, ld, rows, rows_padded, K, ldown_packed, codes, scales, lora_part, rh); break;
+    case 3: quantize_rows_kernel<3, NW><<<grid, block, 0, stream>>>(src, ld, rows, rows_padded, K, ldown_packed, codes, scales, lora_part, rh); break;
+    case 4: quantize_rows_kernel<4, NW><<<grid, block, 0, stream>>>(src, ld, rows, rows_padded, K, ldown_packed, codes, scales, lora_part, rh); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -127,7 +127,7 @@ def cpu_baseline(case, budget_s=10.0):
                  w16=case["w"])
         n += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or n >= 50:
+        if el >= budget_s or n >= 1000:
             break
     c = algorithmic_counts(case["M"], case["N"], case["K"], case["R"])
     return {"value": round(c["layer_ops"] * n / el / 1e12, 6), "unit": "TOPS", "cores": int(cores),
@@ -144,8 +144,9 @@ def main(argv=None):
     ap.add_argument("--workload", default="mlp_up")
     ap.add_argument("--m", type=int, default=None, help="row count override (decode sweep)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--rotate", type=int, default=1,
-                    help="distinct weight blobs cycled through (defeat the 256 MB MALL for decode)")
+    ap.add_argument("--rotate", type=int, default=None,
+                    help="distinct weight blobs cycled through (default: 12 for decode, so that the "
+                         "weight stream comes from HBM and not the 256 MB MALL; 1 otherwise)")
     ap.add_argument("--per-graph", type=int, default=20, help="steps captured per HIP graph")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of a known size (counter calibration)")
@@ -175,6 +176,8 @@ def main(argv=None):
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": COPY_BYTES, "copies": 10}), flush=True)
         return 0
+    if args.rotate is None:
+        args.rotate = 12 if args.workload == "decode" else 1
     case = workloads.generate(args.workload, M=args.m)
     M, K, N, R = case["M"], case["K"], case["N"], case["R"]
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()

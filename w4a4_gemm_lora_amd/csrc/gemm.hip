@@ -508,17 +508,24 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_dot_kernel(GemmArgs g) {
   const uint8_t* sx = reinterpret_cast<const uint8_t*>(g.sx);
   v4u* xs = &xs_lds[wave][0];
 
-  v4f lsum[RTL];
+  // LoRA-down partials j = wave, wave + 4 (< ks) of rows < M: unconditional
+  // loads (clamped addresses: lanes of rows >= M read row 0, out-of-range j
+  // re-read a valid partial; both are zeroed when folded), so no branch makes
+  // the compiler's vmcnt waits conservative.
+  constexpr int LQ = (kMaxLoraSplits + kDecodeWaves - 1) / kDecodeWaves;
+  v4f lpart[LQ][RTL];
   v4h lup[RTL];
-#pragma unroll
-  for (int t = 0; t < RTL; ++t) lsum[t] = v4f{0.f, 0.f, 0.f, 0.f};
   float af = 0.f, bf = 0.f;
   if constexpr (RT > 0) {
-    if (r < g.M)   // rows >= M stay 0 and are never stored
-      for (int j = wave; j < g.ks; j += kDecodeWaves)
+    const int rr = r < g.M ? r : 0;
 #pragma unroll
-        for (int t = 0; t < RT; ++t)
-          lsum[t] += *reinterpret_cast<const v4f*>(g.la + ((size_t)j * 16 + r) * g.R + t * 16 + c * 4);
+    for (int q = 0; q < LQ; ++q) {
+      const int j0 = wave + q * kDecodeWaves;
+      const int j = j0 < g.ks ? j0 : g.ks - 1;
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+        lpart[q][t] = *reinterpret_cast<const v4f*>(g.la + ((size_t)j * 16 + rr) * g.R + t * 16 + c * 4);
+    }
     if (wave == 0) {
 #pragma unroll
       for (int t = 0; t < RT; ++t)
@@ -530,22 +537,68 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_dot_kernel(GemmArgs g) {
     bf = g.cb[nt * 16 + r];
   }
 
+  // LoRA-up early, while the first weight batch is in flight: every wave
+  // folds its partials into LDS (the wait covers only the older partial
+  // loads), a bare barrier (no vmcnt drain) publishes them, and wave 0 sums
+  // them in wave order and runs the LoRA-up MFMAs into its own accumulator.
+  v4f a_lora = v4f{0.f, 0.f, 0.f, 0.f};
+  auto lora_early = [&]() {
+    if constexpr (RT > 0) {
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        v4f l4 = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < LQ; ++q) {
+          const bool use = r < g.M && wave + q * kDecodeWaves < g.ks;
+          l4 += use ? lpart[q][t] : v4f{0.f, 0.f, 0.f, 0.f};
+        }
+        lred[t][wave][lane] = l4;
+      }
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes are done
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (wave == 0) {
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+          v4f l4 = lred[t][0][lane];
+#pragma unroll
+          for (int w = 1; w < kDecodeWaves; ++w) l4 += lred[t][w][lane];
+          v4h hi, lo;
+          split_f16(l4, hi, lo);
+          a_lora = mfma_f16_16x16x16(hi, lup[t], a_lora);
+          a_lora = mfma_f16_16x16x16(lo, lup[t], a_lora);
+        }
+      }
+    }
+  };
+
   float acc[MR];
 #pragma unroll
   for (int m = 0; m < MR; ++m) acc[m] = 0.f;
   int pb = p0;
+  bool lora_done = false;
   for (; pb + KB <= p1; pb += KB) {
     DotBatch<MR, KB> d;
     dot_load<MR, KB, false>(d, wq, sw, g.xq, sx, lane, pb, p1);
+    if (!lora_done) {
+      lora_early();
+      lora_done = true;
+    }
     dot_stage(d, xs, lane);
     dot_accumulate<MR, KB, false>(d, xs, acc, c, pb, p1);
   }
   if (pb < p1) {
     DotBatch<MR, KB> d;
     dot_load<MR, KB, true>(d, wq, sw, g.xq, sx, lane, pb, p1);
+    if (!lora_done) {
+      lora_early();
+      lora_done = true;
+    }
     dot_stage(d, xs, lane);
     dot_accumulate<MR, KB, true>(d, xs, acc, c, pb, p1);
   }
+  if (!lora_done) lora_early();   // a wave with no k-pairs still meets the barrier
 
   // sum the four k segments of each column (lanes r, r+16, r+32, r+48)
 #pragma unroll
@@ -557,31 +610,17 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_dot_kernel(GemmArgs g) {
 #pragma unroll
     for (int m = 0; m < MR; ++m) red[wave][m][r] = acc[m];
   }
-#pragma unroll
-  for (int t = 0; t < RTL; ++t) lred[t][wave][lane] = lsum[t];
   __syncthreads();
   if (wave != 0) return;
   // accumulator layout of a 16x16 tile: lane (c, r) holds rows 4c + ii of column r
-  v4f a = v4f{0.f, 0.f, 0.f, 0.f};
+  v4f a = a_lora;
   if (c == 0) {
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
       float v = red[0][m][r];
 #pragma unroll
       for (int w = 1; w < kDecodeWaves; ++w) v += red[w][m][r];
-      a[m] = v;
-    }
-  }
-  if constexpr (RT > 0) {
-#pragma unroll
-    for (int t = 0; t < RT; ++t) {
-      v4f l4 = lred[t][0][lane];
-#pragma unroll
-      for (int w = 1; w < kDecodeWaves; ++w) l4 += lred[t][w][lane];
-      v4h hi, lo;
-      split_f16(l4, hi, lo);
-      a = mfma_f16_16x16x16(hi, lup[t], a);
-      a = mfma_f16_16x16x16(lo, lup[t], a);
+      a[m] += v;
     }
   }
   store_tile<MR>(g, a, 0, nt * 16, af, bf, lane);
@@ -852,16 +891,38 @@ static hipError_t launch_decode_mv(const GemmArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+
+// Weight k-pairs per batch of the dot decode kernel (rows: M = 1..4, columns:
+// R / 16 = 0..4): as many as fit the 128-VGPR budget, together with the
+// LoRA-down partials held across the first batch, without spills.
+constexpr int dot_kb(int mr, int rt) {
+  constexpr int kTable[4][5] = {{8, 8, 8, 8, 4}, {8, 8, 8, 4, 4}, {8, 4, 4, 2, 4}, {8, 4, 4, 4, 2}};
+  return kTable[mr - 1][rt];
+}
+
+// A wave whose k range is shorter than one batch would run only the
+// bounds-checked tail batch, whose conditional loads make every wait a full
+// drain; a 4-pair batch keeps such short ranges on the unchecked path.
+template <int MR, int RT>
+static void launch_dot_rt(const GemmArgs& a, hipStream_t stream) {
+  constexpr int KB = dot_kb(MR, RT);
+  constexpr int KBS = KB < 4 ? KB : 4;
+  const dim3 grid((unsigned)(a.N / 16)), block(64 * kDecodeWaves);
+  const int64_t per = (a.K / kKPair + kDecodeWaves - 1) / kDecodeWaves;
+  if (KBS < KB && per < KB)
+    gemm_decode_dot_kernel<MR, RT, KBS><<<grid, block, 0, stream>>>(a);
+  else
+    gemm_decode_dot_kernel<MR, RT, KB><<<grid, block, 0, stream>>>(a);
+}
+
 template <int MR>
 static hipError_t launch_decode_dot(const GemmArgs& a, hipStream_t stream) {
-  dim3 grid((unsigned)(a.N / 16)), block(64 * kDecodeWaves);
   switch (a.R / 16) {
-    case 0: gemm_decode_dot_kernel<MR, 0, 8><<<grid, block, 0, stream>>>(a); break;
-    case 1: gemm_decode_dot_kernel<MR, 1, 8><<<grid, block, 0, stream>>>(a); break;
-    case 2: gemm_decode_dot_kernel<MR, 2, 8><<<grid, block, 0, stream>>>(a); break;
-    // k-pairs in flight per wave: as many as fit in 128 VGPRs without spills
-    case 3: gemm_decode_dot_kernel<MR, 3, MR <= 2 ? 8 : 6><<<grid, block, 0, stream>>>(a); break;
-    case 4: gemm_decode_dot_kernel<MR, 4, MR <= 2 ? 8 : 6><<<grid, block, 0, stream>>>(a); break;
+    case 0: launch_dot_rt<MR, 0>(a, stream); break;
+    case 1: launch_dot_rt<MR, 1>(a, stream); break;
+    case 2: launch_dot_rt<MR, 2>(a, stream); break;
+    case 3: launch_dot_rt<MR, 3>(a, stream); break;
+    case 4: launch_dot_rt<MR, 4>(a, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -831,15 +831,23 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void gemm_tiled_kernel(GemmArgs g,
         const v2u r2 = *reinterpret_cast<const v2u*>(&lds[st][BMT + wn * TN + j][lane * 16 + h * 8]);
         Be[j] = expand_group(r2[0], r2[1]);
       }
+      // Per row tile: its TN scale MFMAs, then its TN integer MFMAs, then
+      // the conversions and FMAs -- grouping MFMAs of one kind avoids the
+      // pipeline's switch penalty between the two kinds, and the FMAs of a
+      // tile no longer wait right behind the MFMA that feeds them.
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < TM; ++i) {
+        v4f S[TN];
+        v4i P[TN];
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const v4f S = scale_tile(sxw[i], sww[j], h);
-          const v4i P = mfma_i8_16x16x64(Ae[i], Be[j], v4i{0, 0, 0, 0});
+        for (int j = 0; j < TN; ++j) S[j] = scale_tile(sxw[i], sww[j], h);
 #pragma unroll
-          for (int ii = 0; ii < 4; ++ii) acc[i][j][ii] = fmaf((float)P[ii], S[ii], acc[i][j][ii]);
-        }
+        for (int j = 0; j < TN; ++j) P[j] = mfma_i8_16x16x64(Ae[i], Be[j], v4i{0, 0, 0, 0});
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) acc[i][j][ii] = fmaf((float)P[j][ii], S[j][ii], acc[i][j][ii]);
+      }
     }
     st = st + 1 == NS ? 0 : st + 1;
     st_next = st_next + 1 == NS ? 0 : st_next + 1;

@@ -138,14 +138,14 @@ __global__ __launch_bounds__(NW * 64) void quantize_rows_kernel(
     }
   };
 
-  v8h v[4], vn[4];
+  v8h v[4];
   int64_t p = pbeg + wave;
-  if (p < pend) load_x(p, v);
   for (; p < pend; p += NW) {
-    const bool more = p + NW < pend;
-    // this k-pair's L_down fragments first (L2-resident, shared by every row
-    // tile), then the next k-pair's X: the LoRA MFMAs below then wait only
-    // for the former while the quantizer arithmetic covers their latency
+    // this k-pair's X, then its L_down fragments (L2-resident, shared by
+    // every row tile): the LoRA MFMAs wait for the latter while the quantizer
+    // arithmetic runs.  No prefetch of the next k-pair's X: the registers it
+    // needs cost more occupancy than the latency it hides (measured).
+    load_x(p, v);
     constexpr int RTL = RT > 0 ? RT : 1;
     v8h lb[RTL][4];
     if constexpr (RT > 0) {
@@ -155,7 +155,6 @@ __global__ __launch_bounds__(NW * 64) void quantize_rows_kernel(
 #pragma unroll
         for (int s = 0; s < 4; ++s) lb[t][s] = *reinterpret_cast<const v8h*>(lp + ((size_t)(t * 4 + s) * 64 + lane) * 8);
     }
-    if (more) load_x(p + NW, vn);
     uint32_t d[4];
     _Float16 sc[2];
 #pragma unroll
@@ -187,10 +186,6 @@ __global__ __launch_bounds__(NW * 64) void quantize_rows_kernel(
       for (int t = 0; t < RT; ++t)
 #pragma unroll
         for (int s = 0; s < 4; ++s) acc[t] = mfma_f16_16x16x32(v[s], lb[t][s], acc[t]);
-    }
-    if (more) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) v[s] = vn[s];
     }
   }
 

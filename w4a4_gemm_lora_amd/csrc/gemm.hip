@@ -287,7 +287,8 @@ constexpr int kDecodeWaves = 4;
 template <int MV, int RT, int KB>
 __global__ __launch_bounds__(256, 4) void gemm_decode_kernel(GemmArgs g) {
   constexpr int RTL = RT > 0 ? RT : 1;
-  __shared__ v4f red_lds[(1 + RTL) * kDecodeWaves * 64];
+  __shared__ v4f red[kDecodeWaves][64];
+  __shared__ v4f lred[RTL][kDecodeWaves][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nt = blockIdx.x;
@@ -297,20 +298,26 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_kernel(GemmArgs g) {
   const int64_t p1 = p0 + per < KP ? p0 + per : KP;
   const int c = lane >> 4, r = lane & 15;
 
-  // Epilogue prefetch, issued before the weight stream: wave w sums the LoRA
-  // partials j = w, w+4, ... (fixed order) of rows 0..M-1; wave 0 also takes
-  // the L_up fragments and the affine of its columns.
-  v4f lsum[RTL];
+  // Epilogue operands, issued before the weight stream.  LoRA-down partials
+  // j = wave, wave + 4 (< ks) of rows < M: unconditional loads (clamped
+  // addresses: lanes of rows >= M read row 0, out-of-range j re-read a valid
+  // partial; both are zeroed when folded), so that no wait for them precedes
+  // the weight loads.  Wave 0 also takes the L_up fragments and the affine of
+  // its columns.
+  constexpr int LQ = (kMaxLoraSplits + kDecodeWaves - 1) / kDecodeWaves;
+  v4f lpart[LQ][RTL];
   v4h lup[RTL];
-#pragma unroll
-  for (int t = 0; t < RTL; ++t) lsum[t] = v4f{0.f, 0.f, 0.f, 0.f};
   float af = 0.f, bf = 0.f;
   if constexpr (RT > 0) {
-    if (r < g.M)   // rows >= M stay 0 and are never stored
-      for (int j = wave; j < g.ks; j += kDecodeWaves)
+    const int rr = r < g.M ? r : 0;
 #pragma unroll
-        for (int t = 0; t < RT; ++t)
-          lsum[t] += *reinterpret_cast<const v4f*>(g.la + ((size_t)j * 16 + r) * g.R + t * 16 + c * 4);
+    for (int q = 0; q < LQ; ++q) {
+      const int j0 = wave + q * kDecodeWaves;
+      const int j = j0 < g.ks ? j0 : g.ks - 1;
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+        lpart[q][t] = *reinterpret_cast<const v4f*>(g.la + ((size_t)j * 16 + rr) * g.R + t * 16 + c * 4);
+    }
     if (wave == 0) {
 #pragma unroll
       for (int t = 0; t < RT; ++t)
@@ -321,6 +328,43 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_kernel(GemmArgs g) {
     af = g.ca[nt * 16 + r];
     bf = g.cb[nt * 16 + r];
   }
+
+  // LoRA-up while the first weight batch is in flight: every wave folds its
+  // partials into LDS (the wait covers only the older partial loads), a bare
+  // barrier (no vmcnt drain) publishes them, and wave 0 sums them in wave
+  // order and runs the LoRA-up MFMAs into its own accumulator.
+  v4f a_lora = v4f{0.f, 0.f, 0.f, 0.f};
+  auto lora_early = [&]() {
+    if constexpr (RT > 0) {
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        v4f l4 = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < LQ; ++q) {
+          const bool use = r < g.M && wave + q * kDecodeWaves < g.ks;
+          l4 += use ? lpart[q][t] : v4f{0.f, 0.f, 0.f, 0.f};
+        }
+        lred[t][wave][lane] = l4;
+      }
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes are done
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (wave == 0) {
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+          v4f l4 = lred[t][0][lane];
+#pragma unroll
+          for (int w = 1; w < kDecodeWaves; ++w) l4 += lred[t][w][lane];
+          v4h hi, lo;
+          split_f16(l4, hi, lo);
+          a_lora = mfma_f16_16x16x16(hi, lup[t], a_lora);
+          a_lora = mfma_f16_16x16x16(lo, lup[t], a_lora);
+        }
+      }
+    }
+  };
+  bool lora_done = false;
 
   v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
   const uint8_t* wq = g.wq + (size_t)nt * KP * kTileBytes + lane * 16;
@@ -345,6 +389,10 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_kernel(GemmArgs g) {
       sxw[u] = *reinterpret_cast<const uint32_t*>(sxq + (size_t)p * 64);
       __builtin_amdgcn_sched_barrier(0);
     }
+    if (!lora_done) {
+      lora_early();
+      lora_done = true;
+    }
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
       if (pb + u < p1) {
@@ -360,30 +408,18 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_kernel(GemmArgs g) {
     }
   }
 
+  if (!lora_done) lora_early();   // a wave with no k-pairs still meets the barrier
+
   acc *= (1.0f / 256.0f);   // the int8 operands carry 16 q each
 
   // cross-wave sums in LDS, added by wave 0 in wave order
-  __syncthreads();
-  v4f* red = red_lds;   // [1 + RTL][waves][64]
-  red[wave * 64 + lane] = acc;
-#pragma unroll
-  for (int t = 0; t < RTL; ++t) red[((1 + t) * kDecodeWaves + wave) * 64 + lane] = lsum[t];
+  red[wave][lane] = acc;
   __syncthreads();
   if (wave != 0) return;
+  acc = red[0][lane];
 #pragma unroll
-  for (int w = 1; w < kDecodeWaves; ++w) acc += red[w * 64 + lane];
-  if constexpr (RT > 0) {
-#pragma unroll
-    for (int t = 0; t < RT; ++t) {
-      v4f l4 = red[((1 + t) * kDecodeWaves) * 64 + lane];
-#pragma unroll
-      for (int w = 1; w < kDecodeWaves; ++w) l4 += red[((1 + t) * kDecodeWaves + w) * 64 + lane];
-      v4h hi, lo;
-      split_f16(l4, hi, lo);
-      acc = mfma_f16_16x16x16(hi, lup[t], acc);
-      acc = mfma_f16_16x16x16(lo, lup[t], acc);
-    }
-  }
+  for (int w = 1; w < kDecodeWaves; ++w) acc += red[w][lane];
+  acc += a_lora;
   store_tile<MV>(g, acc, 0, nt * 16, af, bf, lane);
 }
 
@@ -884,16 +920,24 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void gemm_tiled_kernel(GemmArgs g,
   }
 }
 
+// Weight k-pairs per batch of the MFMA decode kernel, by R / 16.  Within the
+// 128-VGPR budget (with the LoRA-down partials held across the first batch)
+// small batches measured best: the per-k-pair arithmetic here is heavy enough
+// that starting it early beats keeping more bytes in flight per wave.
+constexpr int mv_kb(int rt) {
+  constexpr int kTable[5] = {4, 4, 2, 2, 2};
+  return kTable[rt];
+}
+
 template <int MV>
 static hipError_t launch_decode_mv(const GemmArgs& a, hipStream_t stream) {
   dim3 grid((unsigned)(a.N / 16)), block(64 * kDecodeWaves);
   switch (a.R / 16) {
-    // k-pairs in flight per wave: as many as fit in 128 VGPRs without spills
-    case 0: gemm_decode_kernel<MV, 0, 8><<<grid, block, 0, stream>>>(a); break;
-    case 1: gemm_decode_kernel<MV, 1, 8><<<grid, block, 0, stream>>>(a); break;
-    case 2: gemm_decode_kernel<MV, 2, 8><<<grid, block, 0, stream>>>(a); break;
-    case 3: gemm_decode_kernel<MV, 3, 6><<<grid, block, 0, stream>>>(a); break;
-    case 4: gemm_decode_kernel<MV, 4, 6><<<grid, block, 0, stream>>>(a); break;
+    case 0: gemm_decode_kernel<MV, 0, mv_kb(0)><<<grid, block, 0, stream>>>(a); break;
+    case 1: gemm_decode_kernel<MV, 1, mv_kb(1)><<<grid, block, 0, stream>>>(a); break;
+    case 2: gemm_decode_kernel<MV, 2, mv_kb(2)><<<grid, block, 0, stream>>>(a); break;
+    case 3: gemm_decode_kernel<MV, 3, mv_kb(3)><<<grid, block, 0, stream>>>(a); break;
+    case 4: gemm_decode_kernel<MV, 4, mv_kb(4)><<<grid, block, 0, stream>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

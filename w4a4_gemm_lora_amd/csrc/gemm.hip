@@ -284,14 +284,14 @@ __device__ __forceinline__ v4f scale_tile(uint32_t sx_pair, uint32_t sw_pair, in
 // ---------------------------------------------------------------------------
 constexpr int kDecodeWaves = 4;
 
-template <int MV, int RT, int KB>
+template <int MV, int RT, int KB, int NTW>
 __global__ __launch_bounds__(256, 4) void gemm_decode_kernel(GemmArgs g) {
   constexpr int RTL = RT > 0 ? RT : 1;
-  __shared__ v4f red[kDecodeWaves][64];
+  __shared__ v4f red[NTW][kDecodeWaves][64];
   __shared__ v4f lred[RTL][kDecodeWaves][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t nt = blockIdx.x;
+  const int64_t nt0 = (int64_t)blockIdx.x * NTW;   // NTW column tiles per workgroup
   const int64_t KP = g.K / kKPair;
   const int64_t per = (KP + kDecodeWaves - 1) / kDecodeWaves;
   const int64_t p0 = wave * per;
@@ -306,8 +306,8 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_kernel(GemmArgs g) {
   // its columns.
   constexpr int LQ = (kMaxLoraSplits + kDecodeWaves - 1) / kDecodeWaves;
   v4f lpart[LQ][RTL];
-  v4h lup[RTL];
-  float af = 0.f, bf = 0.f;
+  v4h lup[NTW][RTL];
+  float af[NTW], bf[NTW];
   if constexpr (RT > 0) {
     const int rr = r < g.M ? r : 0;
 #pragma unroll
@@ -320,20 +320,29 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_kernel(GemmArgs g) {
     }
     if (wave == 0) {
 #pragma unroll
-      for (int t = 0; t < RT; ++t)
-        lup[t] = *reinterpret_cast<const v4h*>(g.lup + (((size_t)nt * RT + t) * 64 + lane) * 4);
+      for (int n = 0; n < NTW; ++n)
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+          lup[n][t] = *reinterpret_cast<const v4h*>(g.lup + (((size_t)(nt0 + n) * RT + t) * 64 + lane) * 4);
     }
   }
-  if (wave == 0) {
-    af = g.ca[nt * 16 + r];
-    bf = g.cb[nt * 16 + r];
+#pragma unroll
+  for (int n = 0; n < NTW; ++n) {
+    af[n] = 0.f;
+    bf[n] = 0.f;
+    if (wave == 0) {
+      af[n] = g.ca[(nt0 + n) * 16 + r];
+      bf[n] = g.cb[(nt0 + n) * 16 + r];
+    }
   }
 
   // LoRA-up while the first weight batch is in flight: every wave folds its
   // partials into LDS (the wait covers only the older partial loads), a bare
   // barrier (no vmcnt drain) publishes them, and wave 0 sums them in wave
-  // order and runs the LoRA-up MFMAs into its own accumulator.
-  v4f a_lora = v4f{0.f, 0.f, 0.f, 0.f};
+  // order and runs the LoRA-up MFMAs into its own accumulators.
+  v4f a_lora[NTW];
+#pragma unroll
+  for (int n = 0; n < NTW; ++n) a_lora[n] = v4f{0.f, 0.f, 0.f, 0.f};
   auto lora_early = [&]() {
     if constexpr (RT > 0) {
 #pragma unroll
@@ -358,33 +367,43 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_kernel(GemmArgs g) {
           for (int w = 1; w < kDecodeWaves; ++w) l4 += lred[t][w][lane];
           v4h hi, lo;
           split_f16(l4, hi, lo);
-          a_lora = mfma_f16_16x16x16(hi, lup[t], a_lora);
-          a_lora = mfma_f16_16x16x16(lo, lup[t], a_lora);
+#pragma unroll
+          for (int n = 0; n < NTW; ++n) {
+            a_lora[n] = mfma_f16_16x16x16(hi, lup[n][t], a_lora[n]);
+            a_lora[n] = mfma_f16_16x16x16(lo, lup[n][t], a_lora[n]);
+          }
         }
       }
     }
   };
   bool lora_done = false;
 
-  v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
-  const uint8_t* wq = g.wq + (size_t)nt * KP * kTileBytes + lane * 16;
-  const uint16_t* sw = g.sw + (size_t)nt * KP * 32 + r * 2;
-  // The activation tile is lane-ordered like the MFMA A operand, so lane l
-  // loads its own 16 bytes; rows >= M are zero codes with zero scales.
+  v4f acc[NTW];
+#pragma unroll
+  for (int n = 0; n < NTW; ++n) acc[n] = v4f{0.f, 0.f, 0.f, 0.f};
+  // Column tile nt0 + n's weights start KP k-pair tiles after tile nt0 +
+  // n - 1's.  The activation tile is lane-ordered like the MFMA A operand, so
+  // lane l loads its own 16 bytes; rows >= M are zero codes with zero scales.
+  // One activation tile serves the NTW weight tiles.
+  const uint8_t* wq = g.wq + (size_t)nt0 * KP * kTileBytes + lane * 16;
+  const uint16_t* sw = g.sw + (size_t)nt0 * KP * 32 + r * 2;
   const uint8_t* xq = g.xq + lane * 16;
   const uint8_t* sxq = reinterpret_cast<const uint8_t*>(g.sx) + (4 * c + (lane & 3)) * 4;
   for (int64_t pb = p0; pb < p1; pb += KB) {
     // All loads of a batch are plain vector loads issued in k-pair order (one
     // kind of outstanding access keeps the compiler's vmcnt waits
     // incremental, so k-pair u starts as soon as its own data has landed).
-    // Issuing the whole batch at once keeps the most bytes in flight.
-    v4u braw[KB], araw[KB];
-    uint32_t swv[KB], sxw[KB];
+    v4u braw[KB][NTW], araw[KB];
+    uint32_t swv[KB][NTW], sxw[KB];
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
       const int64_t p = pb + u < p1 ? pb + u : p1 - 1;   // clamped duplicates are skipped below
-      braw[u] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(wq + (size_t)p * kTileBytes));
-      swv[u] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(sw + (size_t)p * 32));
+#pragma unroll
+      for (int n = 0; n < NTW; ++n) {
+        braw[u][n] = __builtin_nontemporal_load(
+            reinterpret_cast<const v4u*>(wq + ((size_t)n * KP + p) * kTileBytes));
+        swv[u][n] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(sw + ((size_t)n * KP + p) * 32));
+      }
       araw[u] = *reinterpret_cast<const v4u*>(xq + (size_t)p * kTileBytes);
       sxw[u] = *reinterpret_cast<const uint32_t*>(sxq + (size_t)p * 64);
       __builtin_amdgcn_sched_barrier(0);
@@ -398,29 +417,38 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_kernel(GemmArgs g) {
       if (pb + u < p1) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const v4f S = scale_tile(sxw[u], swv[u], h);
-          const v4i P = mfma_i8_16x16x64(expand_group(araw[u][2 * h], araw[u][2 * h + 1]),
-                                         expand_group(braw[u][2 * h], braw[u][2 * h + 1]), v4i{0, 0, 0, 0});
+          const v4i Ae = expand_group(araw[u][2 * h], araw[u][2 * h + 1]);
+          v4f S[NTW];
+          v4i P[NTW];
 #pragma unroll
-          for (int ii = 0; ii < MV; ++ii) acc[ii] = fmaf((float)P[ii], S[ii], acc[ii]);
+          for (int n = 0; n < NTW; ++n) S[n] = scale_tile(sxw[u], swv[u][n], h);
+#pragma unroll
+          for (int n = 0; n < NTW; ++n)
+            P[n] = mfma_i8_16x16x64(Ae, expand_group(braw[u][n][2 * h], braw[u][n][2 * h + 1]),
+                                    v4i{0, 0, 0, 0});
+#pragma unroll
+          for (int n = 0; n < NTW; ++n)
+#pragma unroll
+            for (int ii = 0; ii < MV; ++ii) acc[n][ii] = fmaf((float)P[n][ii], S[n][ii], acc[n][ii]);
         }
       }
     }
   }
-
   if (!lora_done) lora_early();   // a wave with no k-pairs still meets the barrier
 
-  acc *= (1.0f / 256.0f);   // the int8 operands carry 16 q each
-
   // cross-wave sums in LDS, added by wave 0 in wave order
-  red[wave][lane] = acc;
+#pragma unroll
+  for (int n = 0; n < NTW; ++n) red[n][wave][lane] = acc[n] * (1.0f / 256.0f);   // the int8 operands carry 16 q each
   __syncthreads();
   if (wave != 0) return;
-  acc = red[0][lane];
 #pragma unroll
-  for (int w = 1; w < kDecodeWaves; ++w) acc += red[w][lane];
-  acc += a_lora;
-  store_tile<MV>(g, acc, 0, nt * 16, af, bf, lane);
+  for (int n = 0; n < NTW; ++n) {
+    v4f a = red[n][0][lane];
+#pragma unroll
+    for (int w = 1; w < kDecodeWaves; ++w) a += red[n][w][lane];
+    a += a_lora[n];
+    store_tile<MV>(g, a, 0, (nt0 + n) * 16, af[n], bf[n], lane);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -924,23 +952,38 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void gemm_tiled_kernel(GemmArgs g,
 // 128-VGPR budget (with the LoRA-down partials held across the first batch)
 // small batches measured best: the per-k-pair arithmetic here is heavy enough
 // that starting it early beats keeping more bytes in flight per wave.
-constexpr int mv_kb(int rt) {
-  constexpr int kTable[5] = {4, 4, 2, 2, 2};
-  return kTable[rt];
+constexpr int mv_kb(int rt, int ntw) {
+  constexpr int kTable[2][5] = {{4, 4, 2, 2, 2}, {4, 2, 2, 2, 0}};
+  return kTable[ntw - 1][rt];
 }
 
-template <int MV>
-static hipError_t launch_decode_mv(const GemmArgs& a, hipStream_t stream) {
-  dim3 grid((unsigned)(a.N / 16)), block(64 * kDecodeWaves);
+template <int MV, int NTW>
+static hipError_t launch_decode_mv_n(const GemmArgs& a, hipStream_t stream) {
+  dim3 grid((unsigned)(a.N / 16 / NTW)), block(64 * kDecodeWaves);
   switch (a.R / 16) {
-    case 0: gemm_decode_kernel<MV, 0, mv_kb(0)><<<grid, block, 0, stream>>>(a); break;
-    case 1: gemm_decode_kernel<MV, 1, mv_kb(1)><<<grid, block, 0, stream>>>(a); break;
-    case 2: gemm_decode_kernel<MV, 2, mv_kb(2)><<<grid, block, 0, stream>>>(a); break;
-    case 3: gemm_decode_kernel<MV, 3, mv_kb(3)><<<grid, block, 0, stream>>>(a); break;
-    case 4: gemm_decode_kernel<MV, 4, mv_kb(4)><<<grid, block, 0, stream>>>(a); break;
+    case 0: gemm_decode_kernel<MV, 0, mv_kb(0, NTW), NTW><<<grid, block, 0, stream>>>(a); break;
+    case 1: gemm_decode_kernel<MV, 1, mv_kb(1, NTW), NTW><<<grid, block, 0, stream>>>(a); break;
+    case 2: gemm_decode_kernel<MV, 2, mv_kb(2, NTW), NTW><<<grid, block, 0, stream>>>(a); break;
+    case 3: gemm_decode_kernel<MV, 3, mv_kb(3, NTW), NTW><<<grid, block, 0, stream>>>(a); break;
+    case 4:
+      if constexpr (NTW == 1) {   // rank 64 with two column tiles does not fit 128 VGPRs
+        gemm_decode_kernel<MV, 4, mv_kb(4, NTW), NTW><<<grid, block, 0, stream>>>(a);
+        break;
+      }
+      return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+// Two column tiles per workgroup (one activation tile serves both) when the
+// column tiles pair up, there are still >= 256 workgroups and the rank leaves
+// room in 128 VGPRs (R <= 48); else one.
+template <int MV>
+static hipError_t launch_decode_mv(const GemmArgs& a, hipStream_t stream) {
+  const int64_t ntiles = a.N / 16;
+  if (ntiles % 2 == 0 && ntiles / 2 >= 256 && a.R <= 48) return launch_decode_mv_n<MV, 2>(a, stream);
+  return launch_decode_mv_n<MV, 1>(a, stream);
 }
 
 

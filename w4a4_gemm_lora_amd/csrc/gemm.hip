@@ -226,15 +226,31 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, v4f acc, int64_t r
 // per-row check.
 __device__ __forceinline__ void store_tile4(const GemmArgs& g, v4f acc, int64_t row0, int64_t col0,
                                             float af, float bf, int lane) {
-  const int c = lane >> 4, r = lane & 15;
-  const int64_t row = row0 + c * 4;
-  uint16_t* p = g.y + row * g.ldy + col0 + r;
-  const int64_t rows_left = g.M - row;
+  // Lane (c, r) holds rows 4c..4c+3 of column r.  A 4x4 transpose of the
+  // fp16 values inside each quad of lanes (columns 4q..4q+3, q = r / 4) --
+  // two DPP exchanges and a byte permute -- leaves lane (c, 4q + s) with row
+  // 4c + s, columns 4q..4q+3: one 8-byte store per lane instead of four
+  // 2-byte ones (ldy % 8 == 0 and a 16-byte aligned y keep it aligned).
+  const int c = lane >> 4, r = lane & 15, s = lane & 3;
+  uint32_t h[4];
 #pragma unroll
-  for (int ii = 0; ii < 4; ++ii) {
-    const _Float16 v = (_Float16)fmaf(af, acc[ii], bf);
-    if (rows_left > ii) p[ii * g.ldy] = __builtin_bit_cast(uint16_t, v);
-  }
+  for (int ii = 0; ii < 4; ++ii)
+    h[ii] = __builtin_bit_cast(uint16_t, (_Float16)fmaf(af, acc[ii], bf));
+  uint32_t d0 = h[0] | (h[1] << 16), d1 = h[2] | (h[3] << 16);
+  // 2x2 blocks across lane ^ 2: lanes 0,1 take the partner's low pair as
+  // their high pair, lanes 2,3 the partner's high pair as their low pair
+  const uint32_t p0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)d0, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  const uint32_t p1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)d1, 0x4E, 0xF, 0xF, false);
+  if (s & 2) d0 = p1; else d1 = p0;
+  // 2x2 transposes of 16-bit values across lane ^ 1
+  const uint32_t q0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)d0, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  const uint32_t q1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)d1, 0xB1, 0xF, 0xF, false);
+  const uint32_t sel = (s & 1) ? 0x03020706u : 0x05040100u;   // odd: (hi partner, hi own); even: (lo own, lo partner)
+  d0 = __builtin_amdgcn_perm(q0, d0, sel);
+  d1 = __builtin_amdgcn_perm(q1, d1, sel);
+  const int64_t row = row0 + c * 4 + s;
+  if (row < g.M)
+    *reinterpret_cast<v2u*>(g.y + row * g.ldy + col0 + (r & ~3)) = v2u{d0, d1};
 }
 
 // One 64-group of one 16x16 tile: an i8 MFMA with a zero C (256 P exactly)

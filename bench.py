@@ -25,6 +25,14 @@ if ROOT not in sys.path:
 METRIC = "W4A4+LoRA linear TOPS & HBM GB/s at 1 GPU; % of roofline per shape"
 PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA, 10^12 ops/s
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+# VALU issue peak: the published fp32 vector rate (157.3 TFLOP/s, an FMA is 2
+# flops) in lane-operations: 256 CUs x 4 SIMDs x 32 lanes x 2.4 GHz
+PEAK_VALU_TLANEOPS = 78.6
+CLOCK_GHZ = 2.4             # peak engine clock the utilisation fractions are taken against
+N_SIMDS = 1024
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
+SQ_COUNTERS = ["SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_VALU_MFMA_MOPS_I8", "SQ_VALU_MFMA_BUSY_CYCLES",
+               "SQ_BUSY_CYCLES", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_WAVES"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # sources that define the GEMM kernels: a measured traffic figure is only
 # reported while they are unchanged
@@ -95,6 +103,55 @@ def ingest_pmc(workload, gemm_fetch_dir, gemm_write_dir, cal_fetch_dir, cal_writ
     print(json.dumps(db[workload]))
 
 
+def ingest_sq(workload, csv_dir, command):
+    """Record the GEMM kernel's instruction-mix counters (per-dispatch medians
+    of one rocprofv3 --pmc run, with the dispatches' own durations) in
+    profiles/counters.json."""
+    import csv
+    import glob
+    import statistics
+    per = {}
+    for path in glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if "gemm_" not in row["Kernel_Name"]:
+                    continue
+                d = per.setdefault(row["Dispatch_Id"], {"name": row["Kernel_Name"]})
+                d[row["Counter_Name"]] = float(row["Counter_Value"])
+                d["ns"] = int(row["End_Timestamp"]) - int(row["Start_Timestamp"])
+    if not per:
+        raise SystemExit(f"no gemm dispatches with counters under {csv_dir}")
+    rec = {c: statistics.median(d[c] for d in per.values() if c in d) for c in SQ_COUNTERS}
+    rec["dispatch_ns"] = statistics.median(d["ns"] for d in per.values())
+    rec["dispatches"] = len(per)
+    rec["kernels"] = sorted({d["name"] for d in per.values()})
+    rec["source_sha"] = kernel_source_hash()
+    rec["command"] = command
+    try:
+        with open(COUNTERS_FILE) as f:
+            db = json.load(f)
+    except (OSError, ValueError):
+        db = {}
+    db[workload] = rec
+    with open(COUNTERS_FILE, "w") as f:
+        json.dump(db, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps(rec))
+
+
+def measured_mix(workload: str):
+    """The committed instruction-mix record of `workload`, or None if there is
+    none or the kernel sources changed since it was taken."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            rec = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != kernel_source_hash():
+        return None
+    return rec
+
+
 def algorithmic_counts(M, N, K, R):
     """Ops and bytes the method must do / move (not those of an fp16 GEMM).
 
@@ -152,10 +209,15 @@ def main(argv=None):
                     help="only run a plain device copy of a known size (counter calibration)")
     ap.add_argument("--ingest-pmc", nargs=4, metavar=("GEMM_FETCH", "GEMM_WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="record rocprofv3 FETCH_SIZE / WRITE_SIZE output directories for --workload")
-    ap.add_argument("--pmc-command", default="", help="the profiling command, stored with --ingest-pmc")
+    ap.add_argument("--pmc-command", default="", help="the profiling command, stored with --ingest-pmc/--ingest-sq")
+    ap.add_argument("--ingest-sq", metavar="DIR",
+                    help="record a rocprofv3 SQ instruction-mix counter run (DIR) for --workload")
     args = ap.parse_args(argv)
     if args.ingest_pmc:
         ingest_pmc(args.workload, *args.ingest_pmc, command=args.pmc_command)
+        return 0
+    if args.ingest_sq:
+        ingest_sq(args.workload, args.ingest_sq, command=args.pmc_command)
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the layer's "
@@ -319,6 +381,26 @@ def main(argv=None):
                            "unit": "TFLOP/s", "frac": round(lin_tops / PEAK_INT8_TOPS, 4),
                            "traffic": None if traffic is None else int(traffic)}
     out["roofline"]["algorithmic_bytes"] = c["lin_bytes"]
+    # Instruction mix of the same kernel from committed rocprofv3 SQ counters
+    # (per launch): integer MFMA work against 2MNK, MFMA-busy share of the
+    # SIMD cycles of that profiled launch, and the VALU issue rate of this
+    # run's launches against the chip's VALU peak (the per-group fp32
+    # epilogue is VALU work, a second bound next to the MFMA one).
+    mix = measured_mix(args.workload if args.m is None else f"{args.workload}-{M}")
+    if mix is not None:
+        valu_only = mix["SQ_INSTS_VALU"] - mix["SQ_INSTS_MFMA"]
+        lane_tops = valu_only * 64 / (l_ms * 1e-3) / 1e12
+        simd_cycles = N_SIMDS * CLOCK_GHZ * mix["dispatch_ns"]
+        out["instruction_mix"] = {
+            "valu_insts": int(mix["SQ_INSTS_VALU"]), "mfma_insts": int(mix["SQ_INSTS_MFMA"]),
+            "lds_insts": int(mix["SQ_INSTS_LDS"]), "salu_insts": int(mix["SQ_INSTS_SALU"]),
+            # None for the M <= 4 kernel, whose integer dot products run on v_dot8 (VALU)
+            "i8_mfma_ops_over_2MNK": (round(mix["SQ_INSTS_VALU_MFMA_MOPS_I8"] * 512 / (2 * M * N * K), 4)
+                                      if mix["SQ_INSTS_VALU_MFMA_MOPS_I8"] > 0 else None),
+            "mfma_busy_frac": round(mix["SQ_VALU_MFMA_BUSY_CYCLES"] / simd_cycles, 4),
+            "valu": {"bound": "valu", "achieved": round(lane_tops, 2), "peak": PEAK_VALU_TLANEOPS,
+                     "unit": "T lane-ops/s", "frac": round(lane_tops / PEAK_VALU_TLANEOPS, 4)},
+        }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(case)
     print(json.dumps(out), flush=True)

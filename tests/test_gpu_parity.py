@@ -246,14 +246,16 @@ def test_ragged_and_rank_edges(M, K, N, R):
                                      (3, 1664, 32, 32), (3, 4864, 32, 48), (4, 1664, 32, 64),
                                      (4, 4864, 48, 16), (4, 384, 16, 0), (8, 1664, 32, 32),
                                      (13, 4864, 48, 64), (6, 1664, 8192, 48), (11, 384, 8192, 0),
-                                     (16, 4864, 8192, 16), (9, 1664, 8192, 64)])
+                                     (16, 4864, 8192, 16), (9, 1664, 8192, 64), (1, 1664, 8192, 48),
+                                     (2, 384, 8192, 0), (3, 4864, 8192, 64), (4, 1664, 8192, 16)])
 def test_small_m_decode_shapes(M, K, N, R):
     """M <= 16 kernels over uneven per-wave k-pair ranges (a wave with no
     k-pairs, ranges that are not a multiple of the batch), every rank, and
     groups whose scales differ by 16x between odd and even groups, so a
     group / scale mispairing cannot hide inside the tolerance.  N = 8192
-    (512 column tiles) takes the two-column-tiles-per-workgroup path for
-    M >= 5 and R <= 48, and the one-tile path for R = 64."""
+    (512 column tiles) takes the two-column-tiles-per-workgroup paths: the
+    dot kernel (M <= 4, every rank) and the MFMA decode kernel (M >= 5,
+    R <= 48; R = 64 keeps one tile)."""
     case = workloads.random_case(M, K, N, R, seed=2000 + M + K + R)
     x = case["x"].astype(np.float64)
     x[:, (np.arange(K) // 64) % 2 == 1] *= 16.0

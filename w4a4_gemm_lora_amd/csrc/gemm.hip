@@ -486,12 +486,12 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_kernel(GemmArgs g) {
 // is laid into the MFMA accumulator layout for the LoRA-up and the store.
 // Workgroup and wave decomposition are those of gemm_decode_kernel.
 // ---------------------------------------------------------------------------
-template <int MR, int KB>
+template <int MR, int KB, int NT>
 struct DotBatch {
   static constexpr int kChunks = KB * MR * 4;          // 16 B activation chunks
   static constexpr int kXLoads = (kChunks + 63) / 64;  // per-lane loads for them
-  v4u w[KB];          // weight codes, 16 B per lane per k-pair
-  uint32_t sw[KB];    // s_w of the lane's column, both groups
+  v4u w[KB][NT];      // weight codes of the NT column tiles, 16 B per lane per k-pair
+  uint32_t sw[KB][NT];  // s_w of the lane's column, both groups
   uint32_t sx[KB][MR];
   v4u x[kXLoads];     // activation chunk(s) of this lane, before they go to LDS
 };
@@ -502,10 +502,12 @@ struct DotBatch {
 // batch is (k-pair q / (4 MR), row (q / 4) % MR, segment q % 4).  The
 // activation chunks are issued first and s_x comes through scalar loads, so
 // the wait that parks the chunks in LDS leaves the weight loads in flight.
-template <int MR, int KB, bool TAIL>
-__device__ __forceinline__ void dot_load(DotBatch<MR, KB>& d, const uint8_t* wq, const uint8_t* sw,
-                                         const uint8_t* xq, const uint8_t* sx, int lane, int pb, int p1) {
-  using D = DotBatch<MR, KB>;
+// Column tile n of the workgroup starts n * KP k-pair tiles after the first.
+template <int MR, int KB, int NT, bool TAIL>
+__device__ __forceinline__ void dot_load(DotBatch<MR, KB, NT>& d, const uint8_t* wq, const uint8_t* sw,
+                                         const uint8_t* xq, const uint8_t* sx, int lane, int pb, int p1,
+                                         int KP) {
+  using D = DotBatch<MR, KB, NT>;
   const uint32_t lane_w = lane * 16u, lane_sw = (lane & 15) * 4u;
   // batch bases are wave-uniform (scalar registers)
   const uint8_t* wb = wq + (size_t)pb * kTileBytes;
@@ -525,8 +527,13 @@ __device__ __forceinline__ void dot_load(DotBatch<MR, KB>& d, const uint8_t* wq,
 #pragma unroll
   for (int u = 0; u < KB; ++u) {
     const uint32_t uq = (uint32_t)(TAIL && pb + u >= p1 ? p1 - 1 - pb : u);
-    d.w[u] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(wb + (lane_w + uq * kTileBytes)));
-    d.sw[u] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(swb + (lane_sw + uq * 64u)));
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const uint8_t* wn = wb + (size_t)n * KP * kTileBytes;
+      const uint8_t* swn = swb + (size_t)n * KP * 64u;
+      d.w[u][n] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(wn + (lane_w + uq * kTileBytes)));
+      d.sw[u][n] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(swn + (lane_sw + uq * 64u)));
+    }
 #pragma unroll
     for (int m = 0; m < MR; ++m) d.sx[u][m] = *reinterpret_cast<const uint32_t*>(sxb + (uq * 64u + m * 4u));
     // issue in k-pair order, so that k-pair u waits only for its own loads
@@ -535,9 +542,9 @@ __device__ __forceinline__ void dot_load(DotBatch<MR, KB>& d, const uint8_t* wq,
 }
 
 // Park the batch's activation chunks in the wave's LDS slice [KB][MR][4].
-template <int MR, int KB>
-__device__ __forceinline__ void dot_stage(const DotBatch<MR, KB>& d, v4u* xs, int lane) {
-  using D = DotBatch<MR, KB>;
+template <int MR, int KB, int NT>
+__device__ __forceinline__ void dot_stage(const DotBatch<MR, KB, NT>& d, v4u* xs, int lane) {
+  using D = DotBatch<MR, KB, NT>;
 #pragma unroll
   for (int i = 0; i < D::kXLoads; ++i) {
     const int q = lane + 64 * i;
@@ -545,9 +552,9 @@ __device__ __forceinline__ void dot_stage(const DotBatch<MR, KB>& d, v4u* xs, in
   }
 }
 
-template <int MR, int KB, bool TAIL>
-__device__ __forceinline__ void dot_accumulate(const DotBatch<MR, KB>& d, const v4u* xs, float (&acc)[MR],
-                                               int c, int pb, int p1) {
+template <int MR, int KB, int NT, bool TAIL>
+__device__ __forceinline__ void dot_accumulate(const DotBatch<MR, KB, NT>& d, const v4u* xs,
+                                               float (&acc)[NT][MR], int c, int pb, int p1) {
 #pragma unroll
   for (int u = 0; u < KB; ++u) {
     if (TAIL && pb + u >= p1) break;   // wave-uniform
@@ -556,35 +563,38 @@ __device__ __forceinline__ void dot_accumulate(const DotBatch<MR, KB>& d, const 
     for (int m = 0; m < MR; ++m) xv[m] = xs[(u * MR + m) * 4 + c];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const float swf = half_bits_to_float((uint16_t)(d.sw[u] >> (16 * h)));
 #pragma unroll
-      for (int m = 0; m < MR; ++m) {
-        int P = __builtin_amdgcn_sdot8((int)d.w[u][2 * h], (int)xv[m][2 * h], 0, false);
-        P = __builtin_amdgcn_sdot8((int)d.w[u][2 * h + 1], (int)xv[m][2 * h + 1], P, false);
-        // s_x * s_w is exact in fp32; fma with +0 keeps it one mixed-precision op
-        const float sc = __builtin_fmaf(half_bits_to_float((uint16_t)(d.sx[u][m] >> (16 * h))), swf, 0.f);
-        acc[m] = fmaf((float)P, sc, acc[m]);
+      for (int n = 0; n < NT; ++n) {
+        const float swf = half_bits_to_float((uint16_t)(d.sw[u][n] >> (16 * h)));
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+          int P = __builtin_amdgcn_sdot8((int)d.w[u][n][2 * h], (int)xv[m][2 * h], 0, false);
+          P = __builtin_amdgcn_sdot8((int)d.w[u][n][2 * h + 1], (int)xv[m][2 * h + 1], P, false);
+          // s_x * s_w is exact in fp32; fma with +0 keeps it one mixed-precision op
+          const float sc = __builtin_fmaf(half_bits_to_float((uint16_t)(d.sx[u][m] >> (16 * h))), swf, 0.f);
+          acc[n][m] = fmaf((float)P, sc, acc[n][m]);
+        }
       }
     }
   }
 }
 
-template <int MR, int RT, int KB>
+template <int MR, int RT, int KB, int NT>
 __global__ __launch_bounds__(256, 4) void gemm_decode_dot_kernel(GemmArgs g) {
   constexpr int RTL = RT > 0 ? RT : 1;
-  __shared__ float red[kDecodeWaves][MR][16];
+  __shared__ float red[NT][kDecodeWaves][MR][16];
   __shared__ v4f lred[RTL][kDecodeWaves][64];
-  __shared__ v4u xs_lds[kDecodeWaves][DotBatch<MR, KB>::kXLoads * 64];
+  __shared__ v4u xs_lds[kDecodeWaves][DotBatch<MR, KB, NT>::kXLoads * 64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t nt = blockIdx.x;
+  const int64_t nt0 = (int64_t)blockIdx.x * NT;   // NT column tiles per workgroup
   const int KP = (int)(g.K / kKPair);
   const int per = (KP + kDecodeWaves - 1) / kDecodeWaves;
   const int p0 = wave * per;
   const int p1 = p0 + per < KP ? p0 + per : KP;
   const int c = lane >> 4, r = lane & 15;
-  const uint8_t* wq = g.wq + (size_t)nt * KP * kTileBytes;
-  const uint8_t* sw = reinterpret_cast<const uint8_t*>(g.sw + (size_t)nt * KP * 32);
+  const uint8_t* wq = g.wq + (size_t)nt0 * KP * kTileBytes;
+  const uint8_t* sw = reinterpret_cast<const uint8_t*>(g.sw + (size_t)nt0 * KP * 32);
   const uint8_t* sx = reinterpret_cast<const uint8_t*>(g.sx);
   v4u* xs = &xs_lds[wave][0];
 
@@ -594,8 +604,8 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_dot_kernel(GemmArgs g) {
   // the compiler's vmcnt waits conservative.
   constexpr int LQ = (kMaxLoraSplits + kDecodeWaves - 1) / kDecodeWaves;
   v4f lpart[LQ][RTL];
-  v4h lup[RTL];
-  float af = 0.f, bf = 0.f;
+  v4h lup[NT][RTL];
+  float af[NT], bf[NT];
   if constexpr (RT > 0) {
     const int rr = r < g.M ? r : 0;
 #pragma unroll
@@ -608,20 +618,29 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_dot_kernel(GemmArgs g) {
     }
     if (wave == 0) {
 #pragma unroll
-      for (int t = 0; t < RT; ++t)
-        lup[t] = *reinterpret_cast<const v4h*>(g.lup + (((size_t)nt * RT + t) * 64 + lane) * 4);
+      for (int n = 0; n < NT; ++n)
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+          lup[n][t] = *reinterpret_cast<const v4h*>(g.lup + (((size_t)(nt0 + n) * RT + t) * 64 + lane) * 4);
     }
   }
-  if (wave == 0) {
-    af = g.ca[nt * 16 + r];
-    bf = g.cb[nt * 16 + r];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    af[n] = 0.f;
+    bf[n] = 0.f;
+    if (wave == 0) {
+      af[n] = g.ca[(nt0 + n) * 16 + r];
+      bf[n] = g.cb[(nt0 + n) * 16 + r];
+    }
   }
 
   // LoRA-up early, while the first weight batch is in flight: every wave
   // folds its partials into LDS (the wait covers only the older partial
   // loads), a bare barrier (no vmcnt drain) publishes them, and wave 0 sums
-  // them in wave order and runs the LoRA-up MFMAs into its own accumulator.
-  v4f a_lora = v4f{0.f, 0.f, 0.f, 0.f};
+  // them in wave order and runs the LoRA-up MFMAs into its own accumulators.
+  v4f a_lora[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) a_lora[n] = v4f{0.f, 0.f, 0.f, 0.f};
   auto lora_early = [&]() {
     if constexpr (RT > 0) {
 #pragma unroll
@@ -646,64 +665,76 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_dot_kernel(GemmArgs g) {
           for (int w = 1; w < kDecodeWaves; ++w) l4 += lred[t][w][lane];
           v4h hi, lo;
           split_f16(l4, hi, lo);
-          a_lora = mfma_f16_16x16x16(hi, lup[t], a_lora);
-          a_lora = mfma_f16_16x16x16(lo, lup[t], a_lora);
+#pragma unroll
+          for (int n = 0; n < NT; ++n) {
+            a_lora[n] = mfma_f16_16x16x16(hi, lup[n][t], a_lora[n]);
+            a_lora[n] = mfma_f16_16x16x16(lo, lup[n][t], a_lora[n]);
+          }
         }
       }
     }
   };
 
-  float acc[MR];
+  float acc[NT][MR];
 #pragma unroll
-  for (int m = 0; m < MR; ++m) acc[m] = 0.f;
+  for (int n = 0; n < NT; ++n)
+#pragma unroll
+    for (int m = 0; m < MR; ++m) acc[n][m] = 0.f;
   int pb = p0;
   bool lora_done = false;
   for (; pb + KB <= p1; pb += KB) {
-    DotBatch<MR, KB> d;
-    dot_load<MR, KB, false>(d, wq, sw, g.xq, sx, lane, pb, p1);
+    DotBatch<MR, KB, NT> d;
+    dot_load<MR, KB, NT, false>(d, wq, sw, g.xq, sx, lane, pb, p1, KP);
     if (!lora_done) {
       lora_early();
       lora_done = true;
     }
     dot_stage(d, xs, lane);
-    dot_accumulate<MR, KB, false>(d, xs, acc, c, pb, p1);
+    dot_accumulate<MR, KB, NT, false>(d, xs, acc, c, pb, p1);
   }
   if (pb < p1) {
-    DotBatch<MR, KB> d;
-    dot_load<MR, KB, true>(d, wq, sw, g.xq, sx, lane, pb, p1);
+    DotBatch<MR, KB, NT> d;
+    dot_load<MR, KB, NT, true>(d, wq, sw, g.xq, sx, lane, pb, p1, KP);
     if (!lora_done) {
       lora_early();
       lora_done = true;
     }
     dot_stage(d, xs, lane);
-    dot_accumulate<MR, KB, true>(d, xs, acc, c, pb, p1);
+    dot_accumulate<MR, KB, NT, true>(d, xs, acc, c, pb, p1);
   }
   if (!lora_done) lora_early();   // a wave with no k-pairs still meets the barrier
 
   // sum the four k segments of each column (lanes r, r+16, r+32, r+48)
 #pragma unroll
-  for (int m = 0; m < MR; ++m) {
-    acc[m] += __shfl_xor(acc[m], 16);
-    acc[m] += __shfl_xor(acc[m], 32);
-  }
+  for (int n = 0; n < NT; ++n)
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      acc[n][m] += __shfl_xor(acc[n][m], 16);
+      acc[n][m] += __shfl_xor(acc[n][m], 32);
+    }
   if (c == 0) {
 #pragma unroll
-    for (int m = 0; m < MR; ++m) red[wave][m][r] = acc[m];
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int m = 0; m < MR; ++m) red[n][wave][m][r] = acc[n][m];
   }
   __syncthreads();
   if (wave != 0) return;
   // accumulator layout of a 16x16 tile: lane (c, r) holds rows 4c + ii of column r
-  v4f a = a_lora;
-  if (c == 0) {
 #pragma unroll
-    for (int m = 0; m < MR; ++m) {
-      float v = red[0][m][r];
+  for (int n = 0; n < NT; ++n) {
+    v4f a = a_lora[n];
+    if (c == 0) {
 #pragma unroll
-      for (int w = 1; w < kDecodeWaves; ++w) v += red[w][m][r];
-      a[m] += v;
+      for (int m = 0; m < MR; ++m) {
+        float v = red[n][0][m][r];
+#pragma unroll
+        for (int w = 1; w < kDecodeWaves; ++w) v += red[n][w][m][r];
+        a[m] += v;
+      }
     }
+    store_tile<MR>(g, a, 0, (nt0 + n) * 16, af[n], bf[n], lane);
   }
-  store_tile<MR>(g, a, 0, nt * 16, af, bf, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -1003,40 +1034,52 @@ static hipError_t launch_decode_mv(const GemmArgs& a, hipStream_t stream) {
 }
 
 
-// Weight k-pairs per batch of the dot decode kernel (rows: M = 1..4, columns:
-// R / 16 = 0..4): as many as fit the 128-VGPR budget, together with the
-// LoRA-down partials held across the first batch, without spills.
-constexpr int dot_kb(int mr, int rt) {
-  constexpr int kTable[4][5] = {{8, 8, 8, 8, 4}, {8, 8, 8, 4, 4}, {8, 4, 4, 2, 4}, {8, 4, 4, 4, 2}};
-  return kTable[mr - 1][rt];
+// Weight k-pairs per batch of the dot decode kernel ([column tiles per
+// workgroup - 1][M - 1][R / 16]): as many as fit the 128-VGPR budget,
+// together with the LoRA-down partials held across the first batch, without
+// spills.
+constexpr int dot_kb(int mr, int rt, int nt) {
+  constexpr int kTable[2][4][5] = {{{8, 8, 8, 8, 4}, {8, 8, 8, 4, 4}, {8, 4, 4, 2, 4}, {8, 4, 4, 4, 2}},
+                                   {{4, 4, 4, 2, 1}, {4, 4, 4, 2, 1}, {4, 2, 2, 1, 1}, {4, 2, 2, 1, 1}}};
+  return kTable[nt - 1][mr - 1][rt];
 }
 
 // A wave whose k range is shorter than one batch would run only the
 // bounds-checked tail batch, whose conditional loads make every wait a full
 // drain; a 4-pair batch keeps such short ranges on the unchecked path.
-template <int MR, int RT>
+template <int MR, int RT, int NT>
 static void launch_dot_rt(const GemmArgs& a, hipStream_t stream) {
-  constexpr int KB = dot_kb(MR, RT);
+  constexpr int KB = dot_kb(MR, RT, NT);
   constexpr int KBS = KB < 4 ? KB : 4;
-  const dim3 grid((unsigned)(a.N / 16)), block(64 * kDecodeWaves);
+  const dim3 grid((unsigned)(a.N / 16 / NT)), block(64 * kDecodeWaves);
   const int64_t per = (a.K / kKPair + kDecodeWaves - 1) / kDecodeWaves;
   if (KBS < KB && per < KB)
-    gemm_decode_dot_kernel<MR, RT, KBS><<<grid, block, 0, stream>>>(a);
+    gemm_decode_dot_kernel<MR, RT, KBS, NT><<<grid, block, 0, stream>>>(a);
   else
-    gemm_decode_dot_kernel<MR, RT, KB><<<grid, block, 0, stream>>>(a);
+    gemm_decode_dot_kernel<MR, RT, KB, NT><<<grid, block, 0, stream>>>(a);
 }
 
-template <int MR>
-static hipError_t launch_decode_dot(const GemmArgs& a, hipStream_t stream) {
+template <int MR, int NT>
+static hipError_t launch_decode_dot_n(const GemmArgs& a, hipStream_t stream) {
   switch (a.R / 16) {
-    case 0: launch_dot_rt<MR, 0>(a, stream); break;
-    case 1: launch_dot_rt<MR, 1>(a, stream); break;
-    case 2: launch_dot_rt<MR, 2>(a, stream); break;
-    case 3: launch_dot_rt<MR, 3>(a, stream); break;
-    case 4: launch_dot_rt<MR, 4>(a, stream); break;
+    case 0: launch_dot_rt<MR, 0, NT>(a, stream); break;
+    case 1: launch_dot_rt<MR, 1, NT>(a, stream); break;
+    case 2: launch_dot_rt<MR, 2, NT>(a, stream); break;
+    case 3: launch_dot_rt<MR, 3, NT>(a, stream); break;
+    case 4: launch_dot_rt<MR, 4, NT>(a, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+// Two column tiles per workgroup (sharing the activation chunks, the
+// LoRA-down fold and the cross-wave reduction) when they pair up and at
+// least 256 workgroups remain; else one.
+template <int MR>
+static hipError_t launch_decode_dot(const GemmArgs& a, hipStream_t stream) {
+  const int64_t ntiles = a.N / 16;
+  if (ntiles % 2 == 0 && ntiles / 2 >= 256) return launch_decode_dot_n<MR, 2>(a, stream);
+  return launch_decode_dot_n<MR, 1>(a, stream);
 }
 
 // M <= 4: nibble dot products (about 10 VALU per row and k-pair); larger M:

@@ -101,9 +101,9 @@ __device__ __forceinline__ _Float16 group_scale(float amax) {
 // stores only its own rows' codes, scales and lora_act rows, so splitting a
 // tile's rows over 2 workgroups doubles the parallelism of small M without
 // partial sums (every such workgroup reads the whole L_down slice of its K
-// range, which is why tiles are not split further).  The next k-pair's X loads are issued before the current one is
-// processed.  NW (2, 4, 8 or 16) follows the number of k-pairs per workgroup
-// so that few row tiles still give many waves.
+// range, which is why tiles are not split further).  NW (2, 4, 8 or 16)
+// follows the number of k-pairs per workgroup so that few row tiles still
+// give many waves.
 template <int RT, int NW>  // RT = R / 16 (0 = no LoRA)
 __global__ __launch_bounds__(NW * 64) void quantize_rows_kernel(
     const uint16_t* __restrict__ src, int64_t ld, int64_t rows, int64_t rows_padded, int64_t K,
@@ -126,16 +126,17 @@ __global__ __launch_bounds__(NW * 64) void quantize_rows_kernel(
 #pragma unroll
   for (int t = 0; t < (RT > 0 ? RT : 1); ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
 
+  // Unconditional loads (lanes of rows this workgroup does not own, or past
+  // M, read row 0 of X and are zeroed afterwards): no lane-divergent branch
+  // around the loads, so the compiler's vmcnt waits stay exact.
   auto load_x = [&](int64_t p, v8h* v) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      if (valid) {
-        const int64_t k = p * kKPair + (s >> 1) * kGroup + c * 16 + (s & 1) * 8;
-        v[s] = __builtin_nontemporal_load(reinterpret_cast<const v8h*>(xrow + k));
-      } else {
-        v[s] = v8h{0, 0, 0, 0, 0, 0, 0, 0};
-      }
+      const int64_t k = p * kKPair + (s >> 1) * kGroup + c * 16 + (s & 1) * 8;
+      v[s] = __builtin_nontemporal_load(reinterpret_cast<const v8h*>(xrow + k));
     }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) v[s] = valid ? v[s] : v8h{0, 0, 0, 0, 0, 0, 0, 0};
   };
 
   v8h v[4];

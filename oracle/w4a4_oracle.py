@@ -225,6 +225,41 @@ def quantize_act(x16, lora_down16):
     return qx, sx, la
 
 
+def rms_norm(x16, gamma16, eps: float) -> np.ndarray:
+    """Row-wise RMSNorm of fp16 X into fp16, the way the fused norm +
+    quantize pass defines it.
+
+    Sources: "W4A4 CUDA Kernel for Voice Clone", section 3.1 (every projection
+    input of the Qwen3 layer comes out of an RMSNorm: input_layernorm before
+    q/k/v, post_attention_layernorm before gate/up) and section 3.9 (kernel 5
+    computes 1 / sqrt(mean(x^2) + eps) per row over all K columns, which the
+    quantizer then reads).  The pages give no formula for the learned weight;
+    the reading here is the usual RMSNorm y = x * inv_rms * gamma[k].
+
+    Fixed arithmetic (so that the codes are reproducible bit for bit):
+        ms    = (sum_k x[m,k]^2) / K          fp64
+        inv   = 1 / sqrt(ms + eps)            fp64
+        t     = (x * inv) * gamma[k]          fp64, two roundings, in this order
+        x_out = fp16(fp32(t))                 round to fp32 first, then to fp16 (RNE)
+    """
+    x = np.asarray(x16, np.float16).astype(np.float64)
+    g = np.asarray(gamma16, np.float16).astype(np.float64)
+    K = x.shape[1]
+    ss = (x * x).sum(axis=1)                    # each x^2 is exact in fp64
+    inv = 1.0 / np.sqrt(ss / K + eps)
+    t = (x * inv[:, None]) * g[None, :]
+    return t.astype(np.float32).astype(np.float16)
+
+
+def quantize_act_rmsnorm(x16, gamma16, eps, lora_down16):
+    """The fused pass: RMSNorm (rms_norm above), then the activation
+    quantizer and LoRA-down on the normalized fp16 rows.  Returns
+    (x_norm, q_x, s_x, lora_act)."""
+    xn = rms_norm(x16, gamma16, eps)
+    qx, sx, la = quantize_act(xn, lora_down16)
+    return xn, qx, sx, la
+
+
 def ops_count(M, N, K, R) -> int:
     """Useful operations of one layer evaluation: 2MNK for the int4 product
     plus 2MR(K+N) for the two low-rank products."""

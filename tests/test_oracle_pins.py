@@ -313,3 +313,88 @@ def test_whole_layer_brute_force_python():
             assert abs(out["y64"][m, n] - y) <= 1e-12 * max(1.0, abs(y))
             yh = struct.unpack("e", struct.pack("e", y))[0]
             assert abs(float(out["y"][m, n]) - yh) <= abs(yh) * 2 ** -10  # same fp16 or 1-ulp tie
+
+
+# ----------------------------------------------------------------------------
+# RMSNorm of the fused norm + quantize pass
+# ----------------------------------------------------------------------------
+def test_rmsnorm_constant_rows_closed_form():
+    """A constant row c has mean square c^2, so with eps = 0 every output is
+    sign(c) exactly (catches a sum in place of a mean, a missing square root,
+    a sign slip); with eps > 0 it is c / sqrt(c^2 + eps)."""
+    K = 256
+    cs = np.array([1.0, -3.5, 0.015625, -1000.0, 2.0 ** -10], np.float16)
+    x = np.repeat(cs[:, None], K, axis=1)
+    ones = np.ones(K, np.float16)
+    y = O.rms_norm(x, ones, 0.0)
+    assert np.array_equal(y.astype(np.float64), np.sign(cs.astype(np.float64))[:, None] * np.ones((1, K)))
+    eps = 0.25
+    y = O.rms_norm(x, ones, eps).astype(np.float64)
+    c64 = cs.astype(np.float64)
+    expect = c64 / np.sqrt(c64 * c64 + eps)
+    assert np.all(np.abs(y - expect[:, None]) <= 2.0 ** -10 * np.abs(expect[:, None]))
+
+
+def test_rmsnorm_unit_mean_square():
+    """With gamma = 1 and eps = 0 each output row has mean square 1 (up to
+    the fp16 rounding of its elements): pins the normalizing axis and the
+    1/sqrt."""
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal((6, 512)) * rng.uniform(0.01, 50, (6, 1))).astype(np.float16)
+    y = O.rms_norm(x, np.ones(512, np.float16), 0.0).astype(np.float64)
+    ms = (y * y).mean(axis=1)
+    assert np.all(np.abs(ms - 1.0) < 2e-3), ms
+
+
+def test_rmsnorm_gamma_scale_and_permutation():
+    """gamma multiplies column k: a power-of-two gamma scales the output
+    exactly, and permuting the columns of X together with gamma permutes the
+    output (catches gamma indexed by row or left out).  With eps = 0,
+    scaling X by 2^j leaves the output unchanged."""
+    rng = np.random.default_rng(6)
+    K = 384
+    x = rng.standard_normal((5, K)).astype(np.float16)
+    g = rng.uniform(0.5, 2.0, K).astype(np.float16)
+    base = O.rms_norm(x, g, 1e-5)
+    assert np.array_equal(_bits16(O.rms_norm(x, (g.astype(np.float64) * 4).astype(np.float16), 1e-5)),
+                          _bits16((base.astype(np.float64) * 4).astype(np.float16)))
+    perm = rng.permutation(K)
+    assert np.array_equal(_bits16(O.rms_norm(x[:, perm], g[perm], 1e-5)), _bits16(base[:, perm]))
+    assert np.array_equal(_bits16(O.rms_norm((x.astype(np.float64) * 8).astype(np.float16), g, 0.0)),
+                          _bits16(O.rms_norm(x, g, 0.0)))
+    # rows are independent
+    assert np.array_equal(_bits16(O.rms_norm(x[2:3], g, 1e-5)), _bits16(base[2:3]))
+
+
+def test_rmsnorm_matches_library_routine():
+    """torch's own rms_norm in fp64 (x * rsqrt(mean(x^2) + eps) * weight),
+    rounded the same way (fp32, then fp16), agrees to within one fp16 ulp
+    everywhere and exactly almost everywhere (the two differ only in the last
+    fp64 bit of the reciprocal square root)."""
+    import torch
+    rng = np.random.default_rng(7)
+    M, K, eps = 12, 1024, 1e-6
+    x = (rng.standard_normal((M, K)) * 3).astype(np.float16)
+    g = rng.uniform(0.2, 3.0, K).astype(np.float16)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x.astype(np.float64)), (K,),
+                                       weight=torch.from_numpy(g.astype(np.float64)), eps=eps)
+    ref16 = ref.numpy().astype(np.float32).astype(np.float16)
+    got = O.rms_norm(x, g, eps)
+    d = np.abs(_bits16(got).astype(np.int32) - _bits16(ref16).astype(np.int32))
+    assert d.max() <= 1
+    assert (d == 0).mean() > 0.999
+
+
+def test_quantize_act_rmsnorm_is_norm_then_quantize():
+    """The fused pass is exactly the quantizer and LoRA-down applied to the
+    normalized fp16 rows."""
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((7, 256)).astype(np.float16)
+    g = rng.uniform(0.5, 1.5, 256).astype(np.float16)
+    ld = (rng.standard_normal((256, 16)) * 0.02).astype(np.float16)
+    xn, qx, sx, la = O.quantize_act_rmsnorm(x, g, 1e-6, ld)
+    qx2, sx2, la2 = O.quantize_act(O.rms_norm(x, g, 1e-6), ld)
+    assert np.array_equal(qx, qx2) and np.array_equal(_bits16(sx), _bits16(sx2)) and np.array_equal(la, la2)
+    # and the quantizer saw the normalized values: |xn - q*s| <= s/2 per group
+    deq = qx.astype(np.float64) * np.repeat(sx.astype(np.float64), 64, axis=1)
+    assert np.all(np.abs(xn.astype(np.float64) - deq) <= np.repeat(sx.astype(np.float64), 64, axis=1) / 2)

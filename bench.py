@@ -210,6 +210,9 @@ def main(argv=None):
     ap.add_argument("--ingest-pmc", nargs=4, metavar=("GEMM_FETCH", "GEMM_WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="record rocprofv3 FETCH_SIZE / WRITE_SIZE output directories for --workload")
     ap.add_argument("--pmc-command", default="", help="the profiling command, stored with --ingest-pmc/--ingest-sq")
+    ap.add_argument("--rmsnorm", action="store_true",
+                    help="quantize through the fused RMSNorm + quantize pass (synthetic gamma, eps 1e-6); "
+                         "also times torch's rms_norm followed by the plain quantizer")
     ap.add_argument("--ingest-sq", metavar="DIR",
                     help="record a rocprofv3 SQ instruction-mix counter run (DIR) for --workload")
     args = ap.parse_args(argv)
@@ -256,9 +259,20 @@ def main(argv=None):
     y = torch.empty((M, N), dtype=torch.float16, device="cuda")
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
+    if args.rmsnorm:
+        # synthetic norm weight (the pages' model weights are not here):
+        # gamma ~ U(0.5, 2) fp16, seeded; eps as Qwen3's RMSNorm
+        gamma = dev(np.random.default_rng(20261299).uniform(0.5, 2.0, K).astype(np.float16))
+        eps = 1e-6
+
+    def quant(wb, st):
+        if args.rmsnorm:
+            W.w4a4_quantize_act_rmsnorm(M, K, R, x, gamma, eps, wb, act, stream=st)
+        else:
+            W.w4a4_quantize_act(M, K, R, x, wb, act, stream=st)
 
     def step():
-        W.w4a4_quantize_act(M, K, R, x, wblob, act, stream=sh)
+        quant(wblob, sh)
         W.w4a4_linear(M, N, K, R, act, wblob, y, stream=sh)
 
     for _ in range(args.warmup):
@@ -276,7 +290,7 @@ def main(argv=None):
         cs = torch.cuda.current_stream().cuda_stream
         for i in range(per_graph):
             wb = blobs[i % len(blobs)]
-            W.w4a4_quantize_act(M, K, R, x, wb, act, stream=cs)
+            quant(wb, cs)
             W.w4a4_linear(M, N, K, R, act, wb, y, stream=cs)
     g.replay()
     torch.cuda.synchronize()
@@ -303,7 +317,7 @@ def main(argv=None):
     for i in range(nk):
         wb = blobs[i % len(blobs)]
         ev[i][0].record(stream)
-        W.w4a4_quantize_act(M, K, R, x, wb, act, stream=sh)
+        quant(wb, sh)
         ev[i][1].record(stream)
         W.w4a4_linear(M, N, K, R, act, wb, y, stream=sh)
         ev[i][2].record(stream)
@@ -333,7 +347,21 @@ def main(argv=None):
 
     nk_g = 50
     l_ms = graph_avg_ms(lambda i, cs2: W.w4a4_linear(M, N, K, R, act, blobs[i % len(blobs)], y, stream=cs2), nk_g)
-    q_ms = graph_avg_ms(lambda i, cs2: W.w4a4_quantize_act(M, K, R, x, blobs[i % len(blobs)], act, stream=cs2), nk_g)
+    q_ms = graph_avg_ms(lambda i, cs2: quant(blobs[i % len(blobs)], cs2), nk_g)
+    unfused = None
+    if args.rmsnorm:
+        # the unfused alternative: torch's rms_norm (fp16 out), then the plain quantizer
+        xn = torch.empty_like(x)
+
+        def norm_only(i, cs2):
+            xn.copy_(torch.nn.functional.rms_norm(x, (K,), weight=gamma, eps=eps))
+
+        def norm_then_quant(i, cs2):
+            norm_only(i, cs2)
+            W.w4a4_quantize_act(M, K, R, xn, blobs[i % len(blobs)], act, stream=cs2)
+
+        unfused = {"torch_rms_norm_us": round(graph_avg_ms(norm_only, nk_g) * 1e3, 3),
+                   "torch_rms_norm_then_quantize_us": round(graph_avg_ms(norm_then_quant, nk_g) * 1e3, 3)}
 
     c = algorithmic_counts(M, N, K, R)
     value = c["layer_ops"] / (ms_per_step * 1e-3) / 1e12
@@ -353,16 +381,19 @@ def main(argv=None):
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: W4A4+LoRA linear M={M} K={K} N={N} R={R} group 64",
                    "M": M, "K": K, "N": N, "R": R, "group": 64,
-                   "variant": W.w4a4_query_variant(M, N, K, R), "weight_blobs": len(blobs)},
+                   "variant": W.w4a4_query_variant(M, N, K, R), "weight_blobs": len(blobs),
+                   **({"rmsnorm": {"eps": eps, "gamma": "U(0.5, 2) fp16, seeded"}} if args.rmsnorm else {})},
         "hbm_gbps_step": round((c["lin_bytes"] + c["q_bytes"]) / (ms_per_step * 1e-3) / 1e9, 1),
         "kernels": {
             "w4a4_linear": {"avg_us": round(l_ms * 1e3, 3), "TOPS": round(lin_tops, 2),
                              "GBps": round(c["lin_bytes"] / (l_ms * 1e-3) / 1e9, 1),
                              "event_bracketed_us": round(l_ms_ev * 1e3, 3)},
-            "w4a4_quantize_act": {"avg_us": round(q_ms * 1e3, 3),
-                                   "GBps": round(c["q_bytes"] / (q_ms * 1e-3) / 1e9, 1),
-                                   "event_bracketed_us": round(q_ms_ev * 1e3, 3)},
+            ("w4a4_quantize_act_rmsnorm" if args.rmsnorm else "w4a4_quantize_act"): {
+                "avg_us": round(q_ms * 1e3, 3),
+                "GBps": round(c["q_bytes"] / (q_ms * 1e-3) / 1e9, 1),
+                "event_bracketed_us": round(q_ms_ev * 1e3, 3)},
         },
+        **({"unfused_norm_reference": unfused} if unfused else {}),
         "roofline": None,
         "cpu_baseline": None,
     }

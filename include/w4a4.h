@@ -128,6 +128,22 @@ int w4a4_pack_weights(int64_t N, int64_t K, int32_t R,
 int w4a4_quantize_act(int64_t M, int64_t K, int32_t R, const uint16_t* x,
                       int64_t ldx, const void* wblob, void* act, void* stream);
 
+/* Per forward, the RMSNorm in front of a projection fused into kernel 1
+ * ("W4A4 CUDA Kernel for Voice Clone", section 3.1: an RMSNorm precedes the
+ * q/k/v and gate/up projections; section 3.9: the norm's 1/sqrt(mean(x^2) +
+ * eps) runs over all K columns of a row): the activation blob is exactly what
+ * w4a4_quantize_act writes for the normalized rows
+ *     xn[m][k] = fp16(fp32((x[m][k] * inv[m]) * gamma[k])),
+ *     inv[m]   = 1 / sqrt((sum_k x[m][k]^2) / K + eps),
+ * with inv, the sum and both products in fp64 (the sum's order is the
+ * kernel's; everything after it is fixed).  The normalized rows themselves
+ * are not written out.
+ * gamma: fp16 [K], 16-byte aligned.  eps: > 0 and finite (else
+ * W4A4_ERR_ARG).  Other arguments, layouts and errors as w4a4_quantize_act. */
+int w4a4_quantize_act_rmsnorm(int64_t M, int64_t K, int32_t R, const uint16_t* x,
+                              int64_t ldx, const uint16_t* gamma, double eps,
+                              const void* wblob, void* act, void* stream);
+
 /* Per forward, kernel 2 ("W4A4 CUDA Kernel for Voice Clone", section 3.7;
  * affine: Blackwell article, section 1): Y = a * (int4 GEMM with per-group
  * fp32 dequant + lora_act L_up^T) + b, rounded to fp16.

@@ -120,6 +120,17 @@ def test_validation_errors_before_any_launch():
     assert lib.w4a4_quantize_act(4, 128, 16, FAKE, 128, FAKE, None, None) == 1
     assert lib.w4a4_quantize_act(4, 128, 16, FAKE, 128, None, FAKE, None) == 1
     assert lib.w4a4_quantize_act(0, 128, 16, None, 128, None, None, None) == 0
+    # fused RMSNorm quantizer: NULL gamma, eps <= 0 / NaN / inf, misaligned gamma,
+    # then the plain quantizer's checks
+    q = lib.w4a4_quantize_act_rmsnorm
+    assert q(4, 128, 16, FAKE, 128, None, 1e-6, FAKE, FAKE, None) == 1
+    assert q(4, 128, 16, FAKE, 128, FAKE, 0.0, FAKE, FAKE, None) == 4
+    assert q(4, 128, 16, FAKE, 128, FAKE, -1e-6, FAKE, FAKE, None) == 4
+    assert q(4, 128, 16, FAKE, 128, FAKE, float("nan"), FAKE, FAKE, None) == 4
+    assert q(4, 128, 16, FAKE, 128, FAKE, float("inf"), FAKE, FAKE, None) == 4
+    assert q(4, 128, 16, FAKE, 128, FAKE + 8, 1e-6, FAKE, FAKE, None) == 3
+    assert q(4, 128, 16, FAKE, 64, FAKE, 1e-6, FAKE, FAKE, None) == 2
+    assert q(4, 128, 16, FAKE, 128, FAKE, 1e-6, FAKE, None, None) == 1
     # pack: both or neither code source, half a checkpoint pair, missing LoRA
     assert lib.w4a4_pack_weights(16, 128, 16, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None) == 4
     assert lib.w4a4_pack_weights(16, 128, 16, None, None, None, FAKE, FAKE, None, None, FAKE, None) == 4

@@ -46,7 +46,7 @@ def _to_dev(a):
 class GpuRun:
     """Pack, quantize and run one layer on the GPU; keep host copies."""
 
-    def __init__(self, case, use_qweight=False, ldx=None, ldy=None, R=None):
+    def __init__(self, case, use_qweight=False, ldx=None, ldy=None, R=None, norm=None):
         torch = _torch()
         self.M, self.K, self.N = case["M"], case["K"], case["N"]
         self.R = case["R"] if R is None else R
@@ -68,7 +68,12 @@ class GpuRun:
         self.x = _to_dev(xs)
         self.act = W.alloc_act_blob(M, K, R)
         self.act.fill_(0x5A)
-        W.w4a4_quantize_act(M, K, R, self.x, self.wblob, self.act, ldx=self.ldx)
+        if norm is None:
+            W.w4a4_quantize_act(M, K, R, self.x, self.wblob, self.act, ldx=self.ldx)
+        else:   # (gamma fp16 [K], eps): the fused RMSNorm + quantize pass
+            self.gamma = _to_dev(norm[0])
+            W.w4a4_quantize_act_rmsnorm(M, K, R, self.x, self.gamma, norm[1], self.wblob, self.act,
+                                        ldx=self.ldx)
         self.y = torch.full((max(M, 1), self.ldy), float("nan"), dtype=torch.float16, device="cuda")
         W.w4a4_linear(M, N, K, R, self.act, self.wblob, self.y, ldy=self.ldy)
         torch.cuda.synchronize()
@@ -355,3 +360,30 @@ def test_zero_rows_is_noop():
     W.w4a4_quantize_act(0, 128, 16, None, None, None)
     W.w4a4_linear(0, 16, 128, 16, None, None, None)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("M,K,N,R,eps", [(1, 4096, 64, 32, 1e-6), (3, 1664, 48, 16, 1e-5),
+                                         (16, 4096, 32, 32, 1e-6), (13, 384, 32, 0, 1e-6),
+                                         (40, 1024, 64, 64, 1e-6), (130, 3072, 48, 48, 1e-6),
+                                         (700, 1024, 96, 32, 1e-6)])
+def test_rmsnorm_quantize(M, K, N, R, eps):
+    """The fused RMSNorm + quantize pass against the oracle's norm-then-
+    quantize: codes and scales bit-exact, lora_act within 1e-4 * rms, and the
+    layer output within the usual tolerance.  Rows get magnitudes spread
+    over 1e-2..1e2 and gamma varies per column, so a norm taken over the
+    wrong rows, a K split that misses part of the row (M <= 16 splits K over
+    workgroups) or a gamma indexed by row would change codes."""
+    rng = np.random.default_rng(4000 + M + K + R)
+    case = workloads.random_case(M, K, N, R, seed=4100 + M + K + R)
+    x = case["x"].astype(np.float64) * (10.0 ** rng.uniform(-2, 2, (M, 1)))
+    x[:, rng.choice(K, size=4, replace=False)] *= 20.0
+    case["x"] = x.astype(np.float16)
+    gamma = rng.uniform(0.25, 2.0, K).astype(np.float16)
+    _say(f"[rmsnorm] M={M} K={K} N={N} R={R} eps={eps}")
+    run = GpuRun(case, norm=(gamma, eps))
+    xn, qx, sx, la = O.quantize_act_rmsnorm(case["x"], gamma, eps, case["lora_down"] if R else None)
+    a = _check_quant(run, case, qx, sx)
+    _check_lora_act(a, la, M)
+    ref = O.linear(xn, case["lora_down"] if R else None, case["lora_up"] if R else None,
+                   case["col_scale"], case["bias"], w16=case["w"])
+    _check_y(run.host_y()[:M, :N], ref["y"], f"rmsnorm M={M} K={K} R={R}")

@@ -26,7 +26,7 @@ import os
 __all__ = [
     "W4A4Error", "lib_path", "load_library", "w4a4_status_string",
     "w4a4_weight_layout", "w4a4_act_layout", "w4a4_pack_weights",
-    "w4a4_quantize_act", "w4a4_linear", "w4a4_query_variant",
+    "w4a4_quantize_act", "w4a4_quantize_act_rmsnorm", "w4a4_linear", "w4a4_query_variant",
     "w4a4_debug_group_psums", "alloc_weight_blob", "alloc_act_blob",
     "PackedLinear", "EXPORTED_SYMBOLS",
 ]
@@ -34,7 +34,7 @@ __all__ = [
 _HERE = os.path.dirname(os.path.abspath(__file__))
 EXPORTED_SYMBOLS = (
     "w4a4_status_string", "w4a4_weight_layout", "w4a4_act_layout",
-    "w4a4_pack_weights", "w4a4_quantize_act", "w4a4_linear",
+    "w4a4_pack_weights", "w4a4_quantize_act", "w4a4_quantize_act_rmsnorm", "w4a4_linear",
     "w4a4_query_variant", "w4a4_debug_group_psums",
 )
 
@@ -70,6 +70,8 @@ def load_library() -> ctypes.CDLL:
                                     ctypes.POINTER(ctypes.c_int32)]
     lib.w4a4_pack_weights.argtypes = [_i64, _i64, _i32] + [_vp] * 9
     lib.w4a4_quantize_act.argtypes = [_i64, _i64, _i32, _vp, _i64, _vp, _vp, _vp]
+    lib.w4a4_quantize_act_rmsnorm.argtypes = [_i64, _i64, _i32, _vp, _i64, _vp, ctypes.c_double,
+                                              _vp, _vp, _vp]
     lib.w4a4_linear.argtypes = [_i64, _i64, _i64, _i32, _vp, _vp, _vp, _i64, _vp]
     lib.w4a4_query_variant.argtypes = [_i64, _i64, _i64, _i32]
     lib.w4a4_debug_group_psums.argtypes = [_i64, _i64, _i64, _i32, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp]
@@ -151,6 +153,13 @@ def w4a4_quantize_act(M, K, R, x, wblob, act, ldx=None, stream=None):
     ldx = K if ldx is None else ldx
     st = load_library().w4a4_quantize_act(M, K, R, _ptr(x), ldx, _ptr(wblob), _ptr(act), _stream(stream))
     _check(st, "w4a4_quantize_act")
+
+
+def w4a4_quantize_act_rmsnorm(M, K, R, x, gamma, eps, wblob, act, ldx=None, stream=None):
+    ldx = K if ldx is None else ldx
+    st = load_library().w4a4_quantize_act_rmsnorm(M, K, R, _ptr(x), ldx, _ptr(gamma), float(eps),
+                                                  _ptr(wblob), _ptr(act), _stream(stream))
+    _check(st, "w4a4_quantize_act_rmsnorm")
 
 
 def w4a4_linear(M, N, K, R, act, wblob, y, ldy=None, stream=None):

@@ -123,7 +123,7 @@ int w4a4_pack_weights(int64_t N, int64_t K, int32_t R, const uint16_t* w_fp16,
   uint16_t* sw = reinterpret_cast<uint16_t*>(base + g.off_sw);
   hipError_t e;
   if (have_w)
-    e = launch_quantize_rows(w_fp16, K, N, N, K, 0, 1, nullptr, wq, sw, nullptr, s);
+    e = launch_quantize_rows(w_fp16, K, N, N, K, 0, 1, nullptr, wq, sw, nullptr, nullptr, 0.0, s);
   else
     e = launch_repack_qweight(qweight, w_scales, N, K, wq, sw, s);
   if (e != hipSuccess) return W4A4_ERR_HIP;
@@ -136,15 +136,17 @@ int w4a4_pack_weights(int64_t N, int64_t K, int32_t R, const uint16_t* w_fp16,
   return hip_status(e);
 }
 
-int w4a4_quantize_act(int64_t M, int64_t K, int32_t R, const uint16_t* x, int64_t ldx,
-                      const void* wblob, void* act, void* stream) {
+static int quantize_act_impl(int64_t M, int64_t K, int32_t R, const uint16_t* x, int64_t ldx,
+                             const uint16_t* gamma, double eps, const void* wblob, void* act,
+                             void* stream) {
   int st = check_nkr(16, K, R);
   if (st) return st;
   if ((st = check_m(M))) return st;
   if (M == 0) return W4A4_OK;
   if (!x || !act || (R > 0 && !wblob)) return W4A4_ERR_NULL;
   if (ldx < K) return W4A4_ERR_SHAPE;
-  if (ldx % 8 != 0 || !aligned(x, 16) || !aligned(act, 256) || (wblob && !aligned(wblob, 256)))
+  if (ldx % 8 != 0 || !aligned(x, 16) || !aligned(act, 256) || (wblob && !aligned(wblob, 256)) ||
+      (gamma && !aligned(gamma, 16)))
     return W4A4_ERR_ALIGN;
   ActGeom g = act_geom(M, K, R);
   uint8_t* base = static_cast<uint8_t*>(act);
@@ -153,9 +155,22 @@ int w4a4_quantize_act(int64_t M, int64_t K, int32_t R, const uint16_t* x, int64_
                                 : nullptr;
   hipError_t e = launch_quantize_rows(x, ldx, M, g.Mp, K, R, g.ks, ldown, base + g.off_xq,
                                       reinterpret_cast<uint16_t*>(base + g.off_sx),
-                                      reinterpret_cast<float*>(base + g.off_la),
+                                      reinterpret_cast<float*>(base + g.off_la), gamma, eps,
                                       reinterpret_cast<hipStream_t>(stream));
   return hip_status(e);
+}
+
+int w4a4_quantize_act(int64_t M, int64_t K, int32_t R, const uint16_t* x, int64_t ldx,
+                      const void* wblob, void* act, void* stream) {
+  return quantize_act_impl(M, K, R, x, ldx, nullptr, 0.0, wblob, act, stream);
+}
+
+int w4a4_quantize_act_rmsnorm(int64_t M, int64_t K, int32_t R, const uint16_t* x, int64_t ldx,
+                              const uint16_t* gamma, double eps, const void* wblob, void* act,
+                              void* stream) {
+  if (!gamma) return W4A4_ERR_NULL;
+  if (!(eps > 0.0) || !(eps < 1e300)) return W4A4_ERR_ARG;   // also rejects NaN and inf
+  return quantize_act_impl(M, K, R, x, ldx, gamma, eps, wblob, act, stream);
 }
 
 static int make_gemm_args(int64_t M, int64_t N, int64_t K, int32_t R, const void* act,

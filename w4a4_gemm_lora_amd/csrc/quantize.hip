@@ -104,11 +104,21 @@ __device__ __forceinline__ _Float16 group_scale(float amax) {
 // range, which is why tiles are not split further).  NW (2, 4, 8 or 16)
 // follows the number of k-pairs per workgroup so that few row tiles still
 // give many waves.
-template <int RT, int NW>  // RT = R / 16 (0 = no LoRA)
+//
+// NORM: the rows are RMS-normalized first ("W4A4 CUDA Kernel for Voice
+// Clone", sections 3.1 and 3.9: the RMSNorm ahead of the projections and its
+// 1/sqrt(mean(x^2) + eps) over all of K).  Phase 1: every wave sums x^2 in
+// fp64 over its share of the row's k-pairs -- all of K, also when K is split
+// over workgroups -- and the sums meet in LDS in a fixed wave order; inv =
+// 1/sqrt(sum/K + eps) in fp64.  Phase 2 quantizes and feeds LoRA-down with
+// fp16(fp32((x * inv) * gamma[k])) (fp64 products, in that order) in place of
+// x.  Phase 1's loads are re-read in phase 2 (from L2).
+template <int RT, int NW, bool NORM>  // RT = R / 16 (0 = no LoRA)
 __global__ __launch_bounds__(NW * 64) void quantize_rows_kernel(
     const uint16_t* __restrict__ src, int64_t ld, int64_t rows, int64_t rows_padded, int64_t K,
     const uint16_t* __restrict__ ldown, uint8_t* __restrict__ codes,
-    uint16_t* __restrict__ scales, float* __restrict__ lora_part, int rh) {
+    uint16_t* __restrict__ scales, float* __restrict__ lora_part, int rh,
+    const uint16_t* __restrict__ gamma, double eps) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r = lane & 15, c = lane >> 4;
@@ -129,7 +139,7 @@ __global__ __launch_bounds__(NW * 64) void quantize_rows_kernel(
   // Unconditional loads (lanes of rows this workgroup does not own, or past
   // M, read row 0 of X and are zeroed afterwards): no lane-divergent branch
   // around the loads, so the compiler's vmcnt waits stay exact.
-  auto load_x = [&](int64_t p, v8h* v) {
+  auto load_raw = [&](int64_t p, v8h* v) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int64_t k = p * kKPair + (s >> 1) * kGroup + c * 16 + (s & 1) * 8;
@@ -137,6 +147,47 @@ __global__ __launch_bounds__(NW * 64) void quantize_rows_kernel(
     }
 #pragma unroll
     for (int s = 0; s < 4; ++s) v[s] = valid ? v[s] : v8h{0, 0, 0, 0, 0, 0, 0, 0};
+  };
+
+  double inv = 1.0;   // 1/rms of row r (NORM)
+  if constexpr (NORM) {
+    __shared__ double ssq[NW][16];
+    double ss = 0.0;
+    for (int64_t p = wave; p < KP; p += NW) {
+      v8h v[4];
+      load_raw(p, v);
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const double d = (double)(float)v[s][i];
+          ss = __builtin_fma(d, d, ss);   // d * d is exact
+        }
+    }
+    ss += __shfl_xor(ss, 16);   // the four lanes of row r
+    ss += __shfl_xor(ss, 32);
+    if (c == 0) ssq[wave][r] = ss;
+    __syncthreads();
+    double tot = ssq[0][r];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) tot += ssq[w][r];
+    inv = 1.0 / __builtin_sqrt(tot / (double)K + eps);
+  }
+
+  auto load_x = [&](int64_t p, v8h* v) {
+    load_raw(p, v);
+    if constexpr (NORM) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int64_t k = p * kKPair + (s >> 1) * kGroup + c * 16 + (s & 1) * 8;
+        const v8h gm = *reinterpret_cast<const v8h*>(reinterpret_cast<const _Float16*>(gamma) + k);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const double t = ((double)(float)v[s][i] * inv) * (double)(float)gm[i];
+          v[s][i] = (_Float16)(float)t;
+        }
+      }
+    }
   };
 
   v8h v[4];
@@ -214,43 +265,57 @@ __global__ __launch_bounds__(NW * 64) void quantize_rows_kernel(
   }
 }
 
-template <int NW>
+template <int NW, bool NORM>
 static hipError_t launch_quantize_nw(const uint16_t* src, int64_t ld, int64_t rows,
                                      int64_t rows_padded, int64_t K, int R, int ks,
                                      const uint16_t* ldown_packed, uint8_t* codes,
-                                     uint16_t* scales, float* lora_part, hipStream_t stream) {
+                                     uint16_t* scales, float* lora_part, const uint16_t* gamma,
+                                     double eps, hipStream_t stream) {
   // rows per workgroup: 8 (tiles split in two) when there are < 256 workgroups
   int rh = 16;
   while (rh > 8 && rows_padded / 16 * (16 / rh) * ks < 256) rh /= 2;
   dim3 grid((unsigned)(rows_padded / 16 * (16 / rh)), (unsigned)ks), block(64 * NW);
   switch (R / 16) {
-    case 0: quantize_rows_kernel<0, NW><<<grid, block, 0, stream>>>(src, ld, rows, rows_padded, K, ldown_packed, codes, scales, lora_part, rh); break;
-    case 1: quantize_rows_kernel<1, NW><<<grid, block, 0, stream>>>(src, ld, rows, rows_padded, K, ldown_packed, codes, scales, lora_part, rh); break;
-    case 2: quantize_rows_kernel<2, NW><<<grid, block, 0, stream>>>(src, ld, rows, rows_padded, K, ldown_packed, codes, scales, lora_part, rh); break;
-    case 3: quantize_rows_kernel<3, NW><<<grid, block, 0, stream>>>(src, ld, rows, rows_padded, K, ldown_packed, codes, scales, lora_part, rh); break;
-    case 4: quantize_rows_kernel<4, NW><<<grid, block, 0, stream>>>(src, ld, rows, rows_padded, K, ldown_packed, codes, scales, lora_part, rh); break;
+    case 0: quantize_rows_kernel<0, NW, NORM><<<grid, block, 0, stream>>>(src, ld, rows, rows_padded, K, ldown_packed, codes, scales, lora_part, rh, gamma, eps); break;
+    case 1: quantize_rows_kernel<1, NW, NORM><<<grid, block, 0, stream>>>(src, ld, rows, rows_padded, K, ldown_packed, codes, scales, lora_part, rh, gamma, eps); break;
+    case 2: quantize_rows_kernel<2, NW, NORM><<<grid, block, 0, stream>>>(src, ld, rows, rows_padded, K, ldown_packed, codes, scales, lora_part, rh, gamma, eps); break;
+    case 3: quantize_rows_kernel<3, NW, NORM><<<grid, block, 0, stream>>>(src, ld, rows, rows_padded, K, ldown_packed, codes, scales, lora_part, rh, gamma, eps); break;
+    case 4: quantize_rows_kernel<4, NW, NORM><<<grid, block, 0, stream>>>(src, ld, rows, rows_padded, K, ldown_packed, codes, scales, lora_part, rh, gamma, eps); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+template <bool NORM>
+static hipError_t launch_quantize_nwsel(const uint16_t* src, int64_t ld, int64_t rows,
+                                        int64_t rows_padded, int64_t K, int R, int ks,
+                                        const uint16_t* ldown_packed, uint8_t* codes,
+                                        uint16_t* scales, float* lora_part, const uint16_t* gamma,
+                                        double eps, int64_t wgs, int64_t kp_per_wg, hipStream_t stream) {
+  // waves per workgroup: as many as the k-pairs of a workgroup allow (<= 16),
+  // but 8 when there are enough row tiles to fill the GPU anyway
+  if (kp_per_wg >= 16 && wgs < 256)
+    return launch_quantize_nw<16, NORM>(src, ld, rows, rows_padded, K, R, ks, ldown_packed, codes, scales, lora_part, gamma, eps, stream);
+  if (kp_per_wg >= 8)
+    return launch_quantize_nw<8, NORM>(src, ld, rows, rows_padded, K, R, ks, ldown_packed, codes, scales, lora_part, gamma, eps, stream);
+  if (kp_per_wg >= 4)
+    return launch_quantize_nw<4, NORM>(src, ld, rows, rows_padded, K, R, ks, ldown_packed, codes, scales, lora_part, gamma, eps, stream);
+  return launch_quantize_nw<2, NORM>(src, ld, rows, rows_padded, K, R, ks, ldown_packed, codes, scales, lora_part, gamma, eps, stream);
+}
+
 hipError_t launch_quantize_rows(const uint16_t* src, int64_t ld, int64_t rows,
                                 int64_t rows_padded, int64_t K, int R, int ks,
                                 const uint16_t* ldown_packed, uint8_t* codes,
-                                uint16_t* scales, float* lora_part,
-                                hipStream_t stream) {
-  // waves per workgroup: as many as the k-pairs of a workgroup allow (<= 16),
-  // but 8 when there are enough row tiles to fill the GPU anyway
+                                uint16_t* scales, float* lora_part, const uint16_t* gamma,
+                                double eps, hipStream_t stream) {
   const int64_t wgs = rows_padded / 16 * ks;
   const int64_t kp_per_wg = (K / kKPair) / ks;
-  if (kp_per_wg >= 16 && wgs < 256)
-    return launch_quantize_nw<16>(src, ld, rows, rows_padded, K, R, ks, ldown_packed, codes, scales, lora_part, stream);
-  if (kp_per_wg >= 8)
-    return launch_quantize_nw<8>(src, ld, rows, rows_padded, K, R, ks, ldown_packed, codes, scales, lora_part, stream);
-  if (kp_per_wg >= 4)
-    return launch_quantize_nw<4>(src, ld, rows, rows_padded, K, R, ks, ldown_packed, codes, scales, lora_part, stream);
-  return launch_quantize_nw<2>(src, ld, rows, rows_padded, K, R, ks, ldown_packed, codes, scales, lora_part, stream);
+  if (gamma) return launch_quantize_nwsel<true>(src, ld, rows, rows_padded, K, R, ks, ldown_packed, codes, scales,
+                                                lora_part, gamma, eps, wgs, kp_per_wg, stream);
+  return launch_quantize_nwsel<false>(src, ld, rows, rows_padded, K, R, ks, ldown_packed, codes, scales,
+                                      lora_part, gamma, eps, wgs, kp_per_wg, stream);
 }
+
 
 // ---------------------------------------------------------------------------
 // Offline packers ("W4A4 CUDA Kernel for Voice Clone", sections 2.3 and 3.10)

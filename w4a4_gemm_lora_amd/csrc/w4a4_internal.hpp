@@ -87,11 +87,12 @@ inline ActGeom act_geom(int64_t M, int64_t K, int R) {
 // Quantize `rows` rows (padded up to a multiple of 16 with q=0, s=0) of an
 // fp16 matrix into codes/scales tiles.  With R > 0 also the LoRA-down partial sums lora_part[ks][rows_padded][R]
 // over `ks` k-pair ranges (ks = 1: the full sum).
+// gamma != nullptr: RMS-normalize each row first (fp16 gamma [K], eps > 0).
 hipError_t launch_quantize_rows(const uint16_t* src, int64_t ld, int64_t rows,
                                 int64_t rows_padded, int64_t K, int R, int ks,
                                 const uint16_t* ldown_packed, uint8_t* codes,
-                                uint16_t* scales, float* lora_part,
-                                hipStream_t stream);
+                                uint16_t* scales, float* lora_part, const uint16_t* gamma,
+                                double eps, hipStream_t stream);
 
 hipError_t launch_repack_qweight(const uint8_t* qweight, const uint16_t* w_scales,
                                  int64_t N, int64_t K, uint8_t* codes,

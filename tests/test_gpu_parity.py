@@ -387,3 +387,24 @@ def test_rmsnorm_quantize(M, K, N, R, eps):
     ref = O.linear(xn, case["lora_down"] if R else None, case["lora_up"] if R else None,
                    case["col_scale"], case["bias"], w16=case["w"])
     _check_y(run.host_y()[:M, :N], ref["y"], f"rmsnorm M={M} K={K} R={R}")
+
+
+def test_svdquant_checkpoint_layer():
+    """A checkpoint derived offline (w4a4_gemm_lora_amd.svdquant: RTN int4 plus
+    rank-32 factors of the quantization error) packed through the qweight
+    path and run: codes, scales and factors as derived, output within the
+    usual tolerance of the oracle on the same checkpoint."""
+    from w4a4_gemm_lora_amd import svdquant as S
+    rng = np.random.default_rng(15)
+    M, K, N, R = 48, 1024, 160, 32
+    a = rng.standard_normal((N, 4)) @ rng.standard_normal((4, K))
+    w = (a * 0.02 + rng.standard_normal((N, K)) * 0.01).astype(np.float16)
+    d = S.derive(w, rank=R)
+    case = workloads.random_case(M, K, N, R, seed=4200)
+    case.update(qweight=d["qweight"], w_scales=d["w_scales"], lora_down=d["proj_down"], lora_up=d["proj_up"])
+    _say(f"[svdquant] M={M} K={K} N={N} R={R} residual/rtn={d['residual_norm'] / d['rtn_error_norm']:.3f}")
+    run = GpuRun(case, use_qweight=True)
+    ref = O.linear(case["x"], d["proj_down"], d["proj_up"], case["col_scale"], case["bias"],
+                   qweight=d["qweight"], w_scales=d["w_scales"])
+    _check_weights(run, case, d["codes"], d["w_scales"])
+    _check_y(run.host_y()[:M, :N], ref["y"], "svdquant checkpoint")

@@ -152,6 +152,88 @@ def measured_mix(workload: str):
     return rec
 
 
+def launch_overhead(args, W, torch, M, N, K, R, x, blobs, act, y, sh, quant):
+    """Host-clock time per layer call of a chain of `calls` calls (blobs
+    rotating), synchronized only at the end: eager = the two library calls
+    per layer; graph = one replay of a native layer graph per layer (one
+    graph per blob, captured once).  The GPU time of the same kernels comes
+    from a torch graph of the chain."""
+    import ctypes
+    calls = 200
+    lib = W.load_library()
+    handles = []
+    for wb in blobs:
+        h = ctypes.c_void_p()
+        st = lib.w4a4_layer_graph_create(M, N, K, R, W._ptr(x), K, None, 0.0, W._ptr(wb), W._ptr(act),
+                                         W._ptr(y), N, ctypes.byref(h))
+        if st:
+            raise RuntimeError(W.w4a4_status_string(st))
+        handles.append(h)
+
+    def eager():
+        for i in range(calls):
+            wb = blobs[i % len(blobs)]
+            quant(wb, sh)
+            W.w4a4_linear(M, N, K, R, act, wb, y, stream=sh)
+
+    def graph():
+        for i in range(calls):
+            lib.w4a4_graph_launch(handles[i % len(handles)], sh)
+
+    # the whole chain in one native graph (captured on a side stream)
+    side = torch.cuda.Stream()
+    chain = ctypes.c_void_p()
+    with torch.cuda.stream(side):
+        ss = side.cuda_stream
+        if lib.w4a4_graph_begin(ss):
+            raise RuntimeError("w4a4_graph_begin failed")
+        for i in range(calls):
+            wb = blobs[i % len(blobs)]
+            quant(wb, ss)
+            W.w4a4_linear(M, N, K, R, act, wb, y, stream=ss)
+        if lib.w4a4_graph_end(ss, ctypes.byref(chain)):
+            raise RuntimeError("w4a4_graph_end failed")
+
+    def chain_graph():
+        lib.w4a4_graph_launch(chain, sh)
+
+    def host_us(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fn()
+            torch.cuda.synchronize()
+            best = min(best, (time.perf_counter() - t0) * 1e6 / calls)
+        return best
+
+    e_us, g_us, c_us = host_us(eager), host_us(graph), host_us(chain_graph)
+    tg = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(tg):
+        cs = torch.cuda.current_stream().cuda_stream
+        for i in range(calls):
+            wb = blobs[i % len(blobs)]
+            quant(wb, cs)
+            W.w4a4_linear(M, N, K, R, act, wb, y, stream=cs)
+    tg.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    tg.replay()
+    torch.cuda.synchronize()
+    gpu_us = (time.perf_counter() - t0) * 1e6 / calls
+    for h in handles:
+        lib.w4a4_graph_destroy(h)
+    lib.w4a4_graph_destroy(chain)
+    print(json.dumps({"metric": "host time per layer call in a chain (launch overhead)", "unit": "us",
+                      "config": {"workload": args.workload, "M": M, "K": K, "N": N, "R": R, "calls": calls,
+                                 "weight_blobs": len(blobs)},
+                      "eager_two_calls_us": round(e_us, 2), "native_layer_graph_us": round(g_us, 2),
+                      "native_chain_graph_us": round(c_us, 2), "torch_graph_chain_us": round(gpu_us, 2)}),
+          flush=True)
+    return 0
+
+
 def algorithmic_counts(M, N, K, R):
     """Ops and bytes the method must do / move (not those of an fp16 GEMM).
 
@@ -210,6 +292,9 @@ def main(argv=None):
     ap.add_argument("--ingest-pmc", nargs=4, metavar=("GEMM_FETCH", "GEMM_WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="record rocprofv3 FETCH_SIZE / WRITE_SIZE output directories for --workload")
     ap.add_argument("--pmc-command", default="", help="the profiling command, stored with --ingest-pmc/--ingest-sq")
+    ap.add_argument("--launch-overhead", action="store_true",
+                    help="time a chain of layer calls launched eagerly (two library calls each) against "
+                         "one native graph replay each (w4a4_layer_graph_*), host clock, and print that line")
     ap.add_argument("--rmsnorm", action="store_true",
                     help="quantize through the fused RMSNorm + quantize pass (synthetic gamma, eps 1e-6); "
                          "also times torch's rms_norm followed by the plain quantizer")
@@ -274,6 +359,9 @@ def main(argv=None):
     def step():
         quant(wblob, sh)
         W.w4a4_linear(M, N, K, R, act, wblob, y, stream=sh)
+
+    if args.launch_overhead:
+        return launch_overhead(args, W, torch, M, N, K, R, x, blobs, act, y, sh, quant)
 
     for _ in range(args.warmup):
         step()

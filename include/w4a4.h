@@ -169,6 +169,44 @@ int w4a4_debug_group_psums(int64_t M, int64_t N, int64_t K, int32_t R,
                            int64_t mc, int64_t n0, int64_t nc, int32_t* out,
                            void* stream);
 
+/* Captured forward passes ("W4A4 CUDA Kernel for Voice Clone", section 4:
+ * launch overhead dominates decode-size calls, so the forward step is
+ * replayed from graphs, one pre-captured per bucket of the row count).
+ * A graph bakes in every argument of the calls it holds: the shapes, the
+ * weight blobs and the x / act / y buffers.  The caller writes each
+ * request's rows into the captured x buffers (rows past the request's own
+ * should hold finite values, zeros say), replays, and reads the rows it
+ * needs; every replay recomputes all captured rows.  Buffers must stay
+ * valid while the graph exists; replays of one graph must not overlap (they
+ * share its buffers).  None of the library's kernels uses a memset or an
+ * allocation, so a graph holds kernel nodes only. */
+typedef struct w4a4_graph w4a4_graph;
+
+/* Capture every library call enqueued on stream (not NULL: the legacy
+ * default stream cannot be captured) from w4a4_graph_begin to
+ * w4a4_graph_end -- a whole step of many layers, say.  Calls made in between
+ * are recorded, not run; their own argument errors are returned by them as
+ * usual.  w4a4_graph_end ends the capture in every case and returns
+ * W4A4_ERR_HIP if it or the instantiation fails (*out = NULL then). */
+int w4a4_graph_begin(void* stream);
+int w4a4_graph_end(void* stream, w4a4_graph** out);
+
+/* One layer captured on a private stream: the activation pass
+ * (w4a4_quantize_act, or w4a4_quantize_act_rmsnorm when gamma is not NULL)
+ * followed by w4a4_linear, for exactly these arguments (M > 0 is the
+ * bucket).  The calls' shape and argument errors are returned and nothing is
+ * kept; W4A4_ERR_HIP if capture or instantiation fails. */
+int w4a4_layer_graph_create(int64_t M, int64_t N, int64_t K, int32_t R,
+                            const uint16_t* x, int64_t ldx, const uint16_t* gamma,
+                            double eps, const void* wblob, void* act, uint16_t* y,
+                            int64_t ldy, w4a4_graph** out);
+
+/* Enqueue one replay on stream (asynchronous). */
+int w4a4_graph_launch(w4a4_graph* graph, void* stream);
+/* Free the graph (NULL is a no-op).  Replays already enqueued must have
+ * completed. */
+int w4a4_graph_destroy(w4a4_graph* graph);
+
 #ifdef __cplusplus
 }
 #endif

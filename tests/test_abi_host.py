@@ -120,6 +120,19 @@ def test_validation_errors_before_any_launch():
     assert lib.w4a4_quantize_act(4, 128, 16, FAKE, 128, FAKE, None, None) == 1
     assert lib.w4a4_quantize_act(4, 128, 16, FAKE, 128, None, FAKE, None) == 1
     assert lib.w4a4_quantize_act(0, 128, 16, None, 128, None, None, None) == 0
+    # layer graphs: argument errors return before any HIP call
+    import ctypes
+    h = ctypes.c_void_p()
+    gc = lib.w4a4_layer_graph_create
+    assert gc(4, 64, 128, 16, FAKE, 128, None, 0.0, FAKE, FAKE, FAKE, 64, None) == 1
+    assert gc(0, 64, 128, 16, FAKE, 128, None, 0.0, FAKE, FAKE, FAKE, 64, ctypes.byref(h)) == 2
+    assert h.value is None
+    assert gc(4, 60, 128, 16, FAKE, 128, None, 0.0, FAKE, FAKE, FAKE, 64, ctypes.byref(h)) == 2
+    assert gc(4, 64, 100, 16, FAKE, 128, None, 0.0, FAKE, FAKE, FAKE, 64, ctypes.byref(h)) == 2
+    assert lib.w4a4_graph_launch(None, None) == 1
+    assert lib.w4a4_graph_destroy(None) == 0
+    assert lib.w4a4_graph_begin(None) == 1
+    assert lib.w4a4_graph_end(None, ctypes.byref(h)) == 1
     # fused RMSNorm quantizer: NULL gamma, eps <= 0 / NaN / inf, misaligned gamma,
     # then the plain quantizer's checks
     q = lib.w4a4_quantize_act_rmsnorm

@@ -408,3 +408,90 @@ def test_svdquant_checkpoint_layer():
                    qweight=d["qweight"], w_scales=d["w_scales"])
     _check_weights(run, case, d["codes"], d["w_scales"])
     _check_y(run.host_y()[:M, :N], ref["y"], "svdquant checkpoint")
+
+
+@pytest.mark.parametrize("norm", [False, True])
+def test_layer_graph_buckets_replay_eager(norm):
+    """Bucketed native graphs (LayerGraphs over w4a4_graph_*): requests of several row
+    counts, each padded to its bucket and replayed, give bit for bit the eager
+    two-call result on the same rows; buckets are replayed repeatedly with new
+    data, with the program's own eager work and synchronizations in between."""
+    torch = _torch()
+    rng = np.random.default_rng(16)
+    N, K, R = 96, 1024, 32
+    case = workloads.random_case(16, K, N, R, seed=4300)
+    layer = W.PackedLinear(N, K, R, w_fp16=_to_dev(case["w"]), lora_down=_to_dev(case["lora_down"]),
+                           lora_up=_to_dev(case["lora_up"]), col_scale=_to_dev(case["col_scale"]),
+                           bias=_to_dev(case["bias"]))
+    gamma = _to_dev(rng.uniform(0.5, 2.0, K).astype(np.float16)) if norm else None
+    graphs = W.LayerGraphs(layer, [1, 4, 16, 64], gamma=gamma, eps=1e-6)   # a chain of one layer
+    try:
+        for it, M in enumerate([1, 3, 16, 40, 1, 64, 3, 40]):
+            x = _to_dev((rng.standard_normal((M, K)) * (1 + it)).astype(np.float16))
+            # eager reference at the bucket size (rows past M zero, as the graph sees them)
+            B = graphs.bucket_for(M)
+            xp = torch.zeros((B, K), dtype=torch.float16, device="cuda")
+            xp[:M] = x
+            act = W.alloc_act_blob(B, K, R)
+            y_ref = torch.empty((B, N), dtype=torch.float16, device="cuda")
+            if norm:
+                W.w4a4_quantize_act_rmsnorm(B, K, R, xp, gamma, 1e-6, layer.wblob, act)
+            else:
+                W.w4a4_quantize_act(B, K, R, xp, layer.wblob, act)
+            W.w4a4_linear(B, N, K, R, act, layer.wblob, y_ref)
+            torch.cuda.synchronize()
+            y = graphs.run(x)
+            torch.cuda.synchronize()
+            _say(f"[graph] norm={norm} M={M} bucket={B}")
+            assert torch.equal(y, y_ref[:M]), f"replay {it} (M={M}) differs from eager"
+    finally:
+        graphs.close()
+
+
+def test_graph_capture_of_a_layer_chain():
+    """w4a4_graph_begin/end around a chain of three layers (the second and
+    third reading the previous output) captured on a side stream: every
+    replay, with new input written between replays and eager work in between,
+    equals the eager chain bit for bit."""
+    import ctypes
+    torch = _torch()
+    lib = W.load_library()
+    M, K = 16, 1024
+    dims = [(K, 1024, 32), (1024, 1024, 16), (1024, 2048, 0)]   # (K_in, N, R)
+    layers, acts, ys = [], [], []
+    for j, (k_in, n, r) in enumerate(dims):
+        c = workloads.random_case(16, k_in, n, r, seed=4400 + j)
+        layers.append(W.PackedLinear(n, k_in, r, w_fp16=_to_dev(c["w"]),
+                                     lora_down=_to_dev(c["lora_down"]) if r else None,
+                                     lora_up=_to_dev(c["lora_up"]) if r else None,
+                                     col_scale=_to_dev(c["col_scale"]), bias=_to_dev(c["bias"])))
+        acts.append(W.alloc_act_blob(M, k_in, r))
+        ys.append(torch.empty((M, n), dtype=torch.float16, device="cuda"))
+    x = torch.zeros((M, K), dtype=torch.float16, device="cuda")
+
+    def chain(stream):
+        inp = x
+        for L, act, y in zip(layers, acts, ys):
+            W.w4a4_quantize_act(M, L.K, L.R, inp, L.wblob, act, stream=stream)
+            W.w4a4_linear(M, L.N, L.K, L.R, act, L.wblob, y, stream=stream)
+            inp = y
+
+    side = torch.cuda.Stream()
+    h = ctypes.c_void_p()
+    with torch.cuda.stream(side):
+        assert lib.w4a4_graph_begin(side.cuda_stream) == 0
+        chain(side.cuda_stream)
+        assert lib.w4a4_graph_end(side.cuda_stream, ctypes.byref(h)) == 0
+    try:
+        rng = np.random.default_rng(17)
+        for it in range(4):
+            x.copy_(_to_dev(rng.standard_normal((M, K)).astype(np.float16)))
+            chain(torch.cuda.current_stream().cuda_stream)
+            torch.cuda.synchronize()
+            ref = ys[-1].clone()
+            ys[-1].fill_(float("nan"))
+            assert lib.w4a4_graph_launch(h, torch.cuda.current_stream().cuda_stream) == 0
+            torch.cuda.synchronize()
+            assert torch.equal(ys[-1], ref), f"replay {it} differs from the eager chain"
+    finally:
+        lib.w4a4_graph_destroy(h)

@@ -28,7 +28,7 @@ __all__ = [
     "w4a4_weight_layout", "w4a4_act_layout", "w4a4_pack_weights",
     "w4a4_quantize_act", "w4a4_quantize_act_rmsnorm", "w4a4_linear", "w4a4_query_variant",
     "w4a4_debug_group_psums", "alloc_weight_blob", "alloc_act_blob",
-    "PackedLinear", "EXPORTED_SYMBOLS",
+    "PackedLinear", "LayerGraphs", "EXPORTED_SYMBOLS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -36,6 +36,8 @@ EXPORTED_SYMBOLS = (
     "w4a4_status_string", "w4a4_weight_layout", "w4a4_act_layout",
     "w4a4_pack_weights", "w4a4_quantize_act", "w4a4_quantize_act_rmsnorm", "w4a4_linear",
     "w4a4_query_variant", "w4a4_debug_group_psums",
+    "w4a4_graph_begin", "w4a4_graph_end", "w4a4_layer_graph_create", "w4a4_graph_launch",
+    "w4a4_graph_destroy",
 )
 
 
@@ -74,6 +76,12 @@ def load_library() -> ctypes.CDLL:
                                               _vp, _vp, _vp]
     lib.w4a4_linear.argtypes = [_i64, _i64, _i64, _i32, _vp, _vp, _vp, _i64, _vp]
     lib.w4a4_query_variant.argtypes = [_i64, _i64, _i64, _i32]
+    lib.w4a4_layer_graph_create.argtypes = [_i64, _i64, _i64, _i32, _vp, _i64, _vp, ctypes.c_double,
+                                            _vp, _vp, _vp, _i64, ctypes.POINTER(_vp)]
+    lib.w4a4_graph_begin.argtypes = [_vp]
+    lib.w4a4_graph_end.argtypes = [_vp, ctypes.POINTER(_vp)]
+    lib.w4a4_graph_launch.argtypes = [_vp, _vp]
+    lib.w4a4_graph_destroy.argtypes = [_vp]
     lib.w4a4_debug_group_psums.argtypes = [_i64, _i64, _i64, _i32, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp]
     for name in EXPORTED_SYMBOLS:
         if name != "w4a4_status_string":
@@ -210,3 +218,91 @@ class PackedLinear:
         w4a4_quantize_act(M, self.K, self.R, x, self.wblob, act)
         w4a4_linear(M, self.N, self.K, self.R, act, self.wblob, y)
         return y
+
+
+class LayerGraphs:
+    """Bucketed replay of a chain of packed layers from native HIP graphs
+    ("W4A4 CUDA Kernel for Voice Clone", section 4.3: pre-capture one graph
+    per bucket, pad each request to the nearest bucket, copy the data in,
+    replay).
+
+    layers: one PackedLinear or a list whose shapes chain (layer i's N is
+    layer i+1's K; layer i+1 reads layer i's output).  For every bucket size
+    B the whole chain -- each layer's activation pass and GEMM -- is captured
+    into one graph (w4a4_graph_begin / w4a4_graph_end on a side stream) over
+    buffers sized for B rows.  run(x) copies the request's M rows into the
+    smallest bucket with B >= M (rows past M are zeros), replays that graph
+    on the current stream and returns a view of the last layer's first M
+    output rows (valid until the next run on the same bucket).  gamma/eps:
+    the first layer's activation pass is the fused RMSNorm variant.
+
+    One graph per chain rather than per layer: a graph launch costs more
+    than the two kernel launches it would replace (measured), so graphs pay
+    when they hold many layers."""
+
+    def __init__(self, layers, buckets, gamma=None, eps=1e-6, device="cuda"):
+        import torch
+        self.layers = list(layers) if isinstance(layers, (list, tuple)) else [layers]
+        for a_, b_ in zip(self.layers, self.layers[1:]):
+            if a_.N != b_.K:
+                raise ValueError("layer shapes do not chain")
+        self.buckets = sorted(int(b) for b in buckets)
+        self.gamma, self.eps = gamma, float(eps)
+        self._g = {}
+        self._bufs = {}
+        lib = load_library()
+        side = torch.cuda.Stream(device=device)
+        try:
+            for B in self.buckets:
+                x = torch.zeros((B, self.layers[0].K), dtype=torch.float16, device=device)
+                acts = [alloc_act_blob(B, L.K, L.R, device=device) for L in self.layers]
+                ys = [torch.empty((B, L.N), dtype=torch.float16, device=device) for L in self.layers]
+                ss = side.cuda_stream
+                torch.cuda.synchronize()
+                _check(lib.w4a4_graph_begin(ss), "w4a4_graph_begin")
+                try:
+                    inp = x
+                    for j, (L, act, y) in enumerate(zip(self.layers, acts, ys)):
+                        if j == 0 and gamma is not None:
+                            w4a4_quantize_act_rmsnorm(B, L.K, L.R, inp, gamma, self.eps, L.wblob, act, stream=ss)
+                        else:
+                            w4a4_quantize_act(B, L.K, L.R, inp, L.wblob, act, stream=ss)
+                        w4a4_linear(B, L.N, L.K, L.R, act, L.wblob, y, stream=ss)
+                        inp = y
+                finally:
+                    h = ctypes.c_void_p()
+                    st = lib.w4a4_graph_end(ss, ctypes.byref(h))
+                _check(st, "w4a4_graph_end")
+                self._g[B] = h
+                self._bufs[B] = (x, acts, ys)
+        except Exception:
+            self.close()
+            raise
+
+    def bucket_for(self, M):
+        for B in self.buckets:
+            if B >= M:
+                return B
+        raise ValueError(f"{M} rows exceed the largest bucket {self.buckets[-1]}")
+
+    def run(self, x, stream=None):
+        M = x.shape[0]
+        B = self.bucket_for(M)
+        xb, _, ys = self._bufs[B]
+        xb[:M].copy_(x)
+        if M < B:
+            xb[M:].zero_()
+        _check(load_library().w4a4_graph_launch(self._g[B], _stream(stream)), "w4a4_graph_launch")
+        return ys[-1][:M]
+
+    def close(self):
+        lib = load_library()
+        for h in self._g.values():
+            lib.w4a4_graph_destroy(h)
+        self._g = {}
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

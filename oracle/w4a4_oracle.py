@@ -260,6 +260,30 @@ def quantize_act_rmsnorm(x16, gamma16, eps, lora_down16):
     return xn, qx, sx, la
 
 
+def silu(v) -> np.ndarray:
+    """SiLU(v) = v / (1 + exp(-v)) in fp64 ("W4A4 CUDA Kernel for Voice
+    Clone", section 3.1: the Qwen3 MLP computes SiLU(gate) * up)."""
+    v = np.asarray(v, np.float64)
+    return v / (1.0 + np.exp(-v))
+
+
+def glu(g16, u16) -> np.ndarray:
+    """The MLP's gated activation on the fp16 outputs of the gate and up
+    projections: h = fp16(SiLU(g) * u), SiLU and the product in fp64."""
+    g = np.asarray(g16, np.float16).astype(np.float64)
+    u = np.asarray(u16, np.float16).astype(np.float64)
+    return to_fp16(silu(g) * u)
+
+
+def mlp_gate_up(x16, gate: dict, up: dict):
+    """Gate and up projections of the same X (each a dict of linear()'s
+    keyword arguments: lora_down16, lora_up16, col_scale, bias, w16 or
+    qweight/w_scales) and the gated activation.  Returns (g, u, h)."""
+    g = linear(x16, **gate)["y"]
+    u = linear(x16, **up)["y"]
+    return g, u, glu(g, u)
+
+
 def ops_count(M, N, K, R) -> int:
     """Useful operations of one layer evaluation: 2MNK for the int4 product
     plus 2MR(K+N) for the two low-rank products."""

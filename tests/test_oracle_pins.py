@@ -398,3 +398,29 @@ def test_quantize_act_rmsnorm_is_norm_then_quantize():
     # and the quantizer saw the normalized values: |xn - q*s| <= s/2 per group
     deq = qx.astype(np.float64) * np.repeat(sx.astype(np.float64), 64, axis=1)
     assert np.all(np.abs(xn.astype(np.float64) - deq) <= np.repeat(sx.astype(np.float64), 64, axis=1) / 2)
+
+
+# ----------------------------------------------------------------------------
+# MLP gated activation
+# ----------------------------------------------------------------------------
+def test_silu_closed_forms_and_identity():
+    """SiLU(0) = 0; SiLU(v) - SiLU(-v) = v (odd part is v/2, catches a sign
+    slip in the exponent); SiLU(v) -> v for large v and -> 0 for very negative
+    v; SiLU(ln 3) = ln 3 * 3/4 exactly in the reals."""
+    assert O.silu(0.0) == 0.0
+    v = np.linspace(-12, 12, 97)
+    assert np.allclose(O.silu(v) - O.silu(-v), v, rtol=0, atol=1e-12)
+    assert abs(O.silu(40.0) - 40.0) < 1e-12 and abs(O.silu(-40.0)) < 1e-15
+    assert abs(O.silu(np.log(3.0)) - np.log(3.0) * 0.75) < 1e-15
+
+
+def test_glu_rounding_and_zeros():
+    """h = fp16(SiLU(g) * u): u = 0 or g = 0 gives 0, u = 1 gives fp16(SiLU(g)),
+    and the product is taken in fp64 and rounded once."""
+    g = np.array([0.0, 1.5, -2.25, 7.0, 0.3330078125], np.float16)
+    assert not np.any(O.glu(g, np.zeros(5, np.float16)).astype(np.float64))
+    assert O.glu(np.zeros(5, np.float16), np.full(5, 3.0, np.float16)).astype(np.float64).sum() == 0
+    s64 = g.astype(np.float64) / (1 + np.exp(-g.astype(np.float64)))
+    assert np.array_equal(O.glu(g, np.ones(5, np.float16)), s64.astype(np.float16))
+    u = np.full(5, 1.0009765625, np.float16)   # 1 + 2^-10
+    assert np.array_equal(O.glu(g, u), (s64 * float(u[0])).astype(np.float16))

@@ -154,6 +154,25 @@ int w4a4_quantize_act_rmsnorm(int64_t M, int64_t K, int32_t R, const uint16_t* x
 int w4a4_linear(int64_t M, int64_t N, int64_t K, int32_t R, const void* act,
                 const void* wblob, uint16_t* y, int64_t ldy, void* stream);
 
+/* The gate and up projections of a gated MLP as one layer, and its gated
+ * activation in the GEMM's epilogue ("W4A4 CUDA Kernel for Voice Clone",
+ * section 3.1: the Qwen3 MLP computes SiLU(gate_proj(x)) * up_proj(x); gate
+ * and up read the same X, so one w4a4_quantize_act serves both).
+ * wblob: packed (w4a4_pack_weights) from the two layers interleaved by
+ * 16-row tiles -- rows [32j, 32j+16) are gate rows [16j, 16j+16), rows
+ * [32j+16, 32j+32) up rows [16j, 16j+16) -- with L_down = [L_down_gate |
+ * L_down_up] ([K][Rg + Ru]) and the L_up rows of a gate row being
+ * [L_up_gate row, 0], of an up row [0, L_up_up row] (so the low-rank term of
+ * each half is exactly its own layer's); a and b interleaved the same way.
+ * N = 2 * (columns of each layer), N % 32 == 0; R = Rg + Ru.
+ * y: fp16 [M][ldy], ldy >= N/2, ldy % 8 == 0, 16-byte aligned:
+ *     y[m][c] = fp16(SiLU(g) * u),  g = gate layer's fp16 output (m, c),
+ *                                   u = up layer's fp16 output (m, c),
+ * SiLU and the product in fp64.  Other arguments and errors as w4a4_linear
+ * (W4A4_ERR_SHAPE also if N % 32 != 0). */
+int w4a4_linear_glu(int64_t M, int64_t N, int64_t K, int32_t R, const void* act,
+                    const void* wblob, uint16_t* y, int64_t ldy, void* stream);
+
 /* Which GEMM kernel w4a4_linear runs for a shape (host-only):
  * 0 = generic, 1 = decode (M <= 16), 2 = prefill; -W4A4_ERR_SHAPE if the
  * shape is unsupported.  Lets a caller log the kernel chosen per layer

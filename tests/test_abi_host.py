@@ -4,6 +4,7 @@ the host before anything is enqueued."""
 import ctypes
 import os
 import re
+import sys
 
 import pytest
 
@@ -113,6 +114,16 @@ def test_validation_errors_before_any_launch():
     # M == 0 is a no-op success; negative M is a shape error
     assert lib.w4a4_linear(0, 64, 128, 16, None, None, None, 64, None) == 0
     assert lib.w4a4_linear(-1, 64, 128, 16, FAKE, FAKE, FAKE, 64, None) == 2
+    # gated linear: N not whole (gate, up) tile pairs, ldy below N/2, NULL y,
+    # misaligned y, y overlapping a blob, M == 0 no-op, rank above the maximum
+    assert lib.w4a4_linear_glu(4, 48, 128, 16, FAKE, FAKE, FAKE, 24, None) == 2
+    assert lib.w4a4_linear_glu(4, 64, 128, 16, FAKE, FAKE, FAKE, 16, None) == 2
+    assert lib.w4a4_linear_glu(4, 64, 128, 16, FAKE, FAKE, None, 32, None) == 1
+    assert lib.w4a4_linear_glu(4, 64, 128, 16, FAKE, FAKE, FAKE + 2, 32, None) == 3
+    assert lib.w4a4_linear_glu(4, 64, 128, 16, FAKE, FAKE, FAKE, 36, None) == 3
+    assert lib.w4a4_linear_glu(4, 64, 128, 16, FAKE, FAKE * 4, FAKE, 32, None) == 4
+    assert lib.w4a4_linear_glu(0, 64, 128, 16, None, None, None, 32, None) == 0
+    assert lib.w4a4_linear_glu(4, 64, 128, 80, FAKE, FAKE, FAKE, 32, None) == 2
     # quantize: ldx < K, misaligned x, NULL act, missing weight blob with R > 0
     assert lib.w4a4_quantize_act(4, 128, 16, FAKE, 64, FAKE, FAKE, None) == 2
     assert lib.w4a4_quantize_act(4, 128, 16, FAKE + 8, 128, FAKE, FAKE, None) == 3
@@ -160,3 +171,18 @@ def test_validation_errors_before_any_launch():
 def test_query_variant_is_host_only():
     for M in (1, 4, 16, 700, 8192):
         assert W.w4a4_query_variant(M, 4096, 4096, 32) in (0, 1, 2)
+
+
+def test_library_shares_torch_hip_runtime():
+    """Loading the library before any torch import still leaves one HIP
+    runtime in the process (torch's): a second copy would find no device
+    once torch's copy has opened the GPU."""
+    import subprocess
+    code = ("import w4a4_gemm_lora_amd as W; W.load_library(); "
+            "print(sorted({l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}))")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300,
+                         cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert out.returncode == 0, out.stderr[-2000:]
+    import ast
+    libs = ast.literal_eval(out.stdout.strip().splitlines()[-1])
+    assert len(libs) == 1, libs

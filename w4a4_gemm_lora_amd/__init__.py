@@ -26,7 +26,8 @@ import os
 __all__ = [
     "W4A4Error", "lib_path", "load_library", "w4a4_status_string",
     "w4a4_weight_layout", "w4a4_act_layout", "w4a4_pack_weights",
-    "w4a4_quantize_act", "w4a4_quantize_act_rmsnorm", "w4a4_linear", "w4a4_query_variant",
+    "w4a4_quantize_act", "w4a4_quantize_act_rmsnorm", "w4a4_linear", "w4a4_linear_glu",
+    "w4a4_query_variant", "GatedMLPUp",
     "w4a4_debug_group_psums", "alloc_weight_blob", "alloc_act_blob",
     "PackedLinear", "LayerGraphs", "EXPORTED_SYMBOLS",
 ]
@@ -35,7 +36,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 EXPORTED_SYMBOLS = (
     "w4a4_status_string", "w4a4_weight_layout", "w4a4_act_layout",
     "w4a4_pack_weights", "w4a4_quantize_act", "w4a4_quantize_act_rmsnorm", "w4a4_linear",
-    "w4a4_query_variant", "w4a4_debug_group_psums",
+    "w4a4_linear_glu", "w4a4_query_variant", "w4a4_debug_group_psums",
     "w4a4_graph_begin", "w4a4_graph_end", "w4a4_layer_graph_create", "w4a4_graph_launch",
     "w4a4_graph_destroy",
 )
@@ -57,13 +58,20 @@ _i64, _i32, _vp, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c
 
 
 def load_library() -> ctypes.CDLL:
-    """Load libw4a4.so from the package directory (raises if it is not built)."""
+    """Load libw4a4.so from the package directory (raises if it is not built).
+
+    torch is imported first: its bundled HIP runtime then satisfies the
+    library's libamdhip64 dependency, so the process holds one HIP runtime
+    and the library sees torch's devices, memory and streams.  Loaded before
+    torch, the library would pull in the system runtime as a second copy,
+    which finds no device once torch's copy has opened the GPU."""
     global _LIB
     if _LIB is not None:
         return _LIB
     path = lib_path()
     if not os.path.exists(path):
         raise ImportError(f"{path} is not built; run `python -m w4a4_gemm_lora_amd.build`")
+    import torch  # noqa: F401  (binds the library to torch's HIP runtime)
     lib = ctypes.CDLL(path)
     lib.w4a4_status_string.restype = ctypes.c_char_p
     lib.w4a4_status_string.argtypes = [ctypes.c_int]
@@ -75,6 +83,7 @@ def load_library() -> ctypes.CDLL:
     lib.w4a4_quantize_act_rmsnorm.argtypes = [_i64, _i64, _i32, _vp, _i64, _vp, ctypes.c_double,
                                               _vp, _vp, _vp]
     lib.w4a4_linear.argtypes = [_i64, _i64, _i64, _i32, _vp, _vp, _vp, _i64, _vp]
+    lib.w4a4_linear_glu.argtypes = [_i64, _i64, _i64, _i32, _vp, _vp, _vp, _i64, _vp]
     lib.w4a4_query_variant.argtypes = [_i64, _i64, _i64, _i32]
     lib.w4a4_layer_graph_create.argtypes = [_i64, _i64, _i64, _i32, _vp, _i64, _vp, ctypes.c_double,
                                             _vp, _vp, _vp, _i64, ctypes.POINTER(_vp)]
@@ -176,6 +185,12 @@ def w4a4_linear(M, N, K, R, act, wblob, y, ldy=None, stream=None):
     _check(st, "w4a4_linear")
 
 
+def w4a4_linear_glu(M, N, K, R, act, wblob, y, ldy=None, stream=None):
+    ldy = N // 2 if ldy is None else ldy
+    st = load_library().w4a4_linear_glu(M, N, K, R, _ptr(act), _ptr(wblob), _ptr(y), ldy, _stream(stream))
+    _check(st, "w4a4_linear_glu")
+
+
 def w4a4_debug_group_psums(M, N, K, R, act, wblob, m0, mc, n0, nc, out, stream=None):
     st = load_library().w4a4_debug_group_psums(M, N, K, R, _ptr(act), _ptr(wblob), m0, mc, n0, nc,
                                                _ptr(out), _stream(stream))
@@ -218,6 +233,64 @@ class PackedLinear:
         w4a4_quantize_act(M, self.K, self.R, x, self.wblob, act)
         w4a4_linear(M, self.N, self.K, self.R, act, self.wblob, y)
         return y
+
+
+def interleave_gate_up(gate, up, tile=16):
+    """Rows of two [N, ...] tensors interleaved by 16-row tiles: rows
+    [32j, 32j+16) from gate, [32j+16, 32j+32) from up (the layout
+    w4a4_linear_glu pairs)."""
+    import torch
+    n = gate.shape[0]
+    g = gate.reshape(n // tile, tile, *gate.shape[1:])
+    u = up.reshape(n // tile, tile, *up.shape[1:])
+    return torch.stack([g, u], dim=1).reshape(2 * n, *gate.shape[1:]).contiguous()
+
+
+class GatedMLPUp:
+    """The gate and up projections of a gated MLP packed as one layer, with
+    the gated activation SiLU(gate) * up applied in the GEMM epilogue
+    (w4a4_linear_glu).  One activation pass (w4a4_quantize_act, with the two
+    layers' L_down side by side) serves both projections.  forward(x)
+    returns h = fp16(SiLU(g) * u), [M, N]."""
+
+    def __init__(self, N, K, w_gate, w_up, lora_down_gate=None, lora_up_gate=None,
+                 lora_down_up=None, lora_up_up=None, a_gate=None, b_gate=None, a_up=None, b_up=None):
+        import torch
+        self.N, self.K = int(N), int(K)
+        dev = w_gate.device
+        rg = 0 if lora_down_gate is None else lora_down_gate.shape[1]
+        ru = 0 if lora_down_up is None else lora_down_up.shape[1]
+        self.R = rg + ru
+        ld = lu = None
+        if self.R:
+            parts = [t for t in (lora_down_gate, lora_down_up) if t is not None]
+            ld = torch.cat(parts, dim=1).contiguous()
+            lug = torch.zeros((self.N, self.R), dtype=torch.float16, device=dev)
+            luu = torch.zeros((self.N, self.R), dtype=torch.float16, device=dev)
+            if rg:
+                lug[:, :rg] = lora_up_gate
+            if ru:
+                luu[:, rg:] = lora_up_up
+            lu = interleave_gate_up(lug, luu)
+        ones = torch.ones(self.N, dtype=torch.float32, device=dev)
+        zeros = torch.zeros(self.N, dtype=torch.float32, device=dev)
+        a = interleave_gate_up(ones if a_gate is None else a_gate, ones if a_up is None else a_up)
+        b = interleave_gate_up(zeros if b_gate is None else b_gate, zeros if b_up is None else b_up)
+        w = interleave_gate_up(w_gate, w_up)
+        self.wblob = alloc_weight_blob(2 * self.N, self.K, self.R, device=dev)
+        w4a4_pack_weights(2 * self.N, self.K, self.R, self.wblob, w_fp16=w, lora_down=ld, lora_up=lu,
+                          col_scale=a, bias=b)
+
+    def forward(self, x, act=None, h=None, stream=None):
+        import torch
+        M = x.shape[0]
+        if act is None:
+            act = alloc_act_blob(M, self.K, self.R, device=x.device)
+        if h is None:
+            h = torch.empty((M, self.N), dtype=torch.float16, device=x.device)
+        w4a4_quantize_act(M, self.K, self.R, x, self.wblob, act, stream=stream)
+        w4a4_linear_glu(M, 2 * self.N, self.K, self.R, act, self.wblob, h, stream=stream)
+        return h
 
 
 class LayerGraphs:

@@ -29,14 +29,18 @@ int check_m(int64_t M) {
   return W4A4_OK;
 }
 
-int hip_status(hipError_t e) { return e == hipSuccess ? W4A4_OK : W4A4_ERR_HIP; }
-
 bool log_enabled() {
   static const bool on = [] {
     const char* v = std::getenv("W4A4_LOG");
     return v && v[0] && v[0] != '0';
   }();
   return on;
+}
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return W4A4_OK;
+  if (log_enabled()) std::fprintf(stderr, "w4a4: HIP error %d (%s)\n", (int)e, hipGetErrorName(e));
+  return W4A4_ERR_HIP;
 }
 
 const char* variant_name(int v) {
@@ -126,11 +130,11 @@ int w4a4_pack_weights(int64_t N, int64_t K, int32_t R, const uint16_t* w_fp16,
     e = launch_quantize_rows(w_fp16, K, N, N, K, 0, 1, nullptr, wq, sw, nullptr, nullptr, 0.0, s);
   else
     e = launch_repack_qweight(qweight, w_scales, N, K, wq, sw, s);
-  if (e != hipSuccess) return W4A4_ERR_HIP;
+  if (e != hipSuccess) return hip_status(e);
   e = launch_pack_lora(lora_down, lora_up, N, K, R,
                        reinterpret_cast<uint16_t*>(base + g.off_ldown),
                        reinterpret_cast<uint16_t*>(base + g.off_lup), s);
-  if (e != hipSuccess) return W4A4_ERR_HIP;
+  if (e != hipSuccess) return hip_status(e);
   e = launch_pack_affine(col_scale, bias, N, reinterpret_cast<float*>(base + g.off_a),
                          reinterpret_cast<float*>(base + g.off_b), s);
   return hip_status(e);
@@ -174,7 +178,9 @@ int w4a4_quantize_act_rmsnorm(int64_t M, int64_t K, int32_t R, const uint16_t* x
 }
 
 static int make_gemm_args(int64_t M, int64_t N, int64_t K, int32_t R, const void* act,
-                          const void* wblob, uint16_t* y, int64_t ldy, GemmArgs* a) {
+                          const void* wblob, uint16_t* y, int64_t ldy, GemmArgs* a,
+                          int64_t ycols = -1) {
+  if (ycols < 0) ycols = N;
   int st = check_nkr(N, K, R);
   if (st) return st;
   if ((st = check_m(M))) return st;
@@ -202,7 +208,7 @@ static int make_gemm_args(int64_t M, int64_t N, int64_t K, int32_t R, const void
   // y must not overlap either blob
   if (y) {
     const uint8_t* yb = reinterpret_cast<const uint8_t*>(y);
-    const uint8_t* ye = yb + (size_t)(M > 0 ? (M - 1) * ldy + N : 0) * 2;
+    const uint8_t* ye = yb + (size_t)(M > 0 ? (M - 1) * ldy + ycols : 0) * 2;
     if ((yb < ab + ag.total && ab < ye) || (yb < wb + wg.total && wb < ye)) return W4A4_ERR_ARG;
   }
   return W4A4_OK;
@@ -222,6 +228,26 @@ int w4a4_linear(int64_t M, int64_t N, int64_t K, int32_t R, const void* act,
   const int v = choose_variant(M, N, K, R);
   if (log_enabled())
     std::fprintf(stderr, "w4a4_linear M=%lld N=%lld K=%lld R=%d -> %s\n", (long long)M,
+                 (long long)N, (long long)K, R, variant_name(v));
+  return hip_status(launch_gemm(a, v, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int w4a4_linear_glu(int64_t M, int64_t N, int64_t K, int32_t R, const void* act,
+                    const void* wblob, uint16_t* y, int64_t ldy, void* stream) {
+  int st = check_nkr(N, K, R);
+  if (st) return st;
+  if (N % 32 != 0) return W4A4_ERR_SHAPE;   // whole (gate, up) tile pairs
+  if ((st = check_m(M))) return st;
+  if (M == 0) return W4A4_OK;
+  if (!y) return W4A4_ERR_NULL;
+  if (ldy < N / 2) return W4A4_ERR_SHAPE;
+  if (ldy % 8 != 0 || !aligned(y, 16)) return W4A4_ERR_ALIGN;
+  GemmArgs a;
+  if ((st = make_gemm_args(M, N, K, R, act, wblob, y, ldy, &a, N / 2))) return st;
+  a.glu = 1;
+  const int v = choose_variant(M, N, K, R);
+  if (log_enabled())
+    std::fprintf(stderr, "w4a4_linear_glu M=%lld N=%lld K=%lld R=%d -> %s\n", (long long)M,
                  (long long)N, (long long)K, R, variant_name(v));
   return hip_status(launch_gemm(a, v, reinterpret_cast<hipStream_t>(stream)));
 }

@@ -204,6 +204,18 @@ __device__ __forceinline__ v4f lora_up_tile(v4f acc, const GemmArgs& g, int64_t 
   return acc;
 }
 
+// The gated activation of one output value: the gate and up projections'
+// fp16 outputs (their affine applied to the fp32 accumulators and rounded, as
+// each layer on its own would store them), then fp16(SiLU(g) * u) with SiLU
+// and the product in fp64.
+__device__ __forceinline__ uint32_t glu_bits(float ag, float g_acc, float bg, float au, float u_acc,
+                                             float bu) {
+  const double g = (double)(float)(_Float16)fmaf(ag, g_acc, bg);
+  const double u = (double)(float)(_Float16)fmaf(au, u_acc, bu);
+  const double h = g / (1.0 + exp(-g)) * u;
+  return __builtin_bit_cast(uint16_t, (_Float16)h);
+}
+
 // Y[row, col] = fp16(a * acc + b) for the MV leading rows of each lane's four
 // (rows 4c + ii), column col0 + (lane & 15).
 template <int MV>
@@ -221,21 +233,31 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, v4f acc, int64_t r
   }
 }
 
+template <int MV>
+__device__ __forceinline__ void store_tile_glu(const GemmArgs& g, v4f gacc, v4f uacc, int64_t row0,
+                                               int64_t col0, float ag, float bg, float au, float bu,
+                                               int lane) {
+  const int c = lane >> 4, r = lane & 15;
+  const int64_t col = col0 + r;
+#pragma unroll
+  for (int ii = 0; ii < MV; ++ii) {
+    const int64_t row = row0 + c * 4 + ii;
+    if (row < g.M) g.y[row * g.ldy + col] = (uint16_t)glu_bits(ag, gacc[ii], bg, au, uacc[ii], bu);
+  }
+}
+
 // Same for a tile known to start at a row < M: one 64-bit address per lane,
 // then the four rows at a stride of ldy; only a ragged last tile pays a
 // per-row check.
-__device__ __forceinline__ void store_tile4(const GemmArgs& g, v4f acc, int64_t row0, int64_t col0,
-                                            float af, float bf, int lane) {
-  // Lane (c, r) holds rows 4c..4c+3 of column r.  A 4x4 transpose of the
-  // fp16 values inside each quad of lanes (columns 4q..4q+3, q = r / 4) --
-  // two DPP exchanges and a byte permute -- leaves lane (c, 4q + s) with row
-  // 4c + s, columns 4q..4q+3: one 8-byte store per lane instead of four
-  // 2-byte ones (ldy % 8 == 0 and a 16-byte aligned y keep it aligned).
+
+// Lane (c, r) holds rows 4c..4c+3 of column r as fp16 bits h[0..3].  A 4x4
+// transpose inside each quad of lanes (columns 4q..4q+3, q = r / 4) -- two
+// DPP exchanges and a byte permute -- leaves lane (c, 4q + s) with row
+// 4c + s, columns 4q..4q+3: one 8-byte store per lane instead of four 2-byte
+// ones (ldy % 8 == 0 and a 16-byte aligned y keep it aligned).
+__device__ __forceinline__ void store_tile4_bits(const GemmArgs& g, const uint32_t (&h)[4], int64_t row0,
+                                                 int64_t col0, int lane) {
   const int c = lane >> 4, r = lane & 15, s = lane & 3;
-  uint32_t h[4];
-#pragma unroll
-  for (int ii = 0; ii < 4; ++ii)
-    h[ii] = __builtin_bit_cast(uint16_t, (_Float16)fmaf(af, acc[ii], bf));
   uint32_t d0 = h[0] | (h[1] << 16), d1 = h[2] | (h[3] << 16);
   // 2x2 blocks across lane ^ 2: lanes 0,1 take the partner's low pair as
   // their high pair, lanes 2,3 the partner's high pair as their low pair
@@ -251,6 +273,25 @@ __device__ __forceinline__ void store_tile4(const GemmArgs& g, v4f acc, int64_t 
   const int64_t row = row0 + c * 4 + s;
   if (row < g.M)
     *reinterpret_cast<v2u*>(g.y + row * g.ldy + col0 + (r & ~3)) = v2u{d0, d1};
+}
+
+__device__ __forceinline__ void store_tile4(const GemmArgs& g, v4f acc, int64_t row0, int64_t col0,
+                                            float af, float bf, int lane) {
+  uint32_t h[4];
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii)
+    h[ii] = __builtin_bit_cast(uint16_t, (_Float16)fmaf(af, acc[ii], bf));
+  store_tile4_bits(g, h, row0, col0, lane);
+}
+
+// Gated pair: output tile col0 (in y's N/2 columns) from gate and up tiles.
+__device__ __forceinline__ void store_tile4_glu(const GemmArgs& g, v4f gacc, v4f uacc, int64_t row0,
+                                                int64_t col0, float ag, float bg, float au, float bu,
+                                                int lane) {
+  uint32_t h[4];
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii) h[ii] = glu_bits(ag, gacc[ii], bg, au, uacc[ii], bu);
+  store_tile4_bits(g, h, row0, col0, lane);
 }
 
 // One 64-group of one 16x16 tile: an i8 MFMA with a zero C (256 P exactly)
@@ -457,13 +498,19 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_kernel(GemmArgs g) {
   for (int n = 0; n < NTW; ++n) red[n][wave][lane] = acc[n] * (1.0f / 256.0f);   // the int8 operands carry 16 q each
   __syncthreads();
   if (wave != 0) return;
+  v4f av[NTW];
 #pragma unroll
   for (int n = 0; n < NTW; ++n) {
     v4f a = red[n][0][lane];
 #pragma unroll
     for (int w = 1; w < kDecodeWaves; ++w) a += red[n][w][lane];
-    a += a_lora[n];
-    store_tile<MV>(g, a, 0, (nt0 + n) * 16, af[n], bf[n], lane);
+    av[n] = a + a_lora[n];
+  }
+  if (!g.glu) {
+#pragma unroll
+    for (int n = 0; n < NTW; ++n) store_tile<MV>(g, av[n], 0, (nt0 + n) * 16, af[n], bf[n], lane);
+  } else if constexpr (NTW == 2) {   // the workgroup's tiles are a (gate, up) pair
+    store_tile_glu<MV>(g, av[0], av[1], 0, (nt0 / 2) * 16, af[0], bf[0], af[1], bf[1], lane);
   }
 }
 
@@ -721,6 +768,7 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_dot_kernel(GemmArgs g) {
   __syncthreads();
   if (wave != 0) return;
   // accumulator layout of a 16x16 tile: lane (c, r) holds rows 4c + ii of column r
+  v4f av[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
     v4f a = a_lora[n];
@@ -733,7 +781,13 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_dot_kernel(GemmArgs g) {
         a[m] += v;
       }
     }
-    store_tile<MR>(g, a, 0, (nt0 + n) * 16, af[n], bf[n], lane);
+    av[n] = a;
+  }
+  if (!g.glu) {
+#pragma unroll
+    for (int n = 0; n < NT; ++n) store_tile<MR>(g, av[n], 0, (nt0 + n) * 16, af[n], bf[n], lane);
+  } else if constexpr (NT == 2) {   // the workgroup's tiles are a (gate, up) pair
+    store_tile_glu<MR>(g, av[0], av[1], 0, (nt0 / 2) * 16, af[0], bf[0], af[1], bf[1], lane);
   }
 }
 
@@ -970,27 +1024,48 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void gemm_tiled_kernel(GemmArgs g,
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] *= (1.0f / 256.0f);
 
+  // LoRA-up of tile (i, j): lora_act rows of row tile i (partials summed in
+  // order, split into fp16 hi + lo) times the L_up fragment of column tile j
+  auto lora_tile = [&](int i, int j) {
+    v4f a = acc[i][j];
 #pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int64_t nt = nt0 + wn * TN + j;
-    if (nt >= nt_count) continue;
+    for (int t = 0; t < RT; ++t) {
+      v4f l4 = la_p[0][i][t];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int64_t mt = mt0 + wm * TM + i;
-      if (mt >= mt_count) continue;
-      v4f a = acc[i][j];
+      for (int jj = 1; jj < SPL; ++jj)
+        if (jj < g.ks) l4 += la_p[jj][i][t];
+      v4h hi, lo;
+      split_f16(l4, hi, lo);
+      a = mfma_f16_16x16x16(hi, lu_f[j][t], a);
+      a = mfma_f16_16x16x16(lo, lu_f[j][t], a);
+    }
+    return a;
+  };
+  if (!g.glu) {
 #pragma unroll
-      for (int t = 0; t < RT; ++t) {
-        v4f l4 = la_p[0][i][t];
+    for (int j = 0; j < TN; ++j) {
+      const int64_t nt = nt0 + wn * TN + j;
+      if (nt >= nt_count) continue;
 #pragma unroll
-        for (int jj = 1; jj < SPL; ++jj)
-          if (jj < g.ks) l4 += la_p[jj][i][t];
-        v4h hi, lo;
-        split_f16(l4, hi, lo);
-        a = mfma_f16_16x16x16(hi, lu_f[j][t], a);
-        a = mfma_f16_16x16x16(lo, lu_f[j][t], a);
+      for (int i = 0; i < TM; ++i) {
+        const int64_t mt = mt0 + wm * TM + i;
+        if (mt < mt_count) store_tile4(g, lora_tile(i, j), mt * 16, nt * 16, af[j], bf[j], lane);
       }
-      store_tile4(g, a, mt * 16, nt * 16, af[j], bf[j], lane);
+    }
+  } else if constexpr (TN % 2 == 0) {
+    // (gate, up) tile pairs: the launcher picks shapes whose wave column
+    // tiles start on an even tile, so pairs never straddle waves
+#pragma unroll
+    for (int j = 0; j < TN; j += 2) {
+      const int64_t nt = nt0 + wn * TN + j;
+      if (nt >= nt_count) continue;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int64_t mt = mt0 + wm * TM + i;
+        if (mt < mt_count)
+          store_tile4_glu(g, lora_tile(i, j), lora_tile(i, j + 1), mt * 16, (nt / 2) * 16, af[j], bf[j],
+                          af[j + 1], bf[j + 1], lane);
+      }
     }
   }
 }
@@ -1000,7 +1075,7 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void gemm_tiled_kernel(GemmArgs g,
 // small batches measured best: the per-k-pair arithmetic here is heavy enough
 // that starting it early beats keeping more bytes in flight per wave.
 constexpr int mv_kb(int rt, int ntw) {
-  constexpr int kTable[2][5] = {{4, 4, 2, 2, 2}, {4, 2, 2, 2, 0}};
+  constexpr int kTable[2][5] = {{4, 4, 2, 2, 2}, {4, 2, 2, 2, 1}};
   return kTable[ntw - 1][rt];
 }
 
@@ -1012,12 +1087,7 @@ static hipError_t launch_decode_mv_n(const GemmArgs& a, hipStream_t stream) {
     case 1: gemm_decode_kernel<MV, 1, mv_kb(1, NTW), NTW><<<grid, block, 0, stream>>>(a); break;
     case 2: gemm_decode_kernel<MV, 2, mv_kb(2, NTW), NTW><<<grid, block, 0, stream>>>(a); break;
     case 3: gemm_decode_kernel<MV, 3, mv_kb(3, NTW), NTW><<<grid, block, 0, stream>>>(a); break;
-    case 4:
-      if constexpr (NTW == 1) {   // rank 64 with two column tiles does not fit 128 VGPRs
-        gemm_decode_kernel<MV, 4, mv_kb(4, NTW), NTW><<<grid, block, 0, stream>>>(a);
-        break;
-      }
-      return hipErrorInvalidValue;
+    case 4: gemm_decode_kernel<MV, 4, mv_kb(4, NTW), NTW><<<grid, block, 0, stream>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1025,11 +1095,12 @@ static hipError_t launch_decode_mv_n(const GemmArgs& a, hipStream_t stream) {
 
 // Two column tiles per workgroup (one activation tile serves both) when the
 // column tiles pair up, there are still >= 256 workgroups and the rank leaves
-// room in 128 VGPRs (R <= 48); else one.
+// room in 128 VGPRs (R <= 48); else one.  A gated output always takes two
+// (its (gate, up) pair; rank 64 then spills a few registers).
 template <int MV>
 static hipError_t launch_decode_mv(const GemmArgs& a, hipStream_t stream) {
   const int64_t ntiles = a.N / 16;
-  if (ntiles % 2 == 0 && ntiles / 2 >= 256 && a.R <= 48) return launch_decode_mv_n<MV, 2>(a, stream);
+  if (a.glu || (ntiles % 2 == 0 && ntiles / 2 >= 256 && a.R <= 48)) return launch_decode_mv_n<MV, 2>(a, stream);
   return launch_decode_mv_n<MV, 1>(a, stream);
 }
 
@@ -1074,11 +1145,12 @@ static hipError_t launch_decode_dot_n(const GemmArgs& a, hipStream_t stream) {
 
 // Two column tiles per workgroup (sharing the activation chunks, the
 // LoRA-down fold and the cross-wave reduction) when they pair up and at
-// least 256 workgroups remain; else one.
+// least 256 workgroups remain; else one.  A gated output always takes two
+// (its (gate, up) pair).
 template <int MR>
 static hipError_t launch_decode_dot(const GemmArgs& a, hipStream_t stream) {
   const int64_t ntiles = a.N / 16;
-  if (ntiles % 2 == 0 && ntiles / 2 >= 256) return launch_decode_dot_n<MR, 2>(a, stream);
+  if (a.glu || (ntiles % 2 == 0 && ntiles / 2 >= 256)) return launch_decode_dot_n<MR, 2>(a, stream);
   return launch_decode_dot_n<MR, 1>(a, stream);
 }
 
@@ -1188,14 +1260,16 @@ static bool tiled_fits(const TiledCfg& c, int R, int ks) {
   return ks == 1 || c.tm * (R / 16) * kMaxTiledLoraSplits <= 16;
 }
 
-static int pick_tiled(int64_t M, int64_t N, int64_t K, int R, int ks) {
+static int pick_tiled(int64_t M, int64_t N, int64_t K, int R, int ks, bool glu) {
+  // gated output: a wave's column tiles must hold whole (gate, up) pairs
+  auto ok = [&](const TiledCfg& c) { return tiled_fits(c, R, ks) && (!glu || c.tn % 2 == 0); };
   const int ov = tiled_override();
-  if (ov >= 0 && tiled_fits(kTiledCfgs[ov], R, ks)) return ov;
+  if (ov >= 0 && ok(kTiledCfgs[ov])) return ov;
   const int64_t mt = round_up16(M) / 16, nt = N / 16, kp = K / kKPair;
   int best = -1;
   double best_c = 0;
   for (int i = 0; i < kNumTiledCfgs; ++i) {
-    if (!tiled_fits(kTiledCfgs[i], R, ks)) continue;
+    if (!ok(kTiledCfgs[i])) continue;
     const double c = tiled_cost(kTiledCfgs[i], mt, nt, kp);
     if (best < 0 || c < best_c) {
       best_c = c;
@@ -1234,14 +1308,15 @@ hipError_t launch_gemm(const GemmArgs& a, int variant, hipStream_t stream) {
       return launch_decode(a, stream);
     case kPrefill:
       if (a.ks < 1 || a.ks > kMaxTiledLoraSplits) return hipErrorInvalidValue;   // lora_splits() for M > 16
-      switch (pick_tiled(a.M, a.N, a.K, a.R, a.ks)) {
+      switch (pick_tiled(a.M, a.N, a.K, a.R, a.ks, a.glu != 0)) {
         case 0: return launch_tiled_cfg<2, 2, 4, 4>(a, stream);
         case 1: return launch_tiled_cfg<2, 2, 2, 4>(a, stream);
         case 2: return launch_tiled_cfg<2, 2, 4, 2>(a, stream);
         case 3: return launch_tiled_cfg<2, 2, 2, 2>(a, stream);
         case 4: return launch_tiled_cfg<2, 2, 1, 2>(a, stream);
         case 5: return launch_tiled_cfg<4, 1, 1, 3>(a, stream);
-        default: return launch_tiled_cfg<1, 4, 3, 1>(a, stream);
+        case 6: return launch_tiled_cfg<1, 4, 3, 1>(a, stream);
+        default: return hipErrorInvalidValue;   // no tile shape fits (R, ks, gated)
       }
     default:
       return launch_generic_rt<2, 2, false>(a, 0, mt, 0, nt, nullptr, 0, stream);

@@ -119,6 +119,10 @@ struct GemmArgs {
   int64_t M, N, K;
   int R;
   int ks;   // LoRA-down partials in la: [ks][Mp][R]
+  // Gated output (MLP): column tiles come in (gate, up) pairs -- tile 2j is
+  // gate columns 16j.., tile 2j+1 the up columns 16j.. -- and y gets
+  // h = fp16(SiLU(gate) * up) with N/2 columns instead of the N columns.
+  int glu = 0;
 };
 
 enum Variant { kGeneric = 0, kDecode = 1, kPrefill = 2 };

@@ -96,7 +96,7 @@ def test_glu_strided_output(M):
     assert np.all(np.isnan(h[:, N:].astype(np.float64)))
 
 
-@pytest.mark.parametrize("cfg", range(7))
+@pytest.mark.parametrize("cfg", range(9))
 def test_glu_every_tile_shape(cfg, monkeypatch):
     """Each M > 16 tile shape forced in turn (shapes whose waves hold an odd
     number of column tiles cannot pair gate with up and fall back to the

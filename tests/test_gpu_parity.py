@@ -279,7 +279,7 @@ def test_small_m_decode_shapes(M, K, N, R):
     assert np.all(np.isnan(run.host_y()[M:].astype(np.float64)))
 
 
-@pytest.mark.parametrize("cfg,K", [(c, 512) for c in range(7)] + [(c, 2048) for c in range(7)])
+@pytest.mark.parametrize("cfg,K", [(c, 512) for c in range(9)] + [(c, 2048) for c in range(9)])
 def test_every_tile_shape(cfg, K, monkeypatch):
     """Each M > 16 tile shape (forced) on a shape with ragged row and column
     edges for all of them: M = 130 (9 row tiles), N = 208 (13 column tiles);

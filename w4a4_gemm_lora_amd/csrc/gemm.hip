@@ -206,13 +206,19 @@ __device__ __forceinline__ v4f lora_up_tile(v4f acc, const GemmArgs& g, int64_t 
 
 // The gated activation of one output value: the gate and up projections'
 // fp16 outputs (their affine applied to the fp32 accumulators and rounded, as
-// each layer on its own would store them), then fp16(SiLU(g) * u) with SiLU
-// and the product in fp64.
+// each layer on its own would store them), then fp16(SiLU(g) * u).  SiLU in
+// fp32 from the hardware base-2 exponential and reciprocal (about 1 ulp
+// each, plus the rounding of the exponent's argument), so SiLU(g) * u before
+// the fp16 rounding is within about 1e-6 relative of its exact value for
+// |g| <= 20 -- some 500 times finer than that rounding (2^-11); beyond, the
+// value is g * u or far below fp16's range.  e = 2^(-g log2 e) overflows to
+// +inf for g below about -88, and g * rcp(inf) = g * 0 is the signed zero.
 __device__ __forceinline__ uint32_t glu_bits(float ag, float g_acc, float bg, float au, float u_acc,
                                              float bu) {
-  const double g = (double)(float)(_Float16)fmaf(ag, g_acc, bg);
-  const double u = (double)(float)(_Float16)fmaf(au, u_acc, bu);
-  const double h = g / (1.0 + exp(-g)) * u;
+  const float g = (float)(_Float16)fmaf(ag, g_acc, bg);
+  const float u = (float)(_Float16)fmaf(au, u_acc, bu);
+  const float e = __builtin_amdgcn_exp2f(g * -1.44269504088896341f);
+  const float h = g * __builtin_amdgcn_rcpf(1.0f + e) * u;
   return __builtin_bit_cast(uint16_t, (_Float16)h);
 }
 
@@ -341,7 +347,36 @@ __device__ __forceinline__ v4f scale_tile(uint32_t sx_pair, uint32_t sw_pair, in
 // ---------------------------------------------------------------------------
 constexpr int kDecodeWaves = 4;
 
-template <int MV, int RT, int KB, int NTW>
+// The LoRA operands of the decode epilogue: lora_act partials j = wave,
+// wave + 4 (< ks) of rows < M as unconditional loads (clamped addresses:
+// lanes of rows >= M read row 0, out-of-range j re-read a valid partial;
+// both are zeroed when folded), and for wave 0 the L_up fragments of the
+// workgroup's NTW column tiles.
+template <int RT, int NTW, int LQ, int RTL>
+__device__ __forceinline__ void decode_lora_loads(const GemmArgs& g, int64_t nt0, int wave, int lane,
+                                                  v4f (&lpart)[LQ][RTL], v4h (&lup)[NTW][RTL]) {
+  if constexpr (RT > 0) {
+    const int c = lane >> 4, r = lane & 15;
+    const int rr = r < g.M ? r : 0;
+#pragma unroll
+    for (int q = 0; q < LQ; ++q) {
+      const int j0 = wave + q * kDecodeWaves;
+      const int j = j0 < g.ks ? j0 : g.ks - 1;
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+        lpart[q][t] = *reinterpret_cast<const v4f*>(g.la + ((size_t)j * 16 + rr) * g.R + t * 16 + c * 4);
+    }
+    if (wave == 0) {
+#pragma unroll
+      for (int n = 0; n < NTW; ++n)
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+          lup[n][t] = *reinterpret_cast<const v4h*>(g.lup + (((size_t)(nt0 + n) * RT + t) * 64 + lane) * 4);
+    }
+  }
+}
+
+template <int MV, int RT, int KB, int NTW, bool GLU>
 __global__ __launch_bounds__(256, 4) void gemm_decode_kernel(GemmArgs g) {
   constexpr int RTL = RT > 0 ? RT : 1;
   __shared__ v4f red[NTW][kDecodeWaves][64];
@@ -355,17 +390,20 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_kernel(GemmArgs g) {
   const int64_t p1 = p0 + per < KP ? p0 + per : KP;
   const int c = lane >> 4, r = lane & 15;
 
-  // Epilogue operands, issued before the weight stream.  LoRA-down partials
-  // j = wave, wave + 4 (< ks) of rows < M: unconditional loads (clamped
-  // addresses: lanes of rows >= M read row 0, out-of-range j re-read a valid
-  // partial; both are zeroed when folded), so that no wait for them precedes
-  // the weight loads.  Wave 0 also takes the L_up fragments and the affine of
-  // its columns.
+  // Epilogue operands, issued before the weight stream (unconditional loads,
+  // so that no wait for them precedes the weight loads); wave 0 also takes
+  // the affine of its columns.  At rank 64 with two column tiles the LoRA
+  // operands would not fit the registers beside a weight batch of useful
+  // size: that instance loads them after the stream instead (one more memory
+  // round trip in the tail).
+  constexpr bool kEarly = !(RT == 4 && NTW == 2);
   constexpr int LQ = (kMaxLoraSplits + kDecodeWaves - 1) / kDecodeWaves;
   v4f lpart[LQ][RTL];
   v4h lup[NTW][RTL];
   float af[NTW], bf[NTW];
-  if constexpr (RT > 0) {
+  if constexpr (kEarly && RT > 0) {
+    // decode_lora_loads written out: as a call, the rank-64 one-tile
+    // instance no longer fits its registers (the allocator spills)
     const int rr = r < g.M ? r : 0;
 #pragma unroll
     for (int q = 0; q < LQ; ++q) {
@@ -465,7 +503,7 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_kernel(GemmArgs g) {
       sxw[u] = *reinterpret_cast<const uint32_t*>(sxq + (size_t)p * 64);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (!lora_done) {
+    if (kEarly && !lora_done) {
       lora_early();
       lora_done = true;
     }
@@ -491,6 +529,7 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_kernel(GemmArgs g) {
       }
     }
   }
+  if constexpr (!kEarly) decode_lora_loads<RT, NTW, LQ>(g, nt0, wave, lane, lpart, lup);
   if (!lora_done) lora_early();   // a wave with no k-pairs still meets the barrier
 
   // cross-wave sums in LDS, added by wave 0 in wave order
@@ -506,10 +545,11 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_kernel(GemmArgs g) {
     for (int w = 1; w < kDecodeWaves; ++w) a += red[n][w][lane];
     av[n] = a + a_lora[n];
   }
-  if (!g.glu) {
+  if constexpr (!GLU) {
 #pragma unroll
     for (int n = 0; n < NTW; ++n) store_tile<MV>(g, av[n], 0, (nt0 + n) * 16, af[n], bf[n], lane);
-  } else if constexpr (NTW == 2) {   // the workgroup's tiles are a (gate, up) pair
+  } else {   // the workgroup's tiles are a (gate, up) pair
+    static_assert(NTW == 2, "a gated output needs both tiles of its pair");
     store_tile_glu<MV>(g, av[0], av[1], 0, (nt0 / 2) * 16, af[0], bf[0], af[1], bf[1], lane);
   }
 }
@@ -626,7 +666,7 @@ __device__ __forceinline__ void dot_accumulate(const DotBatch<MR, KB, NT>& d, co
   }
 }
 
-template <int MR, int RT, int KB, int NT>
+template <int MR, int RT, int KB, int NT, bool GLU>
 __global__ __launch_bounds__(256, 4) void gemm_decode_dot_kernel(GemmArgs g) {
   constexpr int RTL = RT > 0 ? RT : 1;
   __shared__ float red[NT][kDecodeWaves][MR][16];
@@ -783,10 +823,11 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_dot_kernel(GemmArgs g) {
     }
     av[n] = a;
   }
-  if (!g.glu) {
+  if constexpr (!GLU) {
 #pragma unroll
     for (int n = 0; n < NT; ++n) store_tile<MR>(g, av[n], 0, (nt0 + n) * 16, af[n], bf[n], lane);
-  } else if constexpr (NT == 2) {   // the workgroup's tiles are a (gate, up) pair
+  } else {   // the workgroup's tiles are a (gate, up) pair
+    static_assert(NT == 2, "a gated output needs both tiles of its pair");
     store_tile_glu<MR>(g, av[0], av[1], 0, (nt0 / 2) * 16, af[0], bf[0], af[1], bf[1], lane);
   }
 }
@@ -808,7 +849,7 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_dot_kernel(GemmArgs g) {
 // ---------------------------------------------------------------------------
 constexpr int kTileGroupRows = 8;
 
-template <int WM, int WN, int TM, int TN, int RT, int NS, int SPL>
+template <int WM, int WN, int TM, int TN, int RT, int NS, int SPL, bool GLU>
 __global__ __launch_bounds__(WM * WN * 64, 2) void gemm_tiled_kernel(GemmArgs g, int64_t mt_count,
                                                                  int64_t nt_count) {
   constexpr int NW = WM * WN;
@@ -923,9 +964,13 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void gemm_tiled_kernel(GemmArgs g,
       lu_f[j][t] = *reinterpret_cast<const v4h*>(g.lup + (((size_t)nt * RT + t) * 64 + lane) * 4);
   }
   // lora_act comes as g.ks <= SPL K-range partials; all of them are loaded
-  // here and summed in order in the epilogue (no wait before the K loop).
-  v4f la_p[SPL][TM][RTL];
-  if constexpr (RT > 0) {
+  // here and summed in order in the epilogue (no wait before the K loop) --
+  // unless they would take more than 64 registers through the loop: then the
+  // epilogue loads them rank block by rank block (one more memory round trip
+  // per workgroup).
+  constexpr bool kLateLora = TM * RT * SPL > 16;
+  v4f la_p[kLateLora ? 1 : SPL][TM][RTL];
+  if constexpr (!kLateLora && RT > 0) {
     const size_t part = (size_t)round_up16(g.M) * g.R;   // floats per partial
 #pragma unroll
     for (int j = 0; j < SPL; ++j) {
@@ -1025,23 +1070,46 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void gemm_tiled_kernel(GemmArgs g,
     for (int j = 0; j < TN; ++j) acc[i][j] *= (1.0f / 256.0f);
 
   // LoRA-up of tile (i, j): lora_act rows of row tile i (partials summed in
-  // order, split into fp16 hi + lo) times the L_up fragment of column tile j
+  // order, split into fp16 hi + lo) times the L_up fragment of column tile j,
+  // rank block by rank block
+  if constexpr (kLateLora) {
+    const size_t part = (size_t)round_up16(g.M) * g.R;
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const float* lp = g.la + (size_t)(tile_index(wm * TM + i) * 16 + (lane & 15)) * g.R + t * 16 + c * 4;
+        v4f l4 = *reinterpret_cast<const v4f*>(lp);
+#pragma unroll
+        for (int jj = 1; jj < SPL; ++jj)
+          if (jj < g.ks) l4 += *reinterpret_cast<const v4f*>(lp + jj * part);
+        v4h hi, lo;
+        split_f16(l4, hi, lo);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          acc[i][j] = mfma_f16_16x16x16(hi, lu_f[j][t], acc[i][j]);
+          acc[i][j] = mfma_f16_16x16x16(lo, lu_f[j][t], acc[i][j]);
+        }
+      }
+  }
   auto lora_tile = [&](int i, int j) {
     v4f a = acc[i][j];
+    if constexpr (!kLateLora) {
 #pragma unroll
-    for (int t = 0; t < RT; ++t) {
-      v4f l4 = la_p[0][i][t];
+      for (int t = 0; t < RT; ++t) {
+        v4f l4 = la_p[0][i][t];
 #pragma unroll
-      for (int jj = 1; jj < SPL; ++jj)
-        if (jj < g.ks) l4 += la_p[jj][i][t];
-      v4h hi, lo;
-      split_f16(l4, hi, lo);
-      a = mfma_f16_16x16x16(hi, lu_f[j][t], a);
-      a = mfma_f16_16x16x16(lo, lu_f[j][t], a);
+        for (int jj = 1; jj < SPL; ++jj)
+          if (jj < g.ks) l4 += la_p[jj][i][t];
+        v4h hi, lo;
+        split_f16(l4, hi, lo);
+        a = mfma_f16_16x16x16(hi, lu_f[j][t], a);
+        a = mfma_f16_16x16x16(lo, lu_f[j][t], a);
+      }
     }
     return a;
   };
-  if (!g.glu) {
+  if constexpr (!GLU) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int64_t nt = nt0 + wn * TN + j;
@@ -1052,9 +1120,10 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void gemm_tiled_kernel(GemmArgs g,
         if (mt < mt_count) store_tile4(g, lora_tile(i, j), mt * 16, nt * 16, af[j], bf[j], lane);
       }
     }
-  } else if constexpr (TN % 2 == 0) {
-    // (gate, up) tile pairs: the launcher picks shapes whose wave column
-    // tiles start on an even tile, so pairs never straddle waves
+  } else {
+    // (gate, up) tile pairs: a wave's column tiles start on an even tile, so
+    // pairs never straddle waves
+    static_assert(TN % 2 == 0, "a gated output needs whole tile pairs per wave");
 #pragma unroll
     for (int j = 0; j < TN; j += 2) {
       const int64_t nt = nt0 + wn * TN + j;
@@ -1075,19 +1144,19 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void gemm_tiled_kernel(GemmArgs g,
 // small batches measured best: the per-k-pair arithmetic here is heavy enough
 // that starting it early beats keeping more bytes in flight per wave.
 constexpr int mv_kb(int rt, int ntw) {
-  constexpr int kTable[2][5] = {{4, 4, 2, 2, 2}, {4, 2, 2, 2, 1}};
+  constexpr int kTable[2][5] = {{4, 4, 2, 2, 2}, {4, 2, 2, 2, 4}};
   return kTable[ntw - 1][rt];
 }
 
-template <int MV, int NTW>
+template <int MV, int NTW, bool GLU>
 static hipError_t launch_decode_mv_n(const GemmArgs& a, hipStream_t stream) {
   dim3 grid((unsigned)(a.N / 16 / NTW)), block(64 * kDecodeWaves);
   switch (a.R / 16) {
-    case 0: gemm_decode_kernel<MV, 0, mv_kb(0, NTW), NTW><<<grid, block, 0, stream>>>(a); break;
-    case 1: gemm_decode_kernel<MV, 1, mv_kb(1, NTW), NTW><<<grid, block, 0, stream>>>(a); break;
-    case 2: gemm_decode_kernel<MV, 2, mv_kb(2, NTW), NTW><<<grid, block, 0, stream>>>(a); break;
-    case 3: gemm_decode_kernel<MV, 3, mv_kb(3, NTW), NTW><<<grid, block, 0, stream>>>(a); break;
-    case 4: gemm_decode_kernel<MV, 4, mv_kb(4, NTW), NTW><<<grid, block, 0, stream>>>(a); break;
+    case 0: gemm_decode_kernel<MV, 0, mv_kb(0, NTW), NTW, GLU><<<grid, block, 0, stream>>>(a); break;
+    case 1: gemm_decode_kernel<MV, 1, mv_kb(1, NTW), NTW, GLU><<<grid, block, 0, stream>>>(a); break;
+    case 2: gemm_decode_kernel<MV, 2, mv_kb(2, NTW), NTW, GLU><<<grid, block, 0, stream>>>(a); break;
+    case 3: gemm_decode_kernel<MV, 3, mv_kb(3, NTW), NTW, GLU><<<grid, block, 0, stream>>>(a); break;
+    case 4: gemm_decode_kernel<MV, 4, mv_kb(4, NTW), NTW, GLU><<<grid, block, 0, stream>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1096,12 +1165,13 @@ static hipError_t launch_decode_mv_n(const GemmArgs& a, hipStream_t stream) {
 // Two column tiles per workgroup (one activation tile serves both) when the
 // column tiles pair up, there are still >= 256 workgroups and the rank leaves
 // room in 128 VGPRs (R <= 48); else one.  A gated output always takes two
-// (its (gate, up) pair; rank 64 then spills a few registers).
+// (its (gate, up) pair).
 template <int MV>
 static hipError_t launch_decode_mv(const GemmArgs& a, hipStream_t stream) {
   const int64_t ntiles = a.N / 16;
-  if (a.glu || (ntiles % 2 == 0 && ntiles / 2 >= 256 && a.R <= 48)) return launch_decode_mv_n<MV, 2>(a, stream);
-  return launch_decode_mv_n<MV, 1>(a, stream);
+  if (a.glu) return launch_decode_mv_n<MV, 2, true>(a, stream);
+  if (ntiles % 2 == 0 && ntiles / 2 >= 256 && a.R <= 48) return launch_decode_mv_n<MV, 2, false>(a, stream);
+  return launch_decode_mv_n<MV, 1, false>(a, stream);
 }
 
 
@@ -1118,26 +1188,26 @@ constexpr int dot_kb(int mr, int rt, int nt) {
 // A wave whose k range is shorter than one batch would run only the
 // bounds-checked tail batch, whose conditional loads make every wait a full
 // drain; a 4-pair batch keeps such short ranges on the unchecked path.
-template <int MR, int RT, int NT>
+template <int MR, int RT, int NT, bool GLU>
 static void launch_dot_rt(const GemmArgs& a, hipStream_t stream) {
   constexpr int KB = dot_kb(MR, RT, NT);
   constexpr int KBS = KB < 4 ? KB : 4;
   const dim3 grid((unsigned)(a.N / 16 / NT)), block(64 * kDecodeWaves);
   const int64_t per = (a.K / kKPair + kDecodeWaves - 1) / kDecodeWaves;
   if (KBS < KB && per < KB)
-    gemm_decode_dot_kernel<MR, RT, KBS, NT><<<grid, block, 0, stream>>>(a);
+    gemm_decode_dot_kernel<MR, RT, KBS, NT, GLU><<<grid, block, 0, stream>>>(a);
   else
-    gemm_decode_dot_kernel<MR, RT, KB, NT><<<grid, block, 0, stream>>>(a);
+    gemm_decode_dot_kernel<MR, RT, KB, NT, GLU><<<grid, block, 0, stream>>>(a);
 }
 
-template <int MR, int NT>
+template <int MR, int NT, bool GLU>
 static hipError_t launch_decode_dot_n(const GemmArgs& a, hipStream_t stream) {
   switch (a.R / 16) {
-    case 0: launch_dot_rt<MR, 0, NT>(a, stream); break;
-    case 1: launch_dot_rt<MR, 1, NT>(a, stream); break;
-    case 2: launch_dot_rt<MR, 2, NT>(a, stream); break;
-    case 3: launch_dot_rt<MR, 3, NT>(a, stream); break;
-    case 4: launch_dot_rt<MR, 4, NT>(a, stream); break;
+    case 0: launch_dot_rt<MR, 0, NT, GLU>(a, stream); break;
+    case 1: launch_dot_rt<MR, 1, NT, GLU>(a, stream); break;
+    case 2: launch_dot_rt<MR, 2, NT, GLU>(a, stream); break;
+    case 3: launch_dot_rt<MR, 3, NT, GLU>(a, stream); break;
+    case 4: launch_dot_rt<MR, 4, NT, GLU>(a, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1150,8 +1220,9 @@ static hipError_t launch_decode_dot_n(const GemmArgs& a, hipStream_t stream) {
 template <int MR>
 static hipError_t launch_decode_dot(const GemmArgs& a, hipStream_t stream) {
   const int64_t ntiles = a.N / 16;
-  if (a.glu || (ntiles % 2 == 0 && ntiles / 2 >= 256)) return launch_decode_dot_n<MR, 2>(a, stream);
-  return launch_decode_dot_n<MR, 1>(a, stream);
+  if (a.glu) return launch_decode_dot_n<MR, 2, true>(a, stream);
+  if (ntiles % 2 == 0 && ntiles / 2 >= 256) return launch_decode_dot_n<MR, 2, false>(a, stream);
+  return launch_decode_dot_n<MR, 1, false>(a, stream);
 }
 
 // M <= 4: nibble dot products (about 10 VALU per row and k-pair); larger M:
@@ -1168,44 +1239,31 @@ static hipError_t launch_decode(const GemmArgs& a, hipStream_t stream) {
 
 constexpr int kTiledStages = 4;
 
-template <int WM, int WN, int TM, int TN, int SPL>
+template <int WM, int WN, int TM, int TN, int SPL, bool GLU>
 static hipError_t launch_tiled_spl(const GemmArgs& a, int64_t mt, int64_t nt, dim3 grid, dim3 block,
                                    hipStream_t stream) {
   constexpr int NS = kTiledStages;
   switch (a.R / 16) {
-    case 0: gemm_tiled_kernel<WM, WN, TM, TN, 0, NS, SPL><<<grid, block, 0, stream>>>(a, mt, nt); break;
-    case 1: gemm_tiled_kernel<WM, WN, TM, TN, 1, NS, SPL><<<grid, block, 0, stream>>>(a, mt, nt); break;
-    case 2: gemm_tiled_kernel<WM, WN, TM, TN, 2, NS, SPL><<<grid, block, 0, stream>>>(a, mt, nt); break;
-    case 3:
-      if constexpr (SPL == 1 || TM == 1) {
-        gemm_tiled_kernel<WM, WN, TM, TN, 3, NS, SPL><<<grid, block, 0, stream>>>(a, mt, nt);
-        break;
-      } else {
-        return hipErrorInvalidValue;
-      }
-    case 4:
-      if constexpr (SPL == 1 || TM == 1) {
-        gemm_tiled_kernel<WM, WN, TM, TN, 4, NS, SPL><<<grid, block, 0, stream>>>(a, mt, nt);
-        break;
-      } else {
-        return hipErrorInvalidValue;
-      }
+    case 0: gemm_tiled_kernel<WM, WN, TM, TN, 0, NS, SPL, GLU><<<grid, block, 0, stream>>>(a, mt, nt); break;
+    case 1: gemm_tiled_kernel<WM, WN, TM, TN, 1, NS, SPL, GLU><<<grid, block, 0, stream>>>(a, mt, nt); break;
+    case 2: gemm_tiled_kernel<WM, WN, TM, TN, 2, NS, SPL, GLU><<<grid, block, 0, stream>>>(a, mt, nt); break;
+    case 3: gemm_tiled_kernel<WM, WN, TM, TN, 3, NS, SPL, GLU><<<grid, block, 0, stream>>>(a, mt, nt); break;
+    case 4: gemm_tiled_kernel<WM, WN, TM, TN, 4, NS, SPL, GLU><<<grid, block, 0, stream>>>(a, mt, nt); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 // SPL = number of lora_act partials a wave sums: 1, or up to
-// kMaxTiledLoraSplits for the shapes where TM * (R/16) * 4 <= 16.
-template <int WM, int WN, int TM, int TN>
+// kMaxTiledLoraSplits.
+template <int WM, int WN, int TM, int TN, bool GLU>
 static hipError_t launch_tiled_cfg(const GemmArgs& a, hipStream_t stream) {
   const int64_t mt = round_up16(a.M) / 16, nt = a.N / 16;
   const int64_t nblk = ((mt + WM * TM - 1) / (WM * TM)) * ((nt + WN * TN - 1) / (WN * TN));
   if (nblk >= ((int64_t)1 << 31)) return hipErrorInvalidValue;   // the kernel's tile math is 32-bit
   dim3 grid((unsigned)nblk), block(64 * WM * WN);
-  if (a.ks == 1) return launch_tiled_spl<WM, WN, TM, TN, 1>(a, mt, nt, grid, block, stream);
-  if constexpr (TM <= 2) return launch_tiled_spl<WM, WN, TM, TN, kMaxTiledLoraSplits>(a, mt, nt, grid, block, stream);
-  return hipErrorInvalidValue;   // pick_tiled never selects this shape with split lora_act
+  if (a.ks == 1) return launch_tiled_spl<WM, WN, TM, TN, 1, GLU>(a, mt, nt, grid, block, stream);
+  return launch_tiled_spl<WM, WN, TM, TN, kMaxTiledLoraSplits, GLU>(a, mt, nt, grid, block, stream);
 }
 
 // Tile shapes for M > 16: a workgroup of WM x WN waves, each wave TM x TN
@@ -1222,6 +1280,8 @@ constexpr TiledCfg kTiledCfgs[] = {
     {2, 2, 1, 2, 4},   //  32 x  64
     {4, 1, 1, 3, 4},   //  64 x  48
     {1, 4, 3, 1, 4},   //  48 x  64
+    {4, 1, 1, 2, 4},   //  64 x  32
+    {4, 1, 1, 4, 4},   //  64 x  64, one row tile per wave
 };
 constexpr int kNumTiledCfgs = (int)(sizeof(kTiledCfgs) / sizeof(kTiledCfgs[0]));
 
@@ -1253,16 +1313,11 @@ static double tiled_cost(const TiledCfg& c, int64_t mt, int64_t nt, int64_t kp) 
   return (double)waves_per_simd * (tiles * per_tile * (double)kp + fixed);
 }
 
-// With split lora_act a wave holds TM * RT * kMaxTiledLoraSplits fragments
-// (4 VGPRs each) while it sums the partials; shapes that would hold more than
-// 16 are not eligible (the launcher builds no such instance).
-static bool tiled_fits(const TiledCfg& c, int R, int ks) {
-  return ks == 1 || c.tm * (R / 16) * kMaxTiledLoraSplits <= 16;
-}
-
 static int pick_tiled(int64_t M, int64_t N, int64_t K, int R, int ks, bool glu) {
   // gated output: a wave's column tiles must hold whole (gate, up) pairs
-  auto ok = [&](const TiledCfg& c) { return tiled_fits(c, R, ks) && (!glu || c.tn % 2 == 0); };
+  (void)R;
+  (void)ks;
+  auto ok = [&](const TiledCfg& c) { return !glu || c.tn % 2 == 0; };
   const int ov = tiled_override();
   if (ov >= 0 && ok(kTiledCfgs[ov])) return ov;
   const int64_t mt = round_up16(M) / 16, nt = N / 16, kp = K / kKPair;
@@ -1308,15 +1363,29 @@ hipError_t launch_gemm(const GemmArgs& a, int variant, hipStream_t stream) {
       return launch_decode(a, stream);
     case kPrefill:
       if (a.ks < 1 || a.ks > kMaxTiledLoraSplits) return hipErrorInvalidValue;   // lora_splits() for M > 16
-      switch (pick_tiled(a.M, a.N, a.K, a.R, a.ks, a.glu != 0)) {
-        case 0: return launch_tiled_cfg<2, 2, 4, 4>(a, stream);
-        case 1: return launch_tiled_cfg<2, 2, 2, 4>(a, stream);
-        case 2: return launch_tiled_cfg<2, 2, 4, 2>(a, stream);
-        case 3: return launch_tiled_cfg<2, 2, 2, 2>(a, stream);
-        case 4: return launch_tiled_cfg<2, 2, 1, 2>(a, stream);
-        case 5: return launch_tiled_cfg<4, 1, 1, 3>(a, stream);
-        case 6: return launch_tiled_cfg<1, 4, 3, 1>(a, stream);
-        default: return hipErrorInvalidValue;   // no tile shape fits (R, ks, gated)
+      if (a.glu) {   // shapes whose waves hold whole (gate, up) tile pairs
+        switch (pick_tiled(a.M, a.N, a.K, a.R, a.ks, true)) {
+          case 0: return launch_tiled_cfg<2, 2, 4, 4, true>(a, stream);
+          case 1: return launch_tiled_cfg<2, 2, 2, 4, true>(a, stream);
+          case 2: return launch_tiled_cfg<2, 2, 4, 2, true>(a, stream);
+          case 3: return launch_tiled_cfg<2, 2, 2, 2, true>(a, stream);
+          case 4: return launch_tiled_cfg<2, 2, 1, 2, true>(a, stream);
+          case 7: return launch_tiled_cfg<4, 1, 1, 2, true>(a, stream);
+          case 8: return launch_tiled_cfg<4, 1, 1, 4, true>(a, stream);
+          default: return hipErrorInvalidValue;
+        }
+      }
+      switch (pick_tiled(a.M, a.N, a.K, a.R, a.ks, false)) {
+        case 0: return launch_tiled_cfg<2, 2, 4, 4, false>(a, stream);
+        case 1: return launch_tiled_cfg<2, 2, 2, 4, false>(a, stream);
+        case 2: return launch_tiled_cfg<2, 2, 4, 2, false>(a, stream);
+        case 3: return launch_tiled_cfg<2, 2, 2, 2, false>(a, stream);
+        case 4: return launch_tiled_cfg<2, 2, 1, 2, false>(a, stream);
+        case 5: return launch_tiled_cfg<4, 1, 1, 3, false>(a, stream);
+        case 6: return launch_tiled_cfg<1, 4, 3, 1, false>(a, stream);
+        case 7: return launch_tiled_cfg<4, 1, 1, 2, false>(a, stream);
+        case 8: return launch_tiled_cfg<4, 1, 1, 4, false>(a, stream);
+        default: return hipErrorInvalidValue;   // no tile shape fits (R, ks)
       }
     default:
       return launch_generic_rt<2, 2, false>(a, 0, mt, 0, nt, nullptr, 0, stream);

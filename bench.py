@@ -234,6 +234,91 @@ def launch_overhead(args, W, torch, M, N, K, R, x, blobs, act, y, sh, quant):
     return 0
 
 
+def graph_avg_ms(torch, fn, n):
+    """Average duration of one fn(i, stream) over a graph of n back-to-back
+    calls, bracketed by two events on the launch stream (3 replays)."""
+    gk = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gk):
+        cs = torch.cuda.current_stream().cuda_stream
+        for i in range(n):
+            fn(i, cs)
+    gk.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s = torch.cuda.current_stream()
+    e0.record(s)
+    for _ in range(3):
+        gk.replay()
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (3 * n)
+
+
+def mlp_gate_up(args, W, torch, np, workloads):
+    """The gated MLP's front half at the workload's shape: gate and up
+    projections (two seeds of the workload's recipe, rank R each) packed as
+    one layer with SiLU(g) * u in the GEMM epilogue (one activation pass +
+    w4a4_linear_glu), against the same work unfused (an activation pass and a
+    GEMM per projection, then torch's silu and mul).  Prints one line."""
+    g = workloads.generate(args.workload, M=args.m)
+    u = workloads.generate(args.workload, M=args.m, seed=workloads.WORKLOADS[args.workload].seed + 7)
+    M, K, N, R = g["M"], g["K"], g["N"], g["R"]
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    x = dev(g["x"])
+    layer = W.GatedMLPUp(N, K, dev(g["w"]), dev(u["w"]), dev(g["lora_down"]), dev(g["lora_up"]),
+                         dev(u["lora_down"]), dev(u["lora_up"]), dev(g["col_scale"]), dev(g["bias"]),
+                         dev(u["col_scale"]), dev(u["bias"]))
+    act = W.alloc_act_blob(M, K, 2 * R)
+    h = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    sep = []
+    for c in (g, u):
+        wb = W.alloc_weight_blob(N, K, R)
+        W.w4a4_pack_weights(N, K, R, wb, w_fp16=dev(c["w"]), lora_down=dev(c["lora_down"]),
+                            lora_up=dev(c["lora_up"]), col_scale=dev(c["col_scale"]), bias=dev(c["bias"]))
+        sep.append((wb, W.alloc_act_blob(M, K, R), torch.empty((M, N), dtype=torch.float16, device="cuda")))
+    h_sep = torch.empty_like(h)
+
+    def fused_quant(i, cs):
+        W.w4a4_quantize_act(M, K, 2 * R, x, layer.wblob, act, stream=cs)
+
+    def fused_gemm(i, cs):
+        W.w4a4_linear_glu(M, 2 * N, K, 2 * R, act, layer.wblob, h, stream=cs)
+
+    def fused(i, cs):
+        fused_quant(i, cs)
+        fused_gemm(i, cs)
+
+    def sep_gemms(i, cs):
+        for wb, a, y in sep:
+            W.w4a4_linear(M, N, K, R, a, wb, y, stream=cs)
+
+    def unfused(i, cs):
+        for wb, a, y in sep:
+            W.w4a4_quantize_act(M, K, R, x, wb, a, stream=cs)
+            W.w4a4_linear(M, N, K, R, a, wb, y, stream=cs)
+        torch.mul(torch.nn.functional.silu(sep[0][2]), sep[1][2], out=h_sep)
+
+    fused(0, torch.cuda.current_stream().cuda_stream)
+    unfused(0, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    n = 50
+    t = {k: graph_avg_ms(torch, f, n) * 1e3 for k, f in
+         [("fused_step", fused), ("fused_quantize", fused_quant), ("fused_glu_gemm", fused_gemm),
+          ("unfused_step", unfused), ("unfused_two_gemms", sep_gemms)]}
+    ops = 2 * algorithmic_counts(M, N, K, R)["layer_ops"]
+    print(json.dumps({"metric": "gated MLP front half (gate + up + SiLU*mul), TOPS at 1 GPU", "unit": "TOPS",
+                      "value": round(ops / (t["fused_step"] * 1e-6) / 1e12, 3),
+                      "config": {"workload": f"{args.workload} gate+up: M={M} K={K} N={N} per projection, "
+                                             f"R={R} each, group 64", "M": M, "K": K, "N": N, "R": R,
+                                 "variant": W.w4a4_query_variant(M, 2 * N, K, 2 * R)},
+                      **{k + "_us": round(v, 3) for k, v in t.items()},
+                      "fused_over_unfused": round(t["unfused_step"] / t["fused_step"], 3),
+                      "max_abs_diff_vs_unfused_over_rms": round(float((h.float() - h_sep.float()).abs().max() /
+                                                                      h_sep.float().pow(2).mean().sqrt()), 6)}),
+          flush=True)
+    return 0
+
+
 def algorithmic_counts(M, N, K, R):
     """Ops and bytes the method must do / move (not those of an fp16 GEMM).
 
@@ -298,6 +383,9 @@ def main(argv=None):
     ap.add_argument("--rmsnorm", action="store_true",
                     help="quantize through the fused RMSNorm + quantize pass (synthetic gamma, eps 1e-6); "
                          "also times torch's rms_norm followed by the plain quantizer")
+    ap.add_argument("--mlp", action="store_true",
+                    help="time the gated MLP front half (gate + up fused with SiLU*mul in the epilogue) "
+                         "at --workload's shape against the unfused path, and print that line")
     ap.add_argument("--ingest-sq", metavar="DIR",
                     help="record a rocprofv3 SQ instruction-mix counter run (DIR) for --workload")
     args = ap.parse_args(argv)
@@ -326,6 +414,8 @@ def main(argv=None):
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": COPY_BYTES, "copies": 10}), flush=True)
         return 0
+    if args.mlp:
+        return mlp_gate_up(args, W, torch, np, workloads)
     if args.rotate is None:
         args.rotate = 12 if args.workload == "decode" else 1
     case = workloads.generate(args.workload, M=args.m)
@@ -416,26 +506,10 @@ def main(argv=None):
     # Kernel-only figures: a graph of `nk_g` back-to-back launches of one
     # kernel, bracketed by two events on the launch stream; the average
     # launch duration is (elapsed) / nk_g.
-    def graph_avg_ms(fn, n):
-        gk = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gk):
-            cs2 = torch.cuda.current_stream().cuda_stream
-            for i in range(n):
-                fn(i, cs2)
-        gk.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s2 = torch.cuda.current_stream()
-        e0.record(s2)
-        for _ in range(3):
-            gk.replay()
-        e1.record(s2)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / (3 * n)
-
     nk_g = 50
-    l_ms = graph_avg_ms(lambda i, cs2: W.w4a4_linear(M, N, K, R, act, blobs[i % len(blobs)], y, stream=cs2), nk_g)
-    q_ms = graph_avg_ms(lambda i, cs2: quant(blobs[i % len(blobs)], cs2), nk_g)
+    l_ms = graph_avg_ms(torch, lambda i, cs2: W.w4a4_linear(M, N, K, R, act, blobs[i % len(blobs)], y, stream=cs2),
+                        nk_g)
+    q_ms = graph_avg_ms(torch, lambda i, cs2: quant(blobs[i % len(blobs)], cs2), nk_g)
     unfused = None
     if args.rmsnorm:
         # the unfused alternative: torch's rms_norm (fp16 out), then the plain quantizer
@@ -448,8 +522,8 @@ def main(argv=None):
             norm_only(i, cs2)
             W.w4a4_quantize_act(M, K, R, xn, blobs[i % len(blobs)], act, stream=cs2)
 
-        unfused = {"torch_rms_norm_us": round(graph_avg_ms(norm_only, nk_g) * 1e3, 3),
-                   "torch_rms_norm_then_quantize_us": round(graph_avg_ms(norm_then_quant, nk_g) * 1e3, 3)}
+        unfused = {"torch_rms_norm_us": round(graph_avg_ms(torch, norm_only, nk_g) * 1e3, 3),
+                   "torch_rms_norm_then_quantize_us": round(graph_avg_ms(torch, norm_then_quant, nk_g) * 1e3, 3)}
 
     c = algorithmic_counts(M, N, K, R)
     value = c["layer_ops"] / (ms_per_step * 1e-3) / 1e12

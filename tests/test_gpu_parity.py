@@ -252,15 +252,17 @@ def test_ragged_and_rank_edges(M, K, N, R):
                                      (4, 4864, 48, 16), (4, 384, 16, 0), (8, 1664, 32, 32),
                                      (13, 4864, 48, 64), (6, 1664, 8192, 48), (11, 384, 8192, 0),
                                      (16, 4864, 8192, 16), (9, 1664, 8192, 64), (1, 1664, 8192, 48),
-                                     (2, 384, 8192, 0), (3, 4864, 8192, 64), (4, 1664, 8192, 16)])
+                                     (2, 384, 8192, 0), (3, 4864, 8192, 64), (4, 1664, 8192, 16),
+                                     (4, 4864, 8192, 64)])
 def test_small_m_decode_shapes(M, K, N, R):
     """M <= 16 kernels over uneven per-wave k-pair ranges (a wave with no
     k-pairs, ranges that are not a multiple of the batch), every rank, and
     groups whose scales differ by 16x between odd and even groups, so a
     group / scale mispairing cannot hide inside the tolerance.  N = 8192
     (512 column tiles) takes the two-column-tiles-per-workgroup paths: the
-    dot kernel (M <= 4, every rank) and the MFMA decode kernel (M >= 5,
-    R <= 48; R = 64 keeps one tile)."""
+    dot kernel (M <= 3, every rank) and the MFMA decode kernel (M >= 4,
+    R <= 48; R = 64 keeps one tile); at N = 8192 M = 4 runs the MFMA decode
+    kernel, at narrower N the dot kernel."""
     case = workloads.random_case(M, K, N, R, seed=2000 + M + K + R)
     x = case["x"].astype(np.float64)
     x[:, (np.arange(K) // 64) % 2 == 1] *= 16.0
@@ -279,17 +281,20 @@ def test_small_m_decode_shapes(M, K, N, R):
     assert np.all(np.isnan(run.host_y()[M:].astype(np.float64)))
 
 
-@pytest.mark.parametrize("cfg,K", [(c, 512) for c in range(9)] + [(c, 2048) for c in range(9)])
-def test_every_tile_shape(cfg, K, monkeypatch):
+@pytest.mark.parametrize("cfg,K,R", [(c, 512, 32) for c in range(9)] + [(c, 2048, 32) for c in range(9)] +
+                         [(c, 2048, 64) for c in range(9)])
+def test_every_tile_shape(cfg, K, R, monkeypatch):
     """Each M > 16 tile shape (forced) on a shape with ragged row and column
     edges for all of them: M = 130 (9 row tiles), N = 208 (13 column tiles);
-    K = 512 gives one lora_act partial, K = 2048 two (shapes that cannot sum
-    partials fall back to the model's pick)."""
-    M, N, R = 130, 208, 32
+    K = 512 gives one lora_act partial, K = 2048 two: shapes whose waves
+    cannot hold every partial through the K loop (row tiles x rank blocks x
+    4 > 16, e.g. all of them at rank 64 but the one-row-tile ones) load and
+    sum them in the epilogue instead."""
+    M, N = 130, 208
     _, _, ks = W.w4a4_act_layout(M, K, R, with_splits=True)
     assert ks == (1 if K == 512 else 2)
     monkeypatch.setenv("W4A4_TILED_CFG", str(cfg))
-    case = workloads.random_case(M, K, N, R, seed=3000 + cfg + K)
+    case = workloads.random_case(M, K, N, R, seed=3000 + cfg + K + R)
     _say(f"[tile shape {cfg}] M={M} K={K} N={N} R={R} partials={ks}")
     run = GpuRun(case)
     ref = O.linear(case["x"], case["lora_down"], case["lora_up"], case["col_scale"], case["bias"], w16=case["w"])

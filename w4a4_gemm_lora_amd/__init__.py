@@ -257,6 +257,10 @@ class GatedMLPUp:
                  lora_down_up=None, lora_up_up=None, a_gate=None, b_gate=None, a_up=None, b_up=None):
         import torch
         self.N, self.K = int(N), int(K)
+        if self.N % 16 or self.N <= 0:
+            raise ValueError("each projection needs a positive multiple of 16 columns")
+        if (lora_down_gate is None) != (lora_up_gate is None) or (lora_down_up is None) != (lora_up_up is None):
+            raise ValueError("give both LoRA factors of a projection, or neither")
         dev = w_gate.device
         rg = 0 if lora_down_gate is None else lora_down_gate.shape[1]
         ru = 0 if lora_down_up is None else lora_down_up.shape[1]

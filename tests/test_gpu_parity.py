@@ -228,8 +228,12 @@ def test_prefill_parity_sampled():
 
 
 @pytest.mark.parametrize("M,K,N,R", [(1, 128, 16, 16), (17, 128, 48, 0), (33, 256, 64, 64),
-                                     (5, 384, 32, 48), (130, 512, 80, 32)])
+                                     (5, 384, 32, 48), (130, 512, 80, 32), (40, 8192, 48, 32),
+                                     (40, 8192, 48, 64), (3, 16384, 32, 16)])
 def test_ragged_and_rank_edges(M, K, N, R):
+    """Ragged M, every rank, and the quantizer's wave counts: K = 8192 at
+    M = 40 splits K four ways with 16 k-pairs per workgroup (16 waves at
+    rank 32, 8 at rank 64), K = 16384 at M = 3 eight ways (16 waves)."""
     case = workloads.random_case(M, K, N, R, seed=1000 + M + K + R)
     _say(f"[edge] M={M} K={K} N={N} R={R}")
     run = GpuRun(case)

@@ -293,8 +293,9 @@ static hipError_t launch_quantize_nwsel(const uint16_t* src, int64_t ld, int64_t
                                         uint16_t* scales, float* lora_part, const uint16_t* gamma,
                                         double eps, int64_t wgs, int64_t kp_per_wg, hipStream_t stream) {
   // waves per workgroup: as many as the k-pairs of a workgroup allow (<= 16),
-  // but 8 when there are enough row tiles to fill the GPU anyway
-  if (kp_per_wg >= 16 && wgs < 256)
+  // but 8 when there are enough row tiles to fill the GPU anyway, and at
+  // ranks above 32 (16 waves leave 128 VGPRs, which rank 48 and 64 exceed)
+  if (kp_per_wg >= 16 && wgs < 256 && R <= 32)
     return launch_quantize_nw<16, NORM>(src, ld, rows, rows_padded, K, R, ks, ldown_packed, codes, scales, lora_part, gamma, eps, stream);
   if (kp_per_wg >= 8)
     return launch_quantize_nw<8, NORM>(src, ld, rows, rows_padded, K, R, ks, ldown_packed, codes, scales, lora_part, gamma, eps, stream);

@@ -214,42 +214,36 @@ static int make_gemm_args(int64_t M, int64_t N, int64_t K, int32_t R, const void
   return W4A4_OK;
 }
 
-int w4a4_linear(int64_t M, int64_t N, int64_t K, int32_t R, const void* act,
-                const void* wblob, uint16_t* y, int64_t ldy, void* stream) {
+// y holds N columns, or N/2 for the gated output (one per (gate, up) pair).
+static int linear_impl(int64_t M, int64_t N, int64_t K, int32_t R, const void* act,
+                       const void* wblob, uint16_t* y, int64_t ldy, void* stream, bool glu) {
   int st = check_nkr(N, K, R);
   if (st) return st;
+  if (glu && N % 32 != 0) return W4A4_ERR_SHAPE;   // whole (gate, up) tile pairs
   if ((st = check_m(M))) return st;
   if (M == 0) return W4A4_OK;
   if (!y) return W4A4_ERR_NULL;
-  if (ldy < N) return W4A4_ERR_SHAPE;
+  const int64_t ycols = glu ? N / 2 : N;
+  if (ldy < ycols) return W4A4_ERR_SHAPE;
   if (ldy % 8 != 0 || !aligned(y, 16)) return W4A4_ERR_ALIGN;
   GemmArgs a;
-  if ((st = make_gemm_args(M, N, K, R, act, wblob, y, ldy, &a))) return st;
+  if ((st = make_gemm_args(M, N, K, R, act, wblob, y, ldy, &a, ycols))) return st;
+  a.glu = glu ? 1 : 0;
   const int v = choose_variant(M, N, K, R);
   if (log_enabled())
-    std::fprintf(stderr, "w4a4_linear M=%lld N=%lld K=%lld R=%d -> %s\n", (long long)M,
-                 (long long)N, (long long)K, R, variant_name(v));
+    std::fprintf(stderr, "%s M=%lld N=%lld K=%lld R=%d -> %s\n", glu ? "w4a4_linear_glu" : "w4a4_linear",
+                 (long long)M, (long long)N, (long long)K, R, variant_name(v));
   return hip_status(launch_gemm(a, v, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int w4a4_linear(int64_t M, int64_t N, int64_t K, int32_t R, const void* act,
+                const void* wblob, uint16_t* y, int64_t ldy, void* stream) {
+  return linear_impl(M, N, K, R, act, wblob, y, ldy, stream, false);
 }
 
 int w4a4_linear_glu(int64_t M, int64_t N, int64_t K, int32_t R, const void* act,
                     const void* wblob, uint16_t* y, int64_t ldy, void* stream) {
-  int st = check_nkr(N, K, R);
-  if (st) return st;
-  if (N % 32 != 0) return W4A4_ERR_SHAPE;   // whole (gate, up) tile pairs
-  if ((st = check_m(M))) return st;
-  if (M == 0) return W4A4_OK;
-  if (!y) return W4A4_ERR_NULL;
-  if (ldy < N / 2) return W4A4_ERR_SHAPE;
-  if (ldy % 8 != 0 || !aligned(y, 16)) return W4A4_ERR_ALIGN;
-  GemmArgs a;
-  if ((st = make_gemm_args(M, N, K, R, act, wblob, y, ldy, &a, N / 2))) return st;
-  a.glu = 1;
-  const int v = choose_variant(M, N, K, R);
-  if (log_enabled())
-    std::fprintf(stderr, "w4a4_linear_glu M=%lld N=%lld K=%lld R=%d -> %s\n", (long long)M,
-                 (long long)N, (long long)K, R, variant_name(v));
-  return hip_status(launch_gemm(a, v, reinterpret_cast<hipStream_t>(stream)));
+  return linear_impl(M, N, K, R, act, wblob, y, ldy, stream, true);
 }
 
 int w4a4_query_variant(int64_t M, int64_t N, int64_t K, int32_t R) {

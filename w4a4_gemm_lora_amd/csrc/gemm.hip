@@ -16,6 +16,13 @@
 // parts, accumulating straight into the main accumulator; the affine and the
 // fp16 rounding follow in registers.
 //
+// Gated variant (GLU template flag): for the MLP's gate and up projections
+// packed as one layer with their rows interleaved by 16-row tiles (voice-
+// clone article, section 3.1: the Qwen3 MLP computes SiLU(gate) * up), a
+// wave or workgroup always holds a (gate, up) tile pair, rounds both to fp16
+// as the two layers would store them, and writes fp16(SiLU(g) * u) to one
+// output tile (glu_bits).
+//
 // Cost model measured on MI355X: one v_mfma_i32_16x16x64_i8 occupies a SIMD
 // for ~16.5 cycles and a wave64 fp32 VALU op for ~2.6-2.9 cycles, and the two
 // barely overlap, so the per-group epilogue (convert, scale product, fma on

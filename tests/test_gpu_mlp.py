@@ -96,16 +96,18 @@ def test_glu_strided_output(M):
     assert np.all(np.isnan(h[:, N:].astype(np.float64)))
 
 
-@pytest.mark.parametrize("cfg", range(9))
-def test_glu_every_tile_shape(cfg, monkeypatch):
-    """Each M > 16 tile shape forced in turn (shapes whose waves hold an odd
-    number of column tiles cannot pair gate with up and fall back to the
-    model's pick); 13 row tiles and 14 fused column tiles leave ragged
-    edges for every shape."""
+@pytest.mark.parametrize("cfg,lean", [(c, "0") for c in range(9)] + [(c, "1") for c in (0, 1, 2, 3, 8)])
+def test_glu_every_tile_shape(cfg, lean, monkeypatch):
+    """Each M > 16 tile shape forced in turn, in the 4-stage and (where it
+    exists) the lean variant (shapes whose waves hold an odd number of
+    column tiles cannot pair gate with up and fall back to the model's
+    pick); 13 row tiles and 14 fused column tiles leave ragged edges for
+    every shape."""
     M, K, N, R = 200, 1024, 112, 16
     monkeypatch.setenv("W4A4_TILED_CFG", str(cfg))
+    monkeypatch.setenv("W4A4_TILED_LEAN", lean)
     x, g, u = _cases(M, K, N, R, R, seed=5300 + cfg)
-    _say(f"[glu tile shape {cfg}] M={M} K={K} N={N}")
+    _say(f"[glu tile shape {cfg} lean={lean}] M={M} K={K} N={N}")
     h = _run_glu(x, g, u, R, R)
     _, _, ref = O.mlp_gate_up(x, _half(g, R), _half(u, R))
     _check_y(h[:M, :N], ref, f"glu tile shape {cfg}")

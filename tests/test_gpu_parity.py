@@ -306,6 +306,23 @@ def test_every_tile_shape(cfg, K, R, monkeypatch):
     assert np.all(np.isnan(run.host_y()[M:].astype(np.float64)))
 
 
+@pytest.mark.parametrize("cfg,K,R", [(c, K, R) for c in (0, 1, 2, 3, 5, 8) for K, R in ((512, 32), (2048, 64))])
+def test_every_lean_tile_shape(cfg, K, R, monkeypatch):
+    """The lean variant (3 workgroups per CU: 3-deep LDS ring, epilogue
+    operands and lora_act partials loaded after the K loop, tile-by-tile
+    loop body) of each tile shape that has one, forced, on the ragged shape
+    of the test above, with one and with two lora_act partials."""
+    M, N = 130, 208
+    monkeypatch.setenv("W4A4_TILED_CFG", str(cfg))
+    monkeypatch.setenv("W4A4_TILED_LEAN", "1")
+    case = workloads.random_case(M, K, N, R, seed=3500 + cfg + K + R)
+    _say(f"[lean tile shape {cfg}] M={M} K={K} N={N} R={R}")
+    run = GpuRun(case)
+    ref = O.linear(case["x"], case["lora_down"], case["lora_up"], case["col_scale"], case["bias"], w16=case["w"])
+    _check_y(run.host_y()[:M, :N], ref["y"], f"lean tile shape {cfg}")
+    assert np.all(np.isnan(run.host_y()[M:].astype(np.float64)))
+
+
 def test_strided_x_and_y():
     M, K, N, R = 40, 256, 64, 32
     case = workloads.random_case(M, K, N, R, seed=7)

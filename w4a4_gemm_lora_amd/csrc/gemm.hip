@@ -856,9 +856,9 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_dot_kernel(GemmArgs g) {
 // ---------------------------------------------------------------------------
 constexpr int kTileGroupRows = 8;
 
-template <int WM, int WN, int TM, int TN, int RT, int NS, int SPL, bool GLU>
-__global__ __launch_bounds__(WM * WN * 64, 2) void gemm_tiled_kernel(GemmArgs g, int64_t mt_count,
-                                                                 int64_t nt_count) {
+template <int WM, int WN, int TM, int TN, int RT, int NS, int SPL, bool GLU, int OCC>
+__global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_tiled_kernel(GemmArgs g, int64_t mt_count,
+                                                                   int64_t nt_count) {
   constexpr int NW = WM * WN;
   constexpr int BMT = WM * TM, BNT = WN * TN;            // tiles per workgroup
   constexpr int CHUNKS = BMT + BNT;                      // 1 KB operand tiles per stage
@@ -953,29 +953,38 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void gemm_tiled_kernel(GemmArgs g,
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
+  // OCC = workgroups per CU the instance is built for.  OCC = 3 (the lean
+  // variant, 3 waves per SIMD, where the VALU work of the per-group epilogue
+  // issues ~1.5x faster than at 2) keeps the loop's registers down: the
+  // epilogue operands below are loaded after the loop, lora_act partials too,
+  // the stage ring is 3 deep, and the loop body runs tile by tile.
+  constexpr bool kLean = OCC >= 3;
   // Epilogue operands, loaded first so that they arrive during the main loop
   // and the exact vmcnt waits below count only stage copies after them:
-  // lora_act fragments of the wave's row tiles (fp32; split into fp16 hi +
-  // lo after the loop), L_up fragments and the affine of its columns.  Tiles
-  // past the edge read the last valid tile (never stored).
+  // L_up fragments and the affine of its columns (lora_act fragments of the
+  // wave's row tiles follow).  Tiles past the edge read the last valid tile
+  // (never stored).
   constexpr int RTL = RT > 0 ? RT : 1;
   v4h lu_f[TN][RTL];
   float af[TN], bf[TN];
+  auto load_epilogue_operands = [&]() {
 #pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int64_t nt = tile_index(BMT + wn * TN + j);
-    af[j] = g.ca[nt * 16 + (lane & 15)];
-    bf[j] = g.cb[nt * 16 + (lane & 15)];
+    for (int j = 0; j < TN; ++j) {
+      const int64_t nt = tile_index(BMT + wn * TN + j);
+      af[j] = g.ca[nt * 16 + (lane & 15)];
+      bf[j] = g.cb[nt * 16 + (lane & 15)];
 #pragma unroll
-    for (int t = 0; t < RT; ++t)
-      lu_f[j][t] = *reinterpret_cast<const v4h*>(g.lup + (((size_t)nt * RT + t) * 64 + lane) * 4);
-  }
+      for (int t = 0; t < RT; ++t)
+        lu_f[j][t] = *reinterpret_cast<const v4h*>(g.lup + (((size_t)nt * RT + t) * 64 + lane) * 4);
+    }
+  };
+  if constexpr (!kLean) load_epilogue_operands();
   // lora_act comes as g.ks <= SPL K-range partials; all of them are loaded
   // here and summed in order in the epilogue (no wait before the K loop) --
   // unless they would take more than 64 registers through the loop: then the
   // epilogue loads them rank block by rank block (one more memory round trip
   // per workgroup).
-  constexpr bool kLateLora = TM * RT * SPL > 16;
+  constexpr bool kLateLora = kLean || TM * RT * SPL > 16;
   v4f la_p[kLateLora ? 1 : SPL][TM][RTL];
   if constexpr (!kLateLora && RT > 0) {
     const size_t part = (size_t)round_up16(g.M) * g.R;   // floats per partial
@@ -1048,27 +1057,42 @@ __global__ __launch_bounds__(WM * WN * 64, 2) void gemm_tiled_kernel(GemmArgs g,
         const v2u r2 = *reinterpret_cast<const v2u*>(&lds[st][BMT + wn * TN + j][lane * 16 + h * 8]);
         Be[j] = expand_group(r2[0], r2[1]);
       }
-      // Per row tile: its TN scale MFMAs, then its TN integer MFMAs, then
-      // the conversions and FMAs -- grouping MFMAs of one kind avoids the
-      // pipeline's switch penalty between the two kinds, and the FMAs of a
-      // tile no longer wait right behind the MFMA that feeds them.
+      if constexpr (kLean) {
+        // tile by tile: fewer registers live
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        v4f S[TN];
-        v4i P[TN];
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) S[j] = scale_tile(sxw[i], sww[j], h);
+          for (int j = 0; j < TN; ++j) {
+            const v4f S = scale_tile(sxw[i], sww[j], h);
+            const v4i P = mfma_i8_16x16x64(Ae[i], Be[j], v4i{0, 0, 0, 0});
 #pragma unroll
-        for (int j = 0; j < TN; ++j) P[j] = mfma_i8_16x16x64(Ae[i], Be[j], v4i{0, 0, 0, 0});
+            for (int ii = 0; ii < 4; ++ii) acc[i][j][ii] = fmaf((float)P[ii], S[ii], acc[i][j][ii]);
+          }
+      } else {
+        // Per row tile: its TN scale MFMAs, then its TN integer MFMAs, then
+        // the conversions and FMAs -- grouping MFMAs of one kind avoids the
+        // pipeline's switch penalty between the two kinds, and the FMAs of a
+        // tile no longer wait right behind the MFMA that feeds them.
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+        for (int i = 0; i < TM; ++i) {
+          v4f S[TN];
+          v4i P[TN];
 #pragma unroll
-          for (int ii = 0; ii < 4; ++ii) acc[i][j][ii] = fmaf((float)P[j][ii], S[j][ii], acc[i][j][ii]);
+          for (int j = 0; j < TN; ++j) S[j] = scale_tile(sxw[i], sww[j], h);
+#pragma unroll
+          for (int j = 0; j < TN; ++j) P[j] = mfma_i8_16x16x64(Ae[i], Be[j], v4i{0, 0, 0, 0});
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) acc[i][j][ii] = fmaf((float)P[j][ii], S[j][ii], acc[i][j][ii]);
+        }
       }
     }
     st = st + 1 == NS ? 0 : st + 1;
     st_next = st_next + 1 == NS ? 0 : st_next + 1;
   }
+
+  if constexpr (kLean) load_epilogue_operands();
 
   // acc holds 256 * main (the int8 operands carry 16 q each)
 #pragma unroll
@@ -1252,18 +1276,18 @@ static hipError_t launch_decode(const GemmArgs& a, hipStream_t stream) {
   }
 }
 
-constexpr int kTiledStages = 4;
-
-template <int WM, int WN, int TM, int TN, int SPL, bool GLU>
+// LDS stage ring depth: 4, or 3 for the lean (3 workgroups per CU) variant,
+// whose 128 x 128 tile shape then fits three 51 KB rings in a CU's 160 KB.
+template <int WM, int WN, int TM, int TN, int SPL, bool GLU, int OCC>
 static hipError_t launch_tiled_spl(const GemmArgs& a, int64_t mt, int64_t nt, dim3 grid, dim3 block,
                                    hipStream_t stream) {
-  constexpr int NS = kTiledStages;
+  constexpr int NS = OCC >= 3 ? 3 : 4;
   switch (a.R / 16) {
-    case 0: gemm_tiled_kernel<WM, WN, TM, TN, 0, NS, SPL, GLU><<<grid, block, 0, stream>>>(a, mt, nt); break;
-    case 1: gemm_tiled_kernel<WM, WN, TM, TN, 1, NS, SPL, GLU><<<grid, block, 0, stream>>>(a, mt, nt); break;
-    case 2: gemm_tiled_kernel<WM, WN, TM, TN, 2, NS, SPL, GLU><<<grid, block, 0, stream>>>(a, mt, nt); break;
-    case 3: gemm_tiled_kernel<WM, WN, TM, TN, 3, NS, SPL, GLU><<<grid, block, 0, stream>>>(a, mt, nt); break;
-    case 4: gemm_tiled_kernel<WM, WN, TM, TN, 4, NS, SPL, GLU><<<grid, block, 0, stream>>>(a, mt, nt); break;
+    case 0: gemm_tiled_kernel<WM, WN, TM, TN, 0, NS, SPL, GLU, OCC><<<grid, block, 0, stream>>>(a, mt, nt); break;
+    case 1: gemm_tiled_kernel<WM, WN, TM, TN, 1, NS, SPL, GLU, OCC><<<grid, block, 0, stream>>>(a, mt, nt); break;
+    case 2: gemm_tiled_kernel<WM, WN, TM, TN, 2, NS, SPL, GLU, OCC><<<grid, block, 0, stream>>>(a, mt, nt); break;
+    case 3: gemm_tiled_kernel<WM, WN, TM, TN, 3, NS, SPL, GLU, OCC><<<grid, block, 0, stream>>>(a, mt, nt); break;
+    case 4: gemm_tiled_kernel<WM, WN, TM, TN, 4, NS, SPL, GLU, OCC><<<grid, block, 0, stream>>>(a, mt, nt); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1271,14 +1295,14 @@ static hipError_t launch_tiled_spl(const GemmArgs& a, int64_t mt, int64_t nt, di
 
 // SPL = number of lora_act partials a wave sums: 1, or up to
 // kMaxTiledLoraSplits.
-template <int WM, int WN, int TM, int TN, bool GLU>
+template <int WM, int WN, int TM, int TN, bool GLU, int OCC>
 static hipError_t launch_tiled_cfg(const GemmArgs& a, hipStream_t stream) {
   const int64_t mt = round_up16(a.M) / 16, nt = a.N / 16;
   const int64_t nblk = ((mt + WM * TM - 1) / (WM * TM)) * ((nt + WN * TN - 1) / (WN * TN));
   if (nblk >= ((int64_t)1 << 31)) return hipErrorInvalidValue;   // the kernel's tile math is 32-bit
   dim3 grid((unsigned)nblk), block(64 * WM * WN);
-  if (a.ks == 1) return launch_tiled_spl<WM, WN, TM, TN, 1, GLU>(a, mt, nt, grid, block, stream);
-  return launch_tiled_spl<WM, WN, TM, TN, kMaxTiledLoraSplits, GLU>(a, mt, nt, grid, block, stream);
+  if (a.ks == 1) return launch_tiled_spl<WM, WN, TM, TN, 1, GLU, OCC>(a, mt, nt, grid, block, stream);
+  return launch_tiled_spl<WM, WN, TM, TN, kMaxTiledLoraSplits, GLU, OCC>(a, mt, nt, grid, block, stream);
 }
 
 // Tile shapes for M > 16: a workgroup of WM x WN waves, each wave TM x TN
@@ -1349,6 +1373,60 @@ static int pick_tiled(int64_t M, int64_t N, int64_t K, int R, int ks, bool glu) 
   return best;
 }
 
+// The lean variant (3 workgroups per CU, epilogue operands loaded after the
+// K loop) wins once every SIMD has enough tile-k-pairs of work to amortize
+// the extra memory round trip at its end: over a grid of prefill shapes
+// (M 300..8192, N x K from 1024 x 3072 to 14336 x 4096) the rule "at least
+// 150 16x16x128 tile-k-pairs per SIMD" came within 0.2% of the per-shape
+// better of the two (M=8192 K=N=4096: 241 -> 224 us; M=700 N=14336 K=4096:
+// 106 -> 86 us; the M=700 MLP shapes keep the 4-stage variant).  Built for
+// the shapes that carry large launches.
+// W4A4_TILED_LEAN=0 / 1 forces the choice where the shape has both (tuning
+// and test aid, read at every launch like W4A4_TILED_CFG).
+constexpr bool kLeanCfg[kNumTiledCfgs] = {true, true, true, true, false, true, false, false, true};
+static bool tiled_lean(int cfg, int64_t M, int64_t N, int64_t K) {
+  if (cfg < 0 || cfg >= kNumTiledCfgs || !kLeanCfg[cfg]) return false;
+  const char* e = std::getenv("W4A4_TILED_LEAN");
+  if (e && (e[0] == '0' || e[0] == '1')) return e[0] == '1';
+  const double tkp = (double)(round_up16(M) / 16) * (double)(N / 16) * (double)(K / kKPair);
+  return tkp >= 150.0 * 1024;
+}
+
+template <bool GLU>
+static hipError_t launch_tiled_pick(const GemmArgs& a, int cfg, bool lean, hipStream_t stream) {
+  if (lean) {
+    switch (cfg) {
+      case 0: return launch_tiled_cfg<2, 2, 4, 4, GLU, 3>(a, stream);
+      case 1: return launch_tiled_cfg<2, 2, 2, 4, GLU, 3>(a, stream);
+      case 2: return launch_tiled_cfg<2, 2, 4, 2, GLU, 3>(a, stream);
+      case 3: return launch_tiled_cfg<2, 2, 2, 2, GLU, 3>(a, stream);
+      case 5:
+        if constexpr (!GLU) return launch_tiled_cfg<4, 1, 1, 3, GLU, 3>(a, stream);
+        break;
+      case 8: return launch_tiled_cfg<4, 1, 1, 4, GLU, 3>(a, stream);
+      default: break;
+    }
+    return hipErrorInvalidValue;
+  }
+  switch (cfg) {
+    case 0: return launch_tiled_cfg<2, 2, 4, 4, GLU, 2>(a, stream);
+    case 1: return launch_tiled_cfg<2, 2, 2, 4, GLU, 2>(a, stream);
+    case 2: return launch_tiled_cfg<2, 2, 4, 2, GLU, 2>(a, stream);
+    case 3: return launch_tiled_cfg<2, 2, 2, 2, GLU, 2>(a, stream);
+    case 4: return launch_tiled_cfg<2, 2, 1, 2, GLU, 2>(a, stream);
+    case 5:
+      if constexpr (!GLU) return launch_tiled_cfg<4, 1, 1, 3, GLU, 2>(a, stream);
+      break;
+    case 6:
+      if constexpr (!GLU) return launch_tiled_cfg<1, 4, 3, 1, GLU, 2>(a, stream);
+      break;
+    case 7: return launch_tiled_cfg<4, 1, 1, 2, GLU, 2>(a, stream);
+    case 8: return launch_tiled_cfg<4, 1, 1, 4, GLU, 2>(a, stream);
+    default: break;
+  }
+  return hipErrorInvalidValue;   // no tile shape fits, or one that cannot pair (gate, up) tiles
+}
+
 template <int TM, int TN, bool PSUM>
 static hipError_t launch_generic_rt(const GemmArgs& a, int64_t mt_base, int64_t mt_end,
                                     int64_t nt_base, int64_t nt_end, int32_t* psum,
@@ -1378,29 +1456,10 @@ hipError_t launch_gemm(const GemmArgs& a, int variant, hipStream_t stream) {
       return launch_decode(a, stream);
     case kPrefill:
       if (a.ks < 1 || a.ks > kMaxTiledLoraSplits) return hipErrorInvalidValue;   // lora_splits() for M > 16
-      if (a.glu) {   // shapes whose waves hold whole (gate, up) tile pairs
-        switch (pick_tiled(a.M, a.N, a.K, a.R, a.ks, true)) {
-          case 0: return launch_tiled_cfg<2, 2, 4, 4, true>(a, stream);
-          case 1: return launch_tiled_cfg<2, 2, 2, 4, true>(a, stream);
-          case 2: return launch_tiled_cfg<2, 2, 4, 2, true>(a, stream);
-          case 3: return launch_tiled_cfg<2, 2, 2, 2, true>(a, stream);
-          case 4: return launch_tiled_cfg<2, 2, 1, 2, true>(a, stream);
-          case 7: return launch_tiled_cfg<4, 1, 1, 2, true>(a, stream);
-          case 8: return launch_tiled_cfg<4, 1, 1, 4, true>(a, stream);
-          default: return hipErrorInvalidValue;
-        }
-      }
-      switch (pick_tiled(a.M, a.N, a.K, a.R, a.ks, false)) {
-        case 0: return launch_tiled_cfg<2, 2, 4, 4, false>(a, stream);
-        case 1: return launch_tiled_cfg<2, 2, 2, 4, false>(a, stream);
-        case 2: return launch_tiled_cfg<2, 2, 4, 2, false>(a, stream);
-        case 3: return launch_tiled_cfg<2, 2, 2, 2, false>(a, stream);
-        case 4: return launch_tiled_cfg<2, 2, 1, 2, false>(a, stream);
-        case 5: return launch_tiled_cfg<4, 1, 1, 3, false>(a, stream);
-        case 6: return launch_tiled_cfg<1, 4, 3, 1, false>(a, stream);
-        case 7: return launch_tiled_cfg<4, 1, 1, 2, false>(a, stream);
-        case 8: return launch_tiled_cfg<4, 1, 1, 4, false>(a, stream);
-        default: return hipErrorInvalidValue;   // no tile shape fits (R, ks)
+      {
+        const int cfg = pick_tiled(a.M, a.N, a.K, a.R, a.ks, a.glu != 0);
+        const bool lean = tiled_lean(cfg, a.M, a.N, a.K);
+        return a.glu ? launch_tiled_pick<true>(a, cfg, lean, stream) : launch_tiled_pick<false>(a, cfg, lean, stream);
       }
     default:
       return launch_generic_rt<2, 2, false>(a, 0, mt, 0, nt, nullptr, 0, stream);

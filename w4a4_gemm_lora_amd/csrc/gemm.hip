@@ -957,7 +957,7 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_tiled_kernel(GemmArgs 
   // variant, 3 waves per SIMD, where the VALU work of the per-group epilogue
   // issues ~1.5x faster than at 2) keeps the loop's registers down: the
   // epilogue operands below are loaded after the loop, lora_act partials too,
-  // the stage ring is 3 deep, and the loop body runs tile by tile.
+  // the stage ring is 3 deep, and the loop body runs a few tiles at a time.
   constexpr bool kLean = OCC >= 3;
   // Epilogue operands, loaded first so that they arrive during the main loop
   // and the exact vmcnt waits below count only stage copies after them:
@@ -981,10 +981,10 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_tiled_kernel(GemmArgs 
   if constexpr (!kLean) load_epilogue_operands();
   // lora_act comes as g.ks <= SPL K-range partials; all of them are loaded
   // here and summed in order in the epilogue (no wait before the K loop) --
-  // unless they would take more than 64 registers through the loop: then the
-  // epilogue loads them rank block by rank block (one more memory round trip
-  // per workgroup).
-  constexpr bool kLateLora = kLean || TM * RT * SPL > 16;
+  // unless they would take more than 64 registers through the loop, or 64
+  // beside 4 x 4 accumulator tiles: then the epilogue loads them rank block
+  // by rank block (one more memory round trip per workgroup).
+  constexpr bool kLateLora = kLean || TM * RT * SPL > 16 || TM * RT >= 16;
   v4f la_p[kLateLora ? 1 : SPL][TM][RTL];
   if constexpr (!kLateLora && RT > 0) {
     const size_t part = (size_t)round_up16(g.M) * g.R;   // floats per partial
@@ -1058,15 +1058,25 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_tiled_kernel(GemmArgs 
         Be[j] = expand_group(r2[0], r2[1]);
       }
       if constexpr (kLean) {
-        // tile by tile: fewer registers live
+        // JP column tiles at a time (scale MFMAs, integer MFMAs, then the
+        // fmas): fewer registers live than a whole row tile's, fewer MFMA
+        // kind switches than tile by tile.  JP measured per shape: the whole
+        // row for 4 x 4 tiles (2-3% faster than pairs), pairs elsewhere.
+        constexpr int JP = TM * TN >= 16 ? TN : (TN % 2 == 0 ? 2 : 1);
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
-          for (int j = 0; j < TN; ++j) {
-            const v4f S = scale_tile(sxw[i], sww[j], h);
-            const v4i P = mfma_i8_16x16x64(Ae[i], Be[j], v4i{0, 0, 0, 0});
+          for (int j0 = 0; j0 < TN; j0 += JP) {
+            v4f S[JP];
+            v4i P[JP];
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) acc[i][j][ii] = fmaf((float)P[ii], S[ii], acc[i][j][ii]);
+            for (int q = 0; q < JP; ++q) S[q] = scale_tile(sxw[i], sww[j0 + q], h);
+#pragma unroll
+            for (int q = 0; q < JP; ++q) P[q] = mfma_i8_16x16x64(Ae[i], Be[j0 + q], v4i{0, 0, 0, 0});
+#pragma unroll
+            for (int q = 0; q < JP; ++q)
+#pragma unroll
+              for (int ii = 0; ii < 4; ++ii) acc[i][j0 + q][ii] = fmaf((float)P[q][ii], S[q][ii], acc[i][j0 + q][ii]);
           }
       } else {
         // Per row tile: its TN scale MFMAs, then its TN integer MFMAs, then

@@ -56,7 +56,8 @@ def _cases(M, K, N, Rg, Ru, seed):
                                          (4, 4096, 1024, 32, 32), (7, 1024, 80, 0, 16),
                                          (16, 4096, 1024, 32, 32), (12, 1536, 272, 16, 16),
                                          (17, 384, 48, 0, 0), (40, 384, 80, 16, 16),
-                                         (130, 3072, 48, 32, 16), (300, 1024, 208, 32, 32)])
+                                         (130, 3072, 48, 32, 16), (300, 1024, 208, 32, 32),
+                                         (3, 8192, 2048, 32, 32), (9, 8192, 2048, 16, 16)])
 def test_glu_layer_against_oracle(M, K, N, Rg, Ru):
     """h = fp16(SiLU(g) * u) within the layer tolerance (taken on h) of the
     oracle's separate gate and up layers; decode (M <= 16) and tiled (M > 16)

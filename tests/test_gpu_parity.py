@@ -257,7 +257,8 @@ def test_ragged_and_rank_edges(M, K, N, R):
                                      (13, 4864, 48, 64), (6, 1664, 8192, 48), (11, 384, 8192, 0),
                                      (16, 4864, 8192, 16), (9, 1664, 8192, 64), (1, 1664, 8192, 48),
                                      (2, 384, 8192, 0), (3, 4864, 8192, 64), (4, 1664, 8192, 16),
-                                     (4, 4864, 8192, 64)])
+                                     (4, 4864, 8192, 64), (1, 8192, 4096, 32), (16, 8192, 4096, 64),
+                                     (4, 16384, 2048, 16), (7, 8320, 1024, 48)])
 def test_small_m_decode_shapes(M, K, N, R):
     """M <= 16 kernels over uneven per-wave k-pair ranges (a wave with no
     k-pairs, ranges that are not a multiple of the batch), every rank, and
@@ -266,7 +267,9 @@ def test_small_m_decode_shapes(M, K, N, R):
     (512 column tiles) takes the two-column-tiles-per-workgroup paths: the
     dot kernel (M <= 3, every rank) and the MFMA decode kernel (M >= 4,
     R <= 48; R = 64 keeps one tile); at N = 8192 M = 4 runs the MFMA decode
-    kernel, at narrower N the dot kernel."""
+    kernel, at narrower N the dot kernel.  K >= 8192 with at most 256
+    workgroups (N <= 4096) takes the 8-wave workgroups, whose waves split K
+    eight ways (K = 8320: 65 k-pairs, a ragged split)."""
     case = workloads.random_case(M, K, N, R, seed=2000 + M + K + R)
     x = case["x"].astype(np.float64)
     x[:, (np.arange(K) // 64) % 2 == 1] *= 16.0

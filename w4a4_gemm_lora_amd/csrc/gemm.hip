@@ -341,7 +341,7 @@ __device__ __forceinline__ v4f scale_tile(uint32_t sx_pair, uint32_t sw_pair, in
 
 // ---------------------------------------------------------------------------
 // Decode kernel (M <= 16): weight-streaming, HBM-bound.
-// One workgroup per 16-column tile; its 4 waves split K into contiguous
+// One workgroup per 16-column tile; its DW waves split K into contiguous
 // ranges, worked through in batches of KB k-pairs: a wave issues the whole
 // batch of loads -- weight codes and scales (non-temporal: every weight byte
 // is used once) and activation codes and scales (shared by every workgroup,
@@ -352,14 +352,21 @@ __device__ __forceinline__ v4f scale_tile(uint32_t sx_pair, uint32_t sw_pair, in
 // MV = accumulator rows per lane that hold valid output (for M <= 4 every
 // valid row sits in lanes 0..15).
 // ---------------------------------------------------------------------------
-constexpr int kDecodeWaves = 4;
+// Waves per decode workgroup (DW): 4, splitting K four ways; 8 where the
+// grid has few workgroups (<= 256, e.g. 4096 columns) and K is long (>= 64
+// k-pairs), which otherwise leaves one wave per SIMD: K = 14336, N = 4096
+// measured 7.87 -> 7.19 us at M = 1 and 14.4 -> 9.6 us at M = 16, while at
+// 448 workgroups or K = 4096 eight waves were no faster or slower.
+static int decode_waves(int64_t workgroups, int64_t K) {
+  return (workgroups <= 256 && K / kKPair >= 64) ? 8 : 4;
+}
 
 // The LoRA operands of the decode epilogue: lora_act partials j = wave,
 // wave + 4 (< ks) of rows < M as unconditional loads (clamped addresses:
 // lanes of rows >= M read row 0, out-of-range j re-read a valid partial;
 // both are zeroed when folded), and for wave 0 the L_up fragments of the
 // workgroup's NTW column tiles.
-template <int RT, int NTW, int LQ, int RTL>
+template <int RT, int NTW, int LQ, int RTL, int DW>
 __device__ __forceinline__ void decode_lora_loads(const GemmArgs& g, int64_t nt0, int wave, int lane,
                                                   v4f (&lpart)[LQ][RTL], v4h (&lup)[NTW][RTL]) {
   if constexpr (RT > 0) {
@@ -367,7 +374,7 @@ __device__ __forceinline__ void decode_lora_loads(const GemmArgs& g, int64_t nt0
     const int rr = r < g.M ? r : 0;
 #pragma unroll
     for (int q = 0; q < LQ; ++q) {
-      const int j0 = wave + q * kDecodeWaves;
+      const int j0 = wave + q * DW;
       const int j = j0 < g.ks ? j0 : g.ks - 1;
 #pragma unroll
       for (int t = 0; t < RT; ++t)
@@ -383,16 +390,16 @@ __device__ __forceinline__ void decode_lora_loads(const GemmArgs& g, int64_t nt0
   }
 }
 
-template <int MV, int RT, int KB, int NTW, bool GLU>
-__global__ __launch_bounds__(256, 4) void gemm_decode_kernel(GemmArgs g) {
+template <int MV, int RT, int KB, int NTW, bool GLU, int DW>
+__global__ __launch_bounds__(64 * DW, 16 / DW) void gemm_decode_kernel(GemmArgs g) {
   constexpr int RTL = RT > 0 ? RT : 1;
-  __shared__ v4f red[NTW][kDecodeWaves][64];
-  __shared__ v4f lred[RTL][kDecodeWaves][64];
+  __shared__ v4f red[NTW][DW][64];
+  __shared__ v4f lred[RTL][DW][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nt0 = (int64_t)blockIdx.x * NTW;   // NTW column tiles per workgroup
   const int64_t KP = g.K / kKPair;
-  const int64_t per = (KP + kDecodeWaves - 1) / kDecodeWaves;
+  const int64_t per = (KP + DW - 1) / DW;
   const int64_t p0 = wave * per;
   const int64_t p1 = p0 + per < KP ? p0 + per : KP;
   const int c = lane >> 4, r = lane & 15;
@@ -404,7 +411,7 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_kernel(GemmArgs g) {
   // size: that instance loads them after the stream instead (one more memory
   // round trip in the tail).
   constexpr bool kEarly = !(RT == 4 && NTW == 2);
-  constexpr int LQ = (kMaxLoraSplits + kDecodeWaves - 1) / kDecodeWaves;
+  constexpr int LQ = (kMaxLoraSplits + DW - 1) / DW;
   v4f lpart[LQ][RTL];
   v4h lup[NTW][RTL];
   float af[NTW], bf[NTW];
@@ -414,7 +421,7 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_kernel(GemmArgs g) {
     const int rr = r < g.M ? r : 0;
 #pragma unroll
     for (int q = 0; q < LQ; ++q) {
-      const int j0 = wave + q * kDecodeWaves;
+      const int j0 = wave + q * DW;
       const int j = j0 < g.ks ? j0 : g.ks - 1;
 #pragma unroll
       for (int t = 0; t < RT; ++t)
@@ -452,7 +459,7 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_kernel(GemmArgs g) {
         v4f l4 = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int q = 0; q < LQ; ++q) {
-          const bool use = r < g.M && wave + q * kDecodeWaves < g.ks;
+          const bool use = r < g.M && wave + q * DW < g.ks;
           l4 += use ? lpart[q][t] : v4f{0.f, 0.f, 0.f, 0.f};
         }
         lred[t][wave][lane] = l4;
@@ -466,7 +473,7 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_kernel(GemmArgs g) {
         for (int t = 0; t < RT; ++t) {
           v4f l4 = lred[t][0][lane];
 #pragma unroll
-          for (int w = 1; w < kDecodeWaves; ++w) l4 += lred[t][w][lane];
+          for (int w = 1; w < DW; ++w) l4 += lred[t][w][lane];
           v4h hi, lo;
           split_f16(l4, hi, lo);
 #pragma unroll
@@ -536,7 +543,7 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_kernel(GemmArgs g) {
       }
     }
   }
-  if constexpr (!kEarly) decode_lora_loads<RT, NTW, LQ>(g, nt0, wave, lane, lpart, lup);
+  if constexpr (!kEarly) decode_lora_loads<RT, NTW, LQ, RTL, DW>(g, nt0, wave, lane, lpart, lup);
   if (!lora_done) lora_early();   // a wave with no k-pairs still meets the barrier
 
   // cross-wave sums in LDS, added by wave 0 in wave order
@@ -549,7 +556,7 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_kernel(GemmArgs g) {
   for (int n = 0; n < NTW; ++n) {
     v4f a = red[n][0][lane];
 #pragma unroll
-    for (int w = 1; w < kDecodeWaves; ++w) a += red[n][w][lane];
+    for (int w = 1; w < DW; ++w) a += red[n][w][lane];
     av[n] = a + a_lora[n];
   }
   if constexpr (!GLU) {
@@ -673,17 +680,17 @@ __device__ __forceinline__ void dot_accumulate(const DotBatch<MR, KB, NT>& d, co
   }
 }
 
-template <int MR, int RT, int KB, int NT, bool GLU>
-__global__ __launch_bounds__(256, 4) void gemm_decode_dot_kernel(GemmArgs g) {
+template <int MR, int RT, int KB, int NT, bool GLU, int DW>
+__global__ __launch_bounds__(64 * DW, 16 / DW) void gemm_decode_dot_kernel(GemmArgs g) {
   constexpr int RTL = RT > 0 ? RT : 1;
-  __shared__ float red[NT][kDecodeWaves][MR][16];
-  __shared__ v4f lred[RTL][kDecodeWaves][64];
-  __shared__ v4u xs_lds[kDecodeWaves][DotBatch<MR, KB, NT>::kXLoads * 64];
+  __shared__ float red[NT][DW][MR][16];
+  __shared__ v4f lred[RTL][DW][64];
+  __shared__ v4u xs_lds[DW][DotBatch<MR, KB, NT>::kXLoads * 64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nt0 = (int64_t)blockIdx.x * NT;   // NT column tiles per workgroup
   const int KP = (int)(g.K / kKPair);
-  const int per = (KP + kDecodeWaves - 1) / kDecodeWaves;
+  const int per = (KP + DW - 1) / DW;
   const int p0 = wave * per;
   const int p1 = p0 + per < KP ? p0 + per : KP;
   const int c = lane >> 4, r = lane & 15;
@@ -696,7 +703,7 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_dot_kernel(GemmArgs g) {
   // loads (clamped addresses: lanes of rows >= M read row 0, out-of-range j
   // re-read a valid partial; both are zeroed when folded), so no branch makes
   // the compiler's vmcnt waits conservative.
-  constexpr int LQ = (kMaxLoraSplits + kDecodeWaves - 1) / kDecodeWaves;
+  constexpr int LQ = (kMaxLoraSplits + DW - 1) / DW;
   v4f lpart[LQ][RTL];
   v4h lup[NT][RTL];
   float af[NT], bf[NT];
@@ -704,7 +711,7 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_dot_kernel(GemmArgs g) {
     const int rr = r < g.M ? r : 0;
 #pragma unroll
     for (int q = 0; q < LQ; ++q) {
-      const int j0 = wave + q * kDecodeWaves;
+      const int j0 = wave + q * DW;
       const int j = j0 < g.ks ? j0 : g.ks - 1;
 #pragma unroll
       for (int t = 0; t < RT; ++t)
@@ -742,7 +749,7 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_dot_kernel(GemmArgs g) {
         v4f l4 = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int q = 0; q < LQ; ++q) {
-          const bool use = r < g.M && wave + q * kDecodeWaves < g.ks;
+          const bool use = r < g.M && wave + q * DW < g.ks;
           l4 += use ? lpart[q][t] : v4f{0.f, 0.f, 0.f, 0.f};
         }
         lred[t][wave][lane] = l4;
@@ -756,7 +763,7 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_dot_kernel(GemmArgs g) {
         for (int t = 0; t < RT; ++t) {
           v4f l4 = lred[t][0][lane];
 #pragma unroll
-          for (int w = 1; w < kDecodeWaves; ++w) l4 += lred[t][w][lane];
+          for (int w = 1; w < DW; ++w) l4 += lred[t][w][lane];
           v4h hi, lo;
           split_f16(l4, hi, lo);
 #pragma unroll
@@ -824,7 +831,7 @@ __global__ __launch_bounds__(256, 4) void gemm_decode_dot_kernel(GemmArgs g) {
       for (int m = 0; m < MR; ++m) {
         float v = red[n][0][m][r];
 #pragma unroll
-        for (int w = 1; w < kDecodeWaves; ++w) v += red[n][w][m][r];
+        for (int w = 1; w < DW; ++w) v += red[n][w][m][r];
         a[m] += v;
       }
     }
@@ -1189,18 +1196,24 @@ constexpr int mv_kb(int rt, int ntw) {
   return kTable[ntw - 1][rt];
 }
 
-template <int MV, int NTW, bool GLU>
-static hipError_t launch_decode_mv_n(const GemmArgs& a, hipStream_t stream) {
-  dim3 grid((unsigned)(a.N / 16 / NTW)), block(64 * kDecodeWaves);
+template <int MV, int NTW, bool GLU, int DW>
+static hipError_t launch_decode_mv_dw(const GemmArgs& a, hipStream_t stream) {
+  dim3 grid((unsigned)(a.N / 16 / NTW)), block(64 * DW);
   switch (a.R / 16) {
-    case 0: gemm_decode_kernel<MV, 0, mv_kb(0, NTW), NTW, GLU><<<grid, block, 0, stream>>>(a); break;
-    case 1: gemm_decode_kernel<MV, 1, mv_kb(1, NTW), NTW, GLU><<<grid, block, 0, stream>>>(a); break;
-    case 2: gemm_decode_kernel<MV, 2, mv_kb(2, NTW), NTW, GLU><<<grid, block, 0, stream>>>(a); break;
-    case 3: gemm_decode_kernel<MV, 3, mv_kb(3, NTW), NTW, GLU><<<grid, block, 0, stream>>>(a); break;
-    case 4: gemm_decode_kernel<MV, 4, mv_kb(4, NTW), NTW, GLU><<<grid, block, 0, stream>>>(a); break;
+    case 0: gemm_decode_kernel<MV, 0, mv_kb(0, NTW), NTW, GLU, DW><<<grid, block, 0, stream>>>(a); break;
+    case 1: gemm_decode_kernel<MV, 1, mv_kb(1, NTW), NTW, GLU, DW><<<grid, block, 0, stream>>>(a); break;
+    case 2: gemm_decode_kernel<MV, 2, mv_kb(2, NTW), NTW, GLU, DW><<<grid, block, 0, stream>>>(a); break;
+    case 3: gemm_decode_kernel<MV, 3, mv_kb(3, NTW), NTW, GLU, DW><<<grid, block, 0, stream>>>(a); break;
+    case 4: gemm_decode_kernel<MV, 4, mv_kb(4, NTW), NTW, GLU, DW><<<grid, block, 0, stream>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <int MV, int NTW, bool GLU>
+static hipError_t launch_decode_mv_n(const GemmArgs& a, hipStream_t stream) {
+  if (decode_waves(a.N / 16 / NTW, a.K) == 8) return launch_decode_mv_dw<MV, NTW, GLU, 8>(a, stream);
+  return launch_decode_mv_dw<MV, NTW, GLU, 4>(a, stream);
 }
 
 // Two column tiles per workgroup (one activation tile serves both) when the
@@ -1229,16 +1242,24 @@ constexpr int dot_kb(int mr, int rt, int nt) {
 // A wave whose k range is shorter than one batch would run only the
 // bounds-checked tail batch, whose conditional loads make every wait a full
 // drain; a 4-pair batch keeps such short ranges on the unchecked path.
-template <int MR, int RT, int NT, bool GLU>
-static void launch_dot_rt(const GemmArgs& a, hipStream_t stream) {
+template <int MR, int RT, int NT, bool GLU, int DW>
+static void launch_dot_rt_dw(const GemmArgs& a, hipStream_t stream) {
   constexpr int KB = dot_kb(MR, RT, NT);
   constexpr int KBS = KB < 4 ? KB : 4;
-  const dim3 grid((unsigned)(a.N / 16 / NT)), block(64 * kDecodeWaves);
-  const int64_t per = (a.K / kKPair + kDecodeWaves - 1) / kDecodeWaves;
+  const dim3 grid((unsigned)(a.N / 16 / NT)), block(64 * DW);
+  const int64_t per = (a.K / kKPair + DW - 1) / DW;
   if (KBS < KB && per < KB)
-    gemm_decode_dot_kernel<MR, RT, KBS, NT, GLU><<<grid, block, 0, stream>>>(a);
+    gemm_decode_dot_kernel<MR, RT, KBS, NT, GLU, DW><<<grid, block, 0, stream>>>(a);
   else
-    gemm_decode_dot_kernel<MR, RT, KB, NT, GLU><<<grid, block, 0, stream>>>(a);
+    gemm_decode_dot_kernel<MR, RT, KB, NT, GLU, DW><<<grid, block, 0, stream>>>(a);
+}
+
+template <int MR, int RT, int NT, bool GLU>
+static void launch_dot_rt(const GemmArgs& a, hipStream_t stream) {
+  if (decode_waves(a.N / 16 / NT, a.K) == 8)
+    launch_dot_rt_dw<MR, RT, NT, GLU, 8>(a, stream);
+  else
+    launch_dot_rt_dw<MR, RT, NT, GLU, 4>(a, stream);
 }
 
 template <int MR, int NT, bool GLU>

@@ -326,6 +326,24 @@ def test_every_lean_tile_shape(cfg, K, R, monkeypatch):
     assert np.all(np.isnan(run.host_y()[M:].astype(np.float64)))
 
 
+@pytest.mark.parametrize("cfg,R", [(c, R) for c in (3, 4, 5, 7, 8) for R in (32, 64)])
+def test_every_k_split_tile_shape(cfg, R, monkeypatch):
+    """The K-split variant (two sets of waves over the two halves of K, the
+    second's accumulators added to the first's in LDS) of each tile shape
+    that has one, forced, on the ragged shape above with K = 2560 (20
+    k-pairs, 10 per half; two lora_act partials)."""
+    M, N, K = 130, 208, 2560
+    monkeypatch.setenv("W4A4_TILED_CFG", str(cfg))
+    monkeypatch.setenv("W4A4_TILED_LEAN", "0")
+    monkeypatch.setenv("W4A4_TILED_KSPLIT", "1")
+    case = workloads.random_case(M, K, N, R, seed=3700 + cfg + R)
+    _say(f"[k-split tile shape {cfg}] M={M} K={K} N={N} R={R}")
+    run = GpuRun(case)
+    ref = O.linear(case["x"], case["lora_down"], case["lora_up"], case["col_scale"], case["bias"], w16=case["w"])
+    _check_y(run.host_y()[:M, :N], ref["y"], f"k-split tile shape {cfg}")
+    assert np.all(np.isnan(run.host_y()[M:].astype(np.float64)))
+
+
 def test_strided_x_and_y():
     M, K, N, R = 40, 256, 64, 32
     case = workloads.random_case(M, K, N, R, seed=7)

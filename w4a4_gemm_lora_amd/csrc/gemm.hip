@@ -863,9 +863,13 @@ __global__ __launch_bounds__(64 * DW, 16 / DW) void gemm_decode_dot_kernel(GemmA
 // ---------------------------------------------------------------------------
 constexpr int kTileGroupRows = 8;
 
-template <int WM, int WN, int TM, int TN, int RT, int NS, int SPL, bool GLU, int OCC>
-__global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_tiled_kernel(GemmArgs g, int64_t mt_count,
-                                                                   int64_t nt_count) {
+template <int WM, int WN, int TM, int TN, int RT, int NS, int SPL, bool GLU, int OCC, int KS>
+__global__ __launch_bounds__(WM * WN * KS * 64, OCC) void gemm_tiled_kernel(GemmArgs g, int64_t mt_count,
+                                                                        int64_t nt_count) {
+  // KS = 2 splits K between two sets of WM x WN waves over the same output
+  // tiles (each with its own stage ring, in lockstep), and the second set's
+  // accumulators are added to the first's in LDS after the loop: twice the
+  // waves for launches too small to give every SIMD two (K % 256 == 0).
   constexpr int NW = WM * WN;
   constexpr int BMT = WM * TM, BNT = WN * TN;            // tiles per workgroup
   constexpr int CHUNKS = BMT + BNT;                      // 1 KB operand tiles per stage
@@ -873,10 +877,12 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_tiled_kernel(GemmArgs 
   constexpr int SLOTS = CPW * NW;                        // >= CHUNKS; extra slots take dummy copies
   static_assert(SLOTS <= 16, "the scale copy covers at most 16 tiles");
   constexpr int OPS = CPW + 1;                           // + one scale copy
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[NS][SLOTS + 1][kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NS][KS][SLOTS + 1][kTileBytes];
 
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+  const int wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+  const int kh = wave_all / NW;      // K part of this wave (KS > 1)
+  const int wave = wave_all % NW;    // the wave's tile role
   const int wm = wave / WN, wn = wave % WN;
   const int c = lane >> 4;
 
@@ -908,7 +914,8 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_tiled_kernel(GemmArgs 
     bm = first_bm + (in_g - bn * gm);
   }
   const int64_t mt0 = bm * BMT, nt0 = bn * BNT;
-  const int64_t KP = g.K / kKPair;
+  const int64_t KPT = g.K / kKPair;   // k-pairs of the whole K
+  const int64_t KP = KPT / KS;        // k-pairs of this wave's part
 
   // operand tile q of a stage: q < BMT -> A tile mt0+q; else B tile nt0+q-BMT.
   // Tiles past the edge re-read the last valid tile (never stored); slots
@@ -931,13 +938,14 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_tiled_kernel(GemmArgs 
   for (int u = 0; u < CPW; ++u) {
     const int q = wave * CPW + u;
     const uint8_t* base = (q < CHUNKS ? q : CHUNKS - 1) < BMT ? g.xq : g.wq;
-    src[u] = base + (size_t)tile_index(q) * KP * kTileBytes;
+    src[u] = base + ((size_t)tile_index(q) * KPT + (size_t)kh * KP) * kTileBytes;
   }
   const uint8_t* ssrc;
   {
     const int q = wave * CPW + ((lane >> 2) < CPW ? (lane >> 2) : CPW - 1);
     const uint16_t* sbase = (q < CHUNKS ? q : CHUNKS - 1) < BMT ? g.sx : g.sw;
-    ssrc = reinterpret_cast<const uint8_t*>(sbase) + (size_t)tile_index(q) * KP * 64 + (lane & 3) * 16;
+    ssrc = reinterpret_cast<const uint8_t*>(sbase) + ((size_t)tile_index(q) * KPT + (size_t)kh * KP) * 64 +
+           (lane & 3) * 16;
   }
   const uint32_t lane_off = lane * 16u;
   auto issue_copy = [&](int stage, int64_t p) {
@@ -947,11 +955,11 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_tiled_kernel(GemmArgs 
       // captured array element feeds the builtin directly)
       const uint8_t* sp = src[u];
       __builtin_amdgcn_global_load_lds(sp + (size_t)p * kTileBytes + lane_off,
-                                       (lds_void*)&lds[stage][wave * CPW + u][0], 16, 0, 0);
+                                       (lds_void*)&lds[stage][kh][wave * CPW + u][0], 16, 0, 0);
     }
     if (lane < 4 * CPW)
-      __builtin_amdgcn_global_load_lds(ssrc + (size_t)p * 64, (lds_void*)&lds[stage][SLOTS][wave * CPW * 64],
-                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds(ssrc + (size_t)p * 64,
+                                       (lds_void*)&lds[stage][kh][SLOTS][wave * CPW * 64], 16, 0, 0);
   };
 
   v4f acc[TM][TN];
@@ -1043,7 +1051,7 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_tiled_kernel(GemmArgs 
     // its row tiles and s_w of column l%16 of each of its column tiles (both
     // groups in one dword).  The 4x4x4 f16 MFMA turns them into the exact
     // fp32 tile S[m][n] = s_x[m] * s_w[n] in the accumulator layout.
-    const uint8_t* sl = &lds[st][SLOTS][0];
+    const uint8_t* sl = &lds[st][kh][SLOTS][0];
     uint32_t sxw[TM], sww[TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -1056,12 +1064,12 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_tiled_kernel(GemmArgs 
       v4i Ae[TM], Be[TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        const v2u r2 = *reinterpret_cast<const v2u*>(&lds[st][wm * TM + i][lane * 16 + h * 8]);
+        const v2u r2 = *reinterpret_cast<const v2u*>(&lds[st][kh][wm * TM + i][lane * 16 + h * 8]);
         Ae[i] = expand_group(r2[0], r2[1]);
       }
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const v2u r2 = *reinterpret_cast<const v2u*>(&lds[st][BMT + wn * TN + j][lane * 16 + h * 8]);
+        const v2u r2 = *reinterpret_cast<const v2u*>(&lds[st][kh][BMT + wn * TN + j][lane * 16 + h * 8]);
         Be[j] = expand_group(r2[0], r2[1]);
       }
       if constexpr (kLean) {
@@ -1107,6 +1115,26 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void gemm_tiled_kernel(GemmArgs 
     }
     st = st + 1 == NS ? 0 : st + 1;
     st_next = st_next + 1 == NS ? 0 : st_next + 1;
+  }
+
+  if constexpr (KS > 1) {
+    // the second K part's accumulators join the first's, in that order
+    static_assert(KS == 2, "two K parts");
+    static_assert(NW * TM * TN * 64 * sizeof(v4f) <= sizeof(lds), "reduction fits the stage ring");
+    v4f* red = reinterpret_cast<v4f*>(&lds[0][0][0][0]);
+    __syncthreads();   // every wave is done with the ring
+    if (kh == 1) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) red[((size_t)wave * TM * TN + i * TN + j) * 64 + lane] = acc[i][j];
+    }
+    __syncthreads();
+    if (kh == 1) return;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] += red[((size_t)wave * TM * TN + i * TN + j) * 64 + lane];
   }
 
   if constexpr (kLean) load_epilogue_operands();
@@ -1309,16 +1337,16 @@ static hipError_t launch_decode(const GemmArgs& a, hipStream_t stream) {
 
 // LDS stage ring depth: 4, or 3 for the lean (3 workgroups per CU) variant,
 // whose 128 x 128 tile shape then fits three 51 KB rings in a CU's 160 KB.
-template <int WM, int WN, int TM, int TN, int SPL, bool GLU, int OCC>
+template <int WM, int WN, int TM, int TN, int SPL, bool GLU, int OCC, int KS>
 static hipError_t launch_tiled_spl(const GemmArgs& a, int64_t mt, int64_t nt, dim3 grid, dim3 block,
                                    hipStream_t stream) {
   constexpr int NS = OCC >= 3 ? 3 : 4;
   switch (a.R / 16) {
-    case 0: gemm_tiled_kernel<WM, WN, TM, TN, 0, NS, SPL, GLU, OCC><<<grid, block, 0, stream>>>(a, mt, nt); break;
-    case 1: gemm_tiled_kernel<WM, WN, TM, TN, 1, NS, SPL, GLU, OCC><<<grid, block, 0, stream>>>(a, mt, nt); break;
-    case 2: gemm_tiled_kernel<WM, WN, TM, TN, 2, NS, SPL, GLU, OCC><<<grid, block, 0, stream>>>(a, mt, nt); break;
-    case 3: gemm_tiled_kernel<WM, WN, TM, TN, 3, NS, SPL, GLU, OCC><<<grid, block, 0, stream>>>(a, mt, nt); break;
-    case 4: gemm_tiled_kernel<WM, WN, TM, TN, 4, NS, SPL, GLU, OCC><<<grid, block, 0, stream>>>(a, mt, nt); break;
+    case 0: gemm_tiled_kernel<WM, WN, TM, TN, 0, NS, SPL, GLU, OCC, KS><<<grid, block, 0, stream>>>(a, mt, nt); break;
+    case 1: gemm_tiled_kernel<WM, WN, TM, TN, 1, NS, SPL, GLU, OCC, KS><<<grid, block, 0, stream>>>(a, mt, nt); break;
+    case 2: gemm_tiled_kernel<WM, WN, TM, TN, 2, NS, SPL, GLU, OCC, KS><<<grid, block, 0, stream>>>(a, mt, nt); break;
+    case 3: gemm_tiled_kernel<WM, WN, TM, TN, 3, NS, SPL, GLU, OCC, KS><<<grid, block, 0, stream>>>(a, mt, nt); break;
+    case 4: gemm_tiled_kernel<WM, WN, TM, TN, 4, NS, SPL, GLU, OCC, KS><<<grid, block, 0, stream>>>(a, mt, nt); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1326,14 +1354,15 @@ static hipError_t launch_tiled_spl(const GemmArgs& a, int64_t mt, int64_t nt, di
 
 // SPL = number of lora_act partials a wave sums: 1, or up to
 // kMaxTiledLoraSplits.
-template <int WM, int WN, int TM, int TN, bool GLU, int OCC>
+template <int WM, int WN, int TM, int TN, bool GLU, int OCC, int KS = 1>
 static hipError_t launch_tiled_cfg(const GemmArgs& a, hipStream_t stream) {
   const int64_t mt = round_up16(a.M) / 16, nt = a.N / 16;
   const int64_t nblk = ((mt + WM * TM - 1) / (WM * TM)) * ((nt + WN * TN - 1) / (WN * TN));
   if (nblk >= ((int64_t)1 << 31)) return hipErrorInvalidValue;   // the kernel's tile math is 32-bit
-  dim3 grid((unsigned)nblk), block(64 * WM * WN);
-  if (a.ks == 1) return launch_tiled_spl<WM, WN, TM, TN, 1, GLU, OCC>(a, mt, nt, grid, block, stream);
-  return launch_tiled_spl<WM, WN, TM, TN, kMaxTiledLoraSplits, GLU, OCC>(a, mt, nt, grid, block, stream);
+  if (KS > 1 && (a.K / kKPair) % KS != 0) return hipErrorInvalidValue;
+  dim3 grid((unsigned)nblk), block(64 * WM * WN * KS);
+  if (a.ks == 1) return launch_tiled_spl<WM, WN, TM, TN, 1, GLU, OCC, KS>(a, mt, nt, grid, block, stream);
+  return launch_tiled_spl<WM, WN, TM, TN, kMaxTiledLoraSplits, GLU, OCC, KS>(a, mt, nt, grid, block, stream);
 }
 
 // Tile shapes for M > 16: a workgroup of WM x WN waves, each wave TM x TN
@@ -1423,8 +1452,37 @@ static bool tiled_lean(int cfg, int64_t M, int64_t N, int64_t K) {
   return tkp >= 150.0 * 1024;
 }
 
+// Split K inside the workgroup (KS = 2) for launches that would leave a
+// SIMD fewer than two waves, on the small tile shapes such launches pick,
+// when K has >= 16 k-pairs in an even count.  W4A4_TILED_KSPLIT=0 / 1
+// forces the choice where both exist (tuning and test aid).
+constexpr bool kKSplitCfg[kNumTiledCfgs] = {false, false, false, true, true, true, false, true, true};
+static bool tiled_ksplit(int cfg, int64_t M, int64_t N, int64_t K) {
+  if (cfg < 0 || cfg >= kNumTiledCfgs || !kKSplitCfg[cfg]) return false;
+  const int64_t kp = K / kKPair;
+  if (kp % 2 != 0) return false;
+  const char* e = std::getenv("W4A4_TILED_KSPLIT");
+  if (e && (e[0] == '0' || e[0] == '1')) return e[0] == '1';
+  const TiledCfg& c = kTiledCfgs[cfg];
+  const int64_t bmt = c.wm * c.tm, bnt = c.wn * c.tn;
+  const int64_t nblk = ((round_up16(M) / 16 + bmt - 1) / bmt) * ((N / 16 + bnt - 1) / bnt);
+  return kp >= 16 && nblk * c.wm * c.wn < 2048;
+}
+
 template <bool GLU>
 static hipError_t launch_tiled_pick(const GemmArgs& a, int cfg, bool lean, hipStream_t stream) {
+  if constexpr (!GLU) {
+    if (!lean && tiled_ksplit(cfg, a.M, a.N, a.K)) {
+      switch (cfg) {
+        case 3: return launch_tiled_cfg<2, 2, 2, 2, false, 2, 2>(a, stream);
+        case 4: return launch_tiled_cfg<2, 2, 1, 2, false, 2, 2>(a, stream);
+        case 5: return launch_tiled_cfg<4, 1, 1, 3, false, 2, 2>(a, stream);
+        case 7: return launch_tiled_cfg<4, 1, 1, 2, false, 2, 2>(a, stream);
+        case 8: return launch_tiled_cfg<4, 1, 1, 4, false, 2, 2>(a, stream);
+        default: break;
+      }
+    }
+  }
   if (lean) {
     switch (cfg) {
       case 0: return launch_tiled_cfg<2, 2, 4, 4, GLU, 3>(a, stream);

@@ -974,8 +974,9 @@ __global__ __launch_bounds__(WM * WN * KS * 64, OCC) void gemm_tiled_kernel(Gemm
   // epilogue operands below are loaded after the loop, lora_act partials too,
   // the stage ring is 3 deep, and the loop body runs a few tiles at a time.
   constexpr bool kLean = OCC >= 3;
-  // Epilogue operands, loaded first so that they arrive during the main loop
-  // and the exact vmcnt waits below count only stage copies after them:
+  // Epilogue operands, loaded during the first k-pair (after the first
+  // stages' copies, so that those reach the memory pipeline first; the exact
+  // vmcnt waits of later k-pairs then only wait a little more than needed):
   // L_up fragments and the affine of its columns (lora_act fragments of the
   // wave's row tiles follow).  Tiles past the edge read the last valid tile
   // (never stored).
@@ -993,31 +994,31 @@ __global__ __launch_bounds__(WM * WN * KS * 64, OCC) void gemm_tiled_kernel(Gemm
         lu_f[j][t] = *reinterpret_cast<const v4h*>(g.lup + (((size_t)nt * RT + t) * 64 + lane) * 4);
     }
   };
-  if constexpr (!kLean) load_epilogue_operands();
   // lora_act comes as g.ks <= SPL K-range partials; all of them are loaded
-  // here and summed in order in the epilogue (no wait before the K loop) --
+  // with the operands above and summed in order in the epilogue --
   // unless they would take more than 64 registers through the loop, or 64
   // beside 4 x 4 accumulator tiles: then the epilogue loads them rank block
   // by rank block (one more memory round trip per workgroup).
   constexpr bool kLateLora = kLean || TM * RT * SPL > 16 || TM * RT >= 16;
   v4f la_p[kLateLora ? 1 : SPL][TM][RTL];
-  if constexpr (!kLateLora && RT > 0) {
-    const size_t part = (size_t)round_up16(g.M) * g.R;   // floats per partial
+  auto load_lora_partials = [&]() {
+    if constexpr (!kLateLora && RT > 0) {
+      const size_t part = (size_t)round_up16(g.M) * g.R;   // floats per partial
 #pragma unroll
-    for (int j = 0; j < SPL; ++j) {
-      if (j < g.ks) {   // uniform
+      for (int j = 0; j < SPL; ++j) {
+        if (j < g.ks) {   // uniform
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          const int64_t mt = tile_index(wm * TM + i);
+          for (int i = 0; i < TM; ++i) {
+            const int64_t mt = tile_index(wm * TM + i);
 #pragma unroll
-          for (int t = 0; t < RT; ++t)
-            la_p[j][i][t] = *reinterpret_cast<const v4f*>(g.la + j * part + (size_t)(mt * 16 + (lane & 15)) * g.R +
-                                                          t * 16 + c * 4);
+            for (int t = 0; t < RT; ++t)
+              la_p[j][i][t] = *reinterpret_cast<const v4f*>(
+                  g.la + j * part + (size_t)(mt * 16 + (lane & 15)) * g.R + t * 16 + c * 4);
+          }
         }
       }
     }
-  }
-
+  };
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
     if (s < KP) issue_copy(s, s);
@@ -1047,6 +1048,15 @@ __global__ __launch_bounds__(WM * WN * KS * 64, OCC) void gemm_tiled_kernel(Gemm
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if (p + NS - 1 < KP) issue_copy(st_next, p + NS - 1);
+    if constexpr (!kLean) {
+      // younger than the copies of stages 1.. issued so far: a later wait
+      // that lets the copies issued after its stage stay in flight finds
+      // these among them, so it completes its stage all the same
+      if (p == 0) {
+        load_epilogue_operands();
+        load_lora_partials();
+      }
+    }
     // Scales of this k-pair: lane l needs s_x of row 4(l/16) + l%4 of each of
     // its row tiles and s_w of column l%16 of each of its column tiles (both
     // groups in one dword).  The 4x4x4 f16 MFMA turns them into the exact

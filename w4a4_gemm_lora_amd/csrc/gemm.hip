@@ -887,7 +887,9 @@ __global__ __launch_bounds__(WM * WN * KS * 64, OCC) void gemm_tiled_kernel(Gemm
   const int c = lane >> 4;
 
   // 32-bit tile arithmetic: the launcher guarantees nblk < 2^31.
-  const uint32_t nbm = (uint32_t)((mt_count + BMT - 1) / BMT), nbn = (uint32_t)((nt_count + BNT - 1) / BNT);
+  // 32-bit tile counts (the launcher keeps them below 2^31)
+  const uint32_t mtc = (uint32_t)mt_count, ntc = (uint32_t)nt_count;
+  const uint32_t nbm = (mtc + BMT - 1) / BMT, nbn = (ntc + BNT - 1) / BNT;
   const uint32_t nblk = nbm * nbn;
   uint32_t b = blockIdx.x;
   {
@@ -913,7 +915,7 @@ __global__ __launch_bounds__(WM * WN * KS * 64, OCC) void gemm_tiled_kernel(Gemm
     bn = in_g / gm;
     bm = first_bm + (in_g - bn * gm);
   }
-  const int64_t mt0 = bm * BMT, nt0 = bn * BNT;
+  const uint32_t mt0 = bm * BMT, nt0 = bn * BNT;
   const int64_t KPT = g.K / kKPair;   // k-pairs of the whole K
   const int64_t KP = KPT / KS;        // k-pairs of this wave's part
 
@@ -924,11 +926,11 @@ __global__ __launch_bounds__(WM * WN * KS * 64, OCC) void gemm_tiled_kernel(Gemm
   auto tile_index = [&](int q) -> int64_t {
     q = q < CHUNKS ? q : CHUNKS - 1;
     if (q < BMT) {
-      const int64_t t = mt0 + q;
-      return t < mt_count ? t : mt_count - 1;
+      const uint32_t t = mt0 + q;
+      return t < mtc ? t : mtc - 1;
     }
-    const int64_t t = nt0 + (q - BMT);
-    return t < nt_count ? t : nt_count - 1;
+    const uint32_t t = nt0 + (q - BMT);
+    return t < ntc ? t : ntc - 1;
   };
   // Copy sources at k-pair 0: the wave's operand tiles (wave-uniform
   // pointers) and, for lanes l < 4*CPW, 16 B of the scales of tile

@@ -860,6 +860,10 @@ __global__ __launch_bounds__(64 * DW, 16 / DW) void gemm_decode_dot_kernel(GemmA
 // renumbered so that the workgroups of one XCD cover a contiguous range of
 // a grouped tile order (groups of 8 row bands, column tiles outer), which
 // keeps both operands' working set of an XCD inside its L2.
+// Variants (template arguments): OCC = 3 -- the lean variant for large
+// launches (3 workgroups per CU, 3-deep ring, epilogue operands after the
+// loop); KS = 2 -- two sets of waves split K for launches that would give a
+// SIMD fewer than two waves; GLU -- the gated (SiLU(gate) * up) epilogue.
 // ---------------------------------------------------------------------------
 constexpr int kTileGroupRows = 8;
 

@@ -11,7 +11,9 @@
 // int8 (16*q per byte, see expand_group) in registers and issues
 // v_mfma_i32_16x16x64_i8 once per (16x16 output tile, group) with a zero C,
 // which yields 256*P exactly.  The fp32 epilogue per group folds the 1/256
-// into the weight scale.  LoRA-up runs on v_mfma_f32_16x16x16_f16 with the
+// into the weight scale.  The tiled kernel (M > 16) instead starts the MFMA
+// from the bits of 3.0f, so that its result read as fp32 is 3 + P 2^-14 and
+// the conversion drops out of the per-group epilogue (kOffsetBits).  LoRA-up runs on v_mfma_f32_16x16x16_f16 with the
 // fp32 lora_act (the in-order sum of its partials) split into fp16 hi + lo
 // parts, accumulating straight into the main accumulator; the affine and the
 // fp16 rounding follow in registers.
@@ -26,7 +28,8 @@
 // Cost model measured on MI355X: one v_mfma_i32_16x16x64_i8 occupies a SIMD
 // for ~16.5 cycles and a wave64 fp32 VALU op for ~2.6-2.9 cycles, and the two
 // barely overlap, so the per-group epilogue (convert, scale product, fma on
-// four accumulators per lane) costs about twice the MFMA itself.  Large-M
+// four accumulators per lane) costs about twice the MFMA itself; the tiled
+// kernel trades the four conversions for half of one more 4x4x4 MFMA.  Large-M
 // kernels are therefore bound by issue of MFMA + VALU, not by HBM.
 #include <cstdlib>
 
@@ -337,6 +340,30 @@ __device__ __forceinline__ v4f scale_tile(uint32_t sx_pair, uint32_t sw_pair, in
   const v4h a = __builtin_bit_cast(v4h, v2u{sx_pair, 0u});
   const v4h b = __builtin_bit_cast(v4h, v2u{sw_pair & (h ? 0xFFFF0000u : 0x0000FFFFu), 0u});
   return __builtin_amdgcn_mfma_f32_4x4x4f16(a, b, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+}
+
+// Integer group sums as fp32 without a conversion.  The i8 MFMA adds 256 P
+// (|256 P| <= 2^20) to its C operand; started from the bits of 3.0f (exponent
+// 1, mantissa field 2^22) instead of zero, the result read as fp32 is exactly
+// 3 + P * 2^-14.  The tiled loop keeps acc' = acc * 2^-14 and, per k-pair and
+// tile, first subtracts 3 (S_0 + S_1) with one more 4x4x4 f16 MFMA whose C is
+// acc' (offset_tile), then adds S_h * (3 + P_h 2^-14) for both groups with one
+// fma each: every group's offset cancels within the k-pair, so acc' never
+// carries more than 3 S of offset (rounding ~2^-24 * 3 S per step, against
+// group terms of P S 2^-14).
+constexpr int kOffsetBits = 0x40400000;   // 3.0f
+
+// acc' - 3 (S_0 + S_1) for one 16 x 16 tile, S_h = s_x[row] s_w[col] of group
+// h in the accumulator layout: A carries (s_x g0, s_x g1, 2 s_x g0, 2 s_x g1)
+// (doubling an fp16 s_x <= 65504 / 7 is exact) and B (-s_w g0, -s_w g1,
+// -s_w g0, -s_w g1); each product is exact in fp32.
+__device__ __forceinline__ v4f offset_tile(uint32_t sx_pair, uint32_t sw_pair, v4f acc) {
+  typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+  const uint32_t nsx = sx_pair ^ 0x80008000u;
+  const v2h sx = __builtin_bit_cast(v2h, nsx);
+  const v4h a = __builtin_bit_cast(v4h, v2u{nsx, __builtin_bit_cast(uint32_t, sx + sx)});
+  const v4h b = __builtin_bit_cast(v4h, v2u{sw_pair, sw_pair});
+  return __builtin_amdgcn_mfma_f32_4x4x4f16(a, b, acc, 0, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -889,6 +916,7 @@ __global__ __launch_bounds__(WM * WN * KS * 64, OCC) void gemm_tiled_kernel(Gemm
   const int wave = wave_all % NW;    // the wave's tile role
   const int wm = wave / WN, wn = wave % WN;
   const int c = lane >> 4;
+  const v4i kOffset = v4i{kOffsetBits, kOffsetBits, kOffsetBits, kOffsetBits};
 
   // 32-bit tile arithmetic: the launcher guarantees nblk < 2^31.
   // 32-bit tile counts (the launcher keeps them below 2^31)
@@ -1075,14 +1103,19 @@ __global__ __launch_bounds__(WM * WN * KS * 64, OCC) void gemm_tiled_kernel(Gemm
 #pragma unroll
     for (int j = 0; j < TN; ++j)
       sww[j] = *reinterpret_cast<const uint32_t*>(sl + (BMT + wn * TN + j) * 64 + (lane & 15) * 4);
+    // both groups' offsets leave the accumulators first (see kOffsetBits)
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = offset_tile(sxw[i], sww[j], acc[i][j]);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      v4i Ae[TM], Be[TN];
+      // A codes stay packed until their row tile comes up (lean: fewer
+      // registers live)
+      v2u Ar[TM];
+      v4i Be[TN];
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const v2u r2 = *reinterpret_cast<const v2u*>(&lds[st][kh][wm * TM + i][lane * 16 + h * 8]);
-        Ae[i] = expand_group(r2[0], r2[1]);
-      }
+      for (int i = 0; i < TM; ++i) Ar[i] = *reinterpret_cast<const v2u*>(&lds[st][kh][wm * TM + i][lane * 16 + h * 8]);
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const v2u r2 = *reinterpret_cast<const v2u*>(&lds[st][kh][BMT + wn * TN + j][lane * 16 + h * 8]);
@@ -1091,11 +1124,12 @@ __global__ __launch_bounds__(WM * WN * KS * 64, OCC) void gemm_tiled_kernel(Gemm
       if constexpr (kLean) {
         // JP column tiles at a time (scale MFMAs, integer MFMAs, then the
         // fmas): fewer registers live than a whole row tile's, fewer MFMA
-        // kind switches than tile by tile.  JP measured per shape: the whole
-        // row for 4 x 4 tiles (2-3% faster than pairs), pairs elsewhere.
-        constexpr int JP = TM * TN >= 16 ? TN : (TN % 2 == 0 ? 2 : 1);
+        // kind switches than tile by tile.  Pairs: a whole row of 4 x 4
+        // tiles no longer fits 168 registers beside the offset operand.
+        constexpr int JP = (TN % 2 == 0 ? 2 : 1);
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TM; ++i) {
+          const v4i Ae = expand_group(Ar[i][0], Ar[i][1]);
 #pragma unroll
           for (int j0 = 0; j0 < TN; j0 += JP) {
             v4f S[JP];
@@ -1103,12 +1137,17 @@ __global__ __launch_bounds__(WM * WN * KS * 64, OCC) void gemm_tiled_kernel(Gemm
 #pragma unroll
             for (int q = 0; q < JP; ++q) S[q] = scale_tile(sxw[i], sww[j0 + q], h);
 #pragma unroll
-            for (int q = 0; q < JP; ++q) P[q] = mfma_i8_16x16x64(Ae[i], Be[j0 + q], v4i{0, 0, 0, 0});
+            for (int q = 0; q < JP; ++q) P[q] = mfma_i8_16x16x64(Ae, Be[j0 + q], kOffset);
 #pragma unroll
-            for (int q = 0; q < JP; ++q)
+            for (int q = 0; q < JP; ++q) {
+              // (cast the whole vector: clang's bit_cast of one element of an
+              // ext_vector reads element 0 whatever the index)
+              const v4f Pf = __builtin_bit_cast(v4f, P[q]);
 #pragma unroll
-              for (int ii = 0; ii < 4; ++ii) acc[i][j0 + q][ii] = fmaf((float)P[q][ii], S[q][ii], acc[i][j0 + q][ii]);
+              for (int ii = 0; ii < 4; ++ii) acc[i][j0 + q][ii] = fmaf(S[q][ii], Pf[ii], acc[i][j0 + q][ii]);
+            }
           }
+        }
       } else {
         // Per row tile: its TN scale MFMAs, then its TN integer MFMAs, then
         // the conversions and FMAs -- grouping MFMAs of one kind avoids the
@@ -1116,16 +1155,19 @@ __global__ __launch_bounds__(WM * WN * KS * 64, OCC) void gemm_tiled_kernel(Gemm
         // tile no longer wait right behind the MFMA that feeds them.
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
+          const v4i Ae = expand_group(Ar[i][0], Ar[i][1]);
           v4f S[TN];
           v4i P[TN];
 #pragma unroll
           for (int j = 0; j < TN; ++j) S[j] = scale_tile(sxw[i], sww[j], h);
 #pragma unroll
-          for (int j = 0; j < TN; ++j) P[j] = mfma_i8_16x16x64(Ae[i], Be[j], v4i{0, 0, 0, 0});
+          for (int j = 0; j < TN; ++j) P[j] = mfma_i8_16x16x64(Ae, Be[j], kOffset);
 #pragma unroll
-          for (int j = 0; j < TN; ++j)
+          for (int j = 0; j < TN; ++j) {
+            const v4f Pf = __builtin_bit_cast(v4f, P[j]);   // whole-vector cast (see above)
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) acc[i][j][ii] = fmaf((float)P[j][ii], S[j][ii], acc[i][j][ii]);
+            for (int ii = 0; ii < 4; ++ii) acc[i][j][ii] = fmaf(S[j][ii], Pf[ii], acc[i][j][ii]);
+          }
         }
       }
     }
@@ -1155,11 +1197,11 @@ __global__ __launch_bounds__(WM * WN * KS * 64, OCC) void gemm_tiled_kernel(Gemm
 
   if constexpr (kLean) load_epilogue_operands();
 
-  // acc holds 256 * main (the int8 operands carry 16 q each)
+  // acc holds main * 2^-14 (see kOffsetBits)
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] *= (1.0f / 256.0f);
+    for (int j = 0; j < TN; ++j) acc[i][j] *= 16384.0f;
 
   // LoRA-up of tile (i, j): lora_act rows of row tile i (partials summed in
   // order, split into fp16 hi + lo) times the L_up fragment of column tile j,

@@ -282,7 +282,7 @@ def mlp_gate_up(args, W, torch, np, workloads):
         W.w4a4_quantize_act(M, K, 2 * R, x, layer.wblob, act, stream=cs)
 
     def fused_gemm(i, cs):
-        W.w4a4_linear_glu(M, 2 * N, K, 2 * R, act, layer.wblob, h, stream=cs)
+        W.w4a4_linear_glu(M, 2 * N, K, 2 * R, R, act, layer.wblob, h, stream=cs)
 
     def fused(i, cs):
         fused_quant(i, cs)

@@ -164,14 +164,17 @@ int w4a4_linear(int64_t M, int64_t N, int64_t K, int32_t R, const void* act,
  * L_down_up] ([K][Rg + Ru]) and the L_up rows of a gate row being
  * [L_up_gate row, 0], of an up row [0, L_up_up row] (so the low-rank term of
  * each half is exactly its own layer's); a and b interleaved the same way.
- * N = 2 * (columns of each layer), N % 32 == 0; R = Rg + Ru.
+ * N = 2 * (columns of each layer), N % 32 == 0; R = Rg + Ru; r_gate = Rg,
+ * 0 <= r_gate <= R: the kernel skips the 16-wide rank blocks of L_up that the
+ * block-diagonal packing makes zero for a half (a wrong r_gate drops LoRA
+ * terms; r_gate only steers that skip, it is not checked against wblob).
  * y: fp16 [M][ldy], ldy >= N/2, ldy % 8 == 0, 16-byte aligned:
  *     y[m][c] = fp16(SiLU(g) * u),  g = gate layer's fp16 output (m, c),
  *                                   u = up layer's fp16 output (m, c),
  * SiLU in fp32 with the hardware exponential and reciprocal (relative error
  * about 1e-6 before the fp16 rounding).  Other arguments and errors as w4a4_linear
- * (W4A4_ERR_SHAPE also if N % 32 != 0). */
-int w4a4_linear_glu(int64_t M, int64_t N, int64_t K, int32_t R, const void* act,
+ * (W4A4_ERR_SHAPE also if N % 32 != 0 or r_gate is outside [0, R]). */
+int w4a4_linear_glu(int64_t M, int64_t N, int64_t K, int32_t R, int32_t r_gate, const void* act,
                     const void* wblob, uint16_t* y, int64_t ldy, void* stream);
 
 /* Which GEMM kernel w4a4_linear runs for a shape (host-only):

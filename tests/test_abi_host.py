@@ -115,15 +115,18 @@ def test_validation_errors_before_any_launch():
     assert lib.w4a4_linear(0, 64, 128, 16, None, None, None, 64, None) == 0
     assert lib.w4a4_linear(-1, 64, 128, 16, FAKE, FAKE, FAKE, 64, None) == 2
     # gated linear: N not whole (gate, up) tile pairs, ldy below N/2, NULL y,
-    # misaligned y, y overlapping a blob, M == 0 no-op, rank above the maximum
-    assert lib.w4a4_linear_glu(4, 48, 128, 16, FAKE, FAKE, FAKE, 24, None) == 2
-    assert lib.w4a4_linear_glu(4, 64, 128, 16, FAKE, FAKE, FAKE, 16, None) == 2
-    assert lib.w4a4_linear_glu(4, 64, 128, 16, FAKE, FAKE, None, 32, None) == 1
-    assert lib.w4a4_linear_glu(4, 64, 128, 16, FAKE, FAKE, FAKE + 2, 32, None) == 3
-    assert lib.w4a4_linear_glu(4, 64, 128, 16, FAKE, FAKE, FAKE, 36, None) == 3
-    assert lib.w4a4_linear_glu(4, 64, 128, 16, FAKE, FAKE * 4, FAKE, 32, None) == 4
-    assert lib.w4a4_linear_glu(0, 64, 128, 16, None, None, None, 32, None) == 0
-    assert lib.w4a4_linear_glu(4, 64, 128, 80, FAKE, FAKE, FAKE, 32, None) == 2
+    # misaligned y, y overlapping a blob, M == 0 no-op, rank above the maximum,
+    # gate rank outside [0, R]
+    assert lib.w4a4_linear_glu(4, 48, 128, 16, 8, FAKE, FAKE, FAKE, 24, None) == 2
+    assert lib.w4a4_linear_glu(4, 64, 128, 16, 8, FAKE, FAKE, FAKE, 16, None) == 2
+    assert lib.w4a4_linear_glu(4, 64, 128, 16, 8, FAKE, FAKE, None, 32, None) == 1
+    assert lib.w4a4_linear_glu(4, 64, 128, 16, 8, FAKE, FAKE, FAKE + 2, 32, None) == 3
+    assert lib.w4a4_linear_glu(4, 64, 128, 16, 8, FAKE, FAKE, FAKE, 36, None) == 3
+    assert lib.w4a4_linear_glu(4, 64, 128, 16, 8, FAKE, FAKE * 4, FAKE, 32, None) == 4
+    assert lib.w4a4_linear_glu(0, 64, 128, 16, 8, None, None, None, 32, None) == 0
+    assert lib.w4a4_linear_glu(4, 64, 128, 80, 16, FAKE, FAKE, FAKE, 32, None) == 2
+    assert lib.w4a4_linear_glu(4, 64, 128, 16, 17, FAKE, FAKE, FAKE, 32, None) == 2
+    assert lib.w4a4_linear_glu(4, 64, 128, 16, -1, FAKE, FAKE, FAKE, 32, None) == 2
     # quantize: ldx < K, misaligned x, NULL act, missing weight blob with R > 0
     assert lib.w4a4_quantize_act(4, 128, 16, FAKE, 64, FAKE, FAKE, None) == 2
     assert lib.w4a4_quantize_act(4, 128, 16, FAKE + 8, 128, FAKE, FAKE, None) == 3

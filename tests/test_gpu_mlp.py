@@ -66,7 +66,7 @@ def _run_glu(x, gate, up, Rg, Ru, ldy=None):
     act = W.alloc_act_blob(M, K, layer.R)
     h = torch.full((max(M, 1), ldy), float("nan"), dtype=torch.float16, device="cuda")
     W.w4a4_quantize_act(M, K, layer.R, xd, layer.wblob, act)
-    W.w4a4_linear_glu(M, 2 * N, K, layer.R, act, layer.wblob, h, ldy=ldy)
+    W.w4a4_linear_glu(M, 2 * N, K, layer.R, layer.r_gate, act, layer.wblob, h, ldy=ldy)
     torch.cuda.synchronize()
     return h.cpu().numpy()
 
@@ -82,12 +82,15 @@ def _cases(M, K, N, Rg, Ru, seed):
                                          (16, 4096, 1024, 32, 32), (12, 1536, 272, 16, 16),
                                          (17, 384, 48, 0, 0), (40, 384, 80, 16, 16),
                                          (130, 3072, 48, 32, 16), (300, 1024, 208, 32, 32),
-                                         (3, 8192, 2048, 32, 32), (9, 8192, 2048, 16, 16)])
+                                         (3, 8192, 2048, 32, 32), (9, 8192, 2048, 16, 16),
+                                         (24, 1024, 64, 8, 8), (5, 1024, 64, 8, 24), (40, 512, 96, 24, 8)])
 def test_glu_layer_against_oracle(M, K, N, Rg, Ru):
     """h = fp16(SiLU(g) * u) within the layer tolerance (taken on h) of the
     oracle's separate gate and up layers; decode (M <= 16) and tiled (M > 16)
     kernels, ragged row counts, either projection without LoRA, unequal
-    ranks, column counts that are and are not multiples of 64."""
+    ranks (also ranks that share a 16-wide rank block of the packed L_up,
+    where no block can be skipped), column counts that are and are not
+    multiples of 64."""
     x, g, u = _cases(M, K, N, Rg, Ru, seed=5000 + M + K + N + Rg)
     _say(f"[glu] M={M} K={K} N={N} Rg={Rg} Ru={Ru} -> variant {W.w4a4_query_variant(M, 2 * N, K, Rg + Ru)}")
     h = _run_glu(x, g, u, Rg, Ru)

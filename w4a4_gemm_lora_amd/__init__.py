@@ -83,7 +83,7 @@ def load_library() -> ctypes.CDLL:
     lib.w4a4_quantize_act_rmsnorm.argtypes = [_i64, _i64, _i32, _vp, _i64, _vp, ctypes.c_double,
                                               _vp, _vp, _vp]
     lib.w4a4_linear.argtypes = [_i64, _i64, _i64, _i32, _vp, _vp, _vp, _i64, _vp]
-    lib.w4a4_linear_glu.argtypes = [_i64, _i64, _i64, _i32, _vp, _vp, _vp, _i64, _vp]
+    lib.w4a4_linear_glu.argtypes = [_i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _i64, _vp]
     lib.w4a4_query_variant.argtypes = [_i64, _i64, _i64, _i32]
     lib.w4a4_layer_graph_create.argtypes = [_i64, _i64, _i64, _i32, _vp, _i64, _vp, ctypes.c_double,
                                             _vp, _vp, _vp, _i64, ctypes.POINTER(_vp)]
@@ -185,9 +185,10 @@ def w4a4_linear(M, N, K, R, act, wblob, y, ldy=None, stream=None):
     _check(st, "w4a4_linear")
 
 
-def w4a4_linear_glu(M, N, K, R, act, wblob, y, ldy=None, stream=None):
+def w4a4_linear_glu(M, N, K, R, r_gate, act, wblob, y, ldy=None, stream=None):
     ldy = N // 2 if ldy is None else ldy
-    st = load_library().w4a4_linear_glu(M, N, K, R, _ptr(act), _ptr(wblob), _ptr(y), ldy, _stream(stream))
+    st = load_library().w4a4_linear_glu(M, N, K, R, r_gate, _ptr(act), _ptr(wblob), _ptr(y), ldy,
+                                        _stream(stream))
     _check(st, "w4a4_linear_glu")
 
 
@@ -265,6 +266,7 @@ class GatedMLPUp:
         rg = 0 if lora_down_gate is None else lora_down_gate.shape[1]
         ru = 0 if lora_down_up is None else lora_down_up.shape[1]
         self.R = rg + ru
+        self.r_gate = rg
         ld = lu = None
         if self.R:
             parts = [t for t in (lora_down_gate, lora_down_up) if t is not None]
@@ -293,7 +295,7 @@ class GatedMLPUp:
         if h is None:
             h = torch.empty((M, self.N), dtype=torch.float16, device=x.device)
         w4a4_quantize_act(M, self.K, self.R, x, self.wblob, act, stream=stream)
-        w4a4_linear_glu(M, 2 * self.N, self.K, self.R, act, self.wblob, h, stream=stream)
+        w4a4_linear_glu(M, 2 * self.N, self.K, self.R, self.r_gate, act, self.wblob, h, stream=stream)
         return h
 
 

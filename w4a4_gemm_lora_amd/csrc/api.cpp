@@ -216,10 +216,12 @@ static int make_gemm_args(int64_t M, int64_t N, int64_t K, int32_t R, const void
 
 // y holds N columns, or N/2 for the gated output (one per (gate, up) pair).
 static int linear_impl(int64_t M, int64_t N, int64_t K, int32_t R, const void* act,
-                       const void* wblob, uint16_t* y, int64_t ldy, void* stream, bool glu) {
+                       const void* wblob, uint16_t* y, int64_t ldy, void* stream, bool glu,
+                       int32_t r_gate = 0) {
   int st = check_nkr(N, K, R);
   if (st) return st;
   if (glu && N % 32 != 0) return W4A4_ERR_SHAPE;   // whole (gate, up) tile pairs
+  if (glu && (r_gate < 0 || r_gate > R)) return W4A4_ERR_SHAPE;
   if ((st = check_m(M))) return st;
   if (M == 0) return W4A4_OK;
   if (!y) return W4A4_ERR_NULL;
@@ -229,6 +231,8 @@ static int linear_impl(int64_t M, int64_t N, int64_t K, int32_t R, const void* a
   GemmArgs a;
   if ((st = make_gemm_args(M, N, K, R, act, wblob, y, ldy, &a, ycols))) return st;
   a.glu = glu ? 1 : 0;
+  a.glu_tlo = r_gate / 16;          // up tiles: blocks wholly at or past r_gate
+  a.glu_thi = (r_gate + 15) / 16;   // gate tiles: blocks that reach below r_gate
   const int v = choose_variant(M, N, K, R);
   if (log_enabled())
     std::fprintf(stderr, "%s M=%lld N=%lld K=%lld R=%d -> %s\n", glu ? "w4a4_linear_glu" : "w4a4_linear",
@@ -241,9 +245,9 @@ int w4a4_linear(int64_t M, int64_t N, int64_t K, int32_t R, const void* act,
   return linear_impl(M, N, K, R, act, wblob, y, ldy, stream, false);
 }
 
-int w4a4_linear_glu(int64_t M, int64_t N, int64_t K, int32_t R, const void* act,
+int w4a4_linear_glu(int64_t M, int64_t N, int64_t K, int32_t R, int32_t r_gate, const void* act,
                     const void* wblob, uint16_t* y, int64_t ldy, void* stream) {
-  return linear_impl(M, N, K, R, act, wblob, y, ldy, stream, true);
+  return linear_impl(M, N, K, R, act, wblob, y, ldy, stream, true, r_gate);
 }
 
 int w4a4_query_variant(int64_t M, int64_t N, int64_t K, int32_t R) {

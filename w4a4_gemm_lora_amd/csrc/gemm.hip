@@ -505,6 +505,8 @@ __global__ __launch_bounds__(64 * DW, 16 / DW) void gemm_decode_kernel(GemmArgs 
           split_f16(l4, hi, lo);
 #pragma unroll
           for (int n = 0; n < NTW; ++n) {
+            // gated pair (n = 0 gate, 1 up): skip the other half's zero blocks
+            if (GLU && ((n & 1) ? t < g.glu_tlo : t >= g.glu_thi)) continue;
             a_lora[n] = mfma_f16_16x16x16(hi, lup[n][t], a_lora[n]);
             a_lora[n] = mfma_f16_16x16x16(lo, lup[n][t], a_lora[n]);
           }
@@ -795,6 +797,8 @@ __global__ __launch_bounds__(64 * DW, 16 / DW) void gemm_decode_dot_kernel(GemmA
           split_f16(l4, hi, lo);
 #pragma unroll
           for (int n = 0; n < NT; ++n) {
+            // gated pair (n = 0 gate, 1 up): skip the other half's zero blocks
+            if (GLU && ((n & 1) ? t < g.glu_tlo : t >= g.glu_thi)) continue;
             a_lora[n] = mfma_f16_16x16x16(hi, lup[n][t], a_lora[n]);
             a_lora[n] = mfma_f16_16x16x16(lo, lup[n][t], a_lora[n]);
           }
@@ -1017,6 +1021,14 @@ __global__ __launch_bounds__(WM * WN * KS * 64, OCC) void gemm_tiled_kernel(Gemm
   constexpr int RTL = RT > 0 ? RT : 1;
   v4h lu_f[TN][RTL];
   float af[TN], bf[TN];
+  // Gated layer: the wave's column tiles alternate gate (even j), up (odd
+  // j), and rank blocks wholly inside the other projection's half of the
+  // block-diagonal L_up are zero: not multiplied (still loaded, so that the
+  // number of epilogue loads stays fixed, see kEpiLoads).
+  auto block_used = [&](int j, int t) -> bool {
+    if constexpr (GLU) return (j & 1) ? t >= g.glu_tlo : t < g.glu_thi;
+    return true;
+  };
   auto load_epilogue_operands = [&]() {
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
@@ -1040,7 +1052,7 @@ __global__ __launch_bounds__(WM * WN * KS * 64, OCC) void gemm_tiled_kernel(Gemm
       const size_t part = (size_t)round_up16(g.M) * g.R;   // floats per partial
 #pragma unroll
       for (int j = 0; j < SPL; ++j) {
-        if (j < g.ks) {   // uniform
+        if (j == 0 || j < g.ks) {   // uniform; partial 0 always exists (and kEpiLoads counts it)
 #pragma unroll
           for (int i = 0; i < TM; ++i) {
             const int64_t mt = tile_index(wm * TM + i);
@@ -1058,13 +1070,26 @@ __global__ __launch_bounds__(WM * WN * KS * 64, OCC) void gemm_tiled_kernel(Gemm
     if (s < KP) issue_copy(s, s);
 
 
+  // Loads of the epilogue operands issued at k-pair 0 right after that
+  // iteration's copies (not lean): younger than the copies of stages 1 ..
+  // NS-1, so the waits for those stages leave them in flight as well.  Loads
+  // complete in issue order, so the count is what the wait may leave
+  // outstanding; the conditional lora_act partials (split index >= 1) are
+  // not counted -- more younger loads than counted only make a wait longer.
+  constexpr int kEpiLoads = kLean ? 0 : 2 * TN + TN * RT + ((!kLateLora && RT > 0) ? TM * RT : 0);
+  static_assert(2 * OPS + kEpiLoads <= 63, "vmcnt counts to 63");
   int st = 0;                      // == p % NS
   int st_next = (NS - 1) % NS;     // == (p + NS - 1) % NS
   for (int64_t p = 0; p < KP; ++p) {
     // stages issued after p and still allowed in flight
     const int64_t after = (KP - 1 - p) < (NS - 2) ? (KP - 1 - p) : (NS - 2);
     asm volatile("" ::: "memory");
-    if constexpr (NS >= 4) {
+    if (kEpiLoads > 0 && p >= 1 && p <= NS - 1) {
+      // the epilogue loads are younger than stage p
+      if (after >= 2) W4A4_WAIT_VMCNT(2 * OPS + kEpiLoads);
+      else if (after == 1) W4A4_WAIT_VMCNT(OPS + kEpiLoads);
+      else W4A4_WAIT_VMCNT(kEpiLoads);
+    } else if constexpr (NS >= 4) {
       if (after >= 2) W4A4_WAIT_VMCNT(2 * OPS);
       else if (after == 1) W4A4_WAIT_VMCNT(OPS);
       else W4A4_WAIT_VMCNT(0);
@@ -1083,10 +1108,10 @@ __global__ __launch_bounds__(WM * WN * KS * 64, OCC) void gemm_tiled_kernel(Gemm
     asm volatile("" ::: "memory");
     if (p + NS - 1 < KP) issue_copy(st_next, p + NS - 1);
     if constexpr (!kLean) {
-      // younger than the copies of stages 1.. issued so far: a later wait
-      // that lets the copies issued after its stage stay in flight finds
-      // these among them, so it completes its stage all the same
+      // after every copy of stages <= NS-1 (the fence keeps the compiler
+      // from moving these loads ahead of the copies: kEpiLoads relies on it)
       if (p == 0) {
+        asm volatile("" ::: "memory");
         load_epilogue_operands();
         load_lora_partials();
       }
@@ -1221,6 +1246,7 @@ __global__ __launch_bounds__(WM * WN * KS * 64, OCC) void gemm_tiled_kernel(Gemm
         split_f16(l4, hi, lo);
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
+          if (!block_used(j, t)) continue;
           acc[i][j] = mfma_f16_16x16x16(hi, lu_f[j][t], acc[i][j]);
           acc[i][j] = mfma_f16_16x16x16(lo, lu_f[j][t], acc[i][j]);
         }
@@ -1231,6 +1257,7 @@ __global__ __launch_bounds__(WM * WN * KS * 64, OCC) void gemm_tiled_kernel(Gemm
     if constexpr (!kLateLora) {
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
+        if (!block_used(j, t)) continue;
         v4f l4 = la_p[0][i][t];
 #pragma unroll
         for (int jj = 1; jj < SPL; ++jj)

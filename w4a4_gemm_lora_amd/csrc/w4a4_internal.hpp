@@ -123,6 +123,10 @@ struct GemmArgs {
   // gate columns 16j.., tile 2j+1 the up columns 16j.. -- and y gets
   // h = fp16(SiLU(gate) * up) with N/2 columns instead of the N columns.
   int glu = 0;
+  // gated layer: rank blocks [0, glu_thi) can carry the gate projection's
+  // L_up and [glu_tlo, R/16) the up projection's (blocks wholly inside the
+  // other half are zero by the packing and are skipped)
+  int glu_tlo = 0, glu_thi = 0;
 };
 
 enum Variant { kGeneric = 0, kDecode = 1, kPrefill = 2 };

@@ -42,11 +42,17 @@ COPY_BYTES = 256 << 20      # the calibration copy moves this many bytes each wa
 
 
 def kernel_source_hash() -> str:
+    """Hash of the GEMM kernels' code: the sources with their // comments and
+    blank lines removed, so that an edit of a comment keeps the measured
+    counters valid while any change to the code itself invalidates them."""
     import hashlib
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            for line in f:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

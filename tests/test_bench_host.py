@@ -50,3 +50,21 @@ def test_traffic_record_is_ignored_once_the_kernels_change(tmp_path, monkeypatch
     f.write_text(json.dumps({"w": rec}))
     assert bench.measured_traffic("w") is None
     assert bench.measured_traffic("missing") is None
+
+
+def test_kernel_hash_ignores_comments_but_not_code(tmp_path, monkeypatch):
+    """Comment-only edits of the kernel sources keep committed counters valid;
+    any change to a line of code invalidates them."""
+    import shutil
+    for rel in bench.KERNEL_SOURCES:
+        dst = tmp_path / rel
+        dst.parent.mkdir(parents=True, exist_ok=True)
+        shutil.copy(os.path.join(bench.ROOT, rel), dst)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    base = bench.kernel_source_hash()
+    gemm = tmp_path / bench.KERNEL_SOURCES[0]
+    text = gemm.read_text()
+    gemm.write_text(text.replace("namespace w4a4 {", "namespace w4a4 {   // a new comment\n\n// and another", 1))
+    assert bench.kernel_source_hash() == base
+    gemm.write_text(text.replace("kTileGroupRows = 8", "kTileGroupRows = 4", 1))
+    assert bench.kernel_source_hash() != base

@@ -4,8 +4,11 @@
 One step = one pass of the whole hot path over one batch already resident in
 HBM: w4a4_quantize_act (int4 codes + scales + LoRA-down) followed by
 w4a4_linear (integer MFMA GEMM + per-group dequant + LoRA-up + affine).
-Default workload: the MLP up-projection at a 700-token batch
-(M=700, K=1024, N=3072, LoRA rank 32, group 64), seeded synthetic inputs.
+Default workload: the large prefill layer (M=8192, K=4096, N=4096, LoRA rank
+32, group 64), seeded synthetic inputs; the same line also carries the
+decode sweep (M = 1, 4, 16 at K=4096, N=14336, weights streamed from HBM),
+the measured int8-MFMA and HBM-read peaks beside the published ones, and the
+CPU oracle timed on the host.
 
 Prints ONE JSON line (rank 0, N=1 only).  Per-kernel durations come from HIP
 events recorded on the stream the kernels are launched on.
@@ -25,9 +28,12 @@ if ROOT not in sys.path:
 METRIC = "W4A4+LoRA linear TOPS & HBM GB/s at 1 GPU; % of roofline per shape"
 PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA, 10^12 ops/s
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
-# VALU issue peak: the published fp32 vector rate (157.3 TFLOP/s, an FMA is 2
-# flops) in lane-operations: 256 CUs x 4 SIMDs x 32 lanes x 2.4 GHz
-PEAK_VALU_TLANEOPS = 78.6
+# VALU issue peak for the unpacked 32-bit operations this code issues: a
+# wave64 op takes 4 cycles of a SIMD (16 lanes per clock, measured: ~4.2
+# cycles per dependent-free v_fma_f32 with 2-4 waves per SIMD), so 256 CUs x
+# 4 SIMDs x 16 lanes x 2.4 GHz.  The published 157.3 TFLOP/s fp32 vector rate
+# counts packed two-wide FMAs, which this build does not use.
+PEAK_VALU_TLANEOPS = 39.3
 CLOCK_GHZ = 2.4             # peak engine clock the utilisation fractions are taken against
 N_SIMDS = 1024
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
@@ -342,28 +348,131 @@ def algorithmic_counts(M, N, K, R):
                 layer_ops=2 * M * N * K + 2 * M * R * (K + N))
 
 
-def cpu_baseline(case, budget_s=10.0):
-    """The oracle, as it stands, on the same workload: whole layers repeated
-    until about budget_s seconds of CPU time have been spent."""
+def _oracle_layer(case, rows=None):
     from oracle import w4a4_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = 1
-    n, t0 = 0, time.perf_counter()
+    O.linear(case["x"], case["lora_down"], case["lora_up"], case["col_scale"], case["bias"], w16=case["w"],
+             rows=rows)
+
+
+def cpu_baseline(case, target_s=8.0):
+    """The oracle, as it stands, on the same workload, on this host's cores:
+    with all the cores the process may use (its BLAS pool at that size) on
+    a row slice grown until it takes about target_s, and with one thread on
+    a 256-row slice (or the whole layer if smaller), each scaled to the
+    whole layer's operations; the one-thread whole-layer time is an
+    extrapolation and is labelled so."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    cores = len(os.sched_getaffinity(0))
+    M = case["M"]
+    c = algorithmic_counts(M, case["N"], case["K"], case["R"])
+
+    def timed(rows_n, threads):
+        rows = None if rows_n >= M else np.arange(rows_n)
+        with threadpool_limits(limits=threads):
+            t0 = time.perf_counter()
+            _oracle_layer(case, rows)
+            return time.perf_counter() - t0
+
+    # all cores: whole layers if one takes under target_s, else a row slice
+    rows_n, el = min(M, 256), 0.0
     while True:
-        O.linear(case["x"], case["lora_down"], case["lora_up"], case["col_scale"], case["bias"],
-                 w16=case["w"])
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or n >= 1000:
+        el = timed(rows_n, cores)
+        if el >= target_s or rows_n >= M:
             break
-    c = algorithmic_counts(case["M"], case["N"], case["K"], case["R"])
-    return {"value": round(c["layer_ops"] * n / el / 1e12, 6), "unit": "TOPS", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"{n} full-layer oracle evaluations (M={case['M']} K={case['K']} N={case['N']} "
-                      f"R={case['R']}), numpy fp64 + BLAS, {el:.1f} s wall"}
+        rows_n = min(M, max(rows_n * 2, int(rows_n * target_s / max(el, 1e-3))))
+    reps = 1
+    if rows_n >= M and el < target_s:   # small layers: repeat whole evaluations
+        reps = max(1, int(target_s / max(el, 1e-3)))
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            timed(M, cores)
+        el = time.perf_counter() - t0
+    ops_all = c["layer_ops"] * (rows_n / M) * reps
+    one_rows = min(M, 256)
+    el1 = timed(one_rows, 1)
+    full1 = el1 * M / one_rows
+    sample = (f"{reps} whole-layer oracle evaluations" if rows_n >= M else
+              f"oracle on rows 0..{rows_n - 1} of the M={M} layer (each row of X is quantized on its own, so a "
+              f"row slice is the same computation), scaled to the layer's {c['layer_ops']:.4g} ops") + \
+        f"; numpy fp64 + BLAS with {cores} threads, {el:.1f} s wall"
+    return {"value": round(ops_all / el / 1e12, 6), "unit": "TOPS", "cores": cores, "kind": "oracle",
+            "sample": sample,
+            "one_thread": {"value": round(c["layer_ops"] * (one_rows / M) / el1 / 1e12, 6), "unit": "TOPS",
+                           "slice_rows": one_rows, "slice_s": round(el1, 2),
+                           "whole_layer_s": round(full1, 1),
+                           "whole_layer_s_is": "extrapolated" if one_rows < M else "measured"}}
+
+
+def measured_peaks(torch, W):
+    """Attainable int8 MFMA and HBM read rates of this GPU (libw4a4_peaks.so):
+    the best of 5 timed launches each, events on the launch stream."""
+    lib = W.load_peaks_library()
+    s = torch.cuda.current_stream()
+    out = torch.empty(max(lib.w4a4_peak_i8_mfma_out_ints(), lib.w4a4_peak_hbm_read_out_ints()),
+                      dtype=torch.int32, device="cuda")
+    iters = 20000
+    nbytes = 2 << 30   # 2 GiB: 8x the last-level cache
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(7)
+
+    def best_ms(fn):
+        fn()
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            fn()
+            e1.record(s)
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1))
+        return best
+
+    def mfma():
+        if lib.w4a4_peak_i8_mfma(iters, out.data_ptr(), s.cuda_stream):
+            raise RuntimeError("w4a4_peak_i8_mfma failed")
+
+    def hbm():
+        if lib.w4a4_peak_hbm_read(buf.data_ptr(), nbytes, out.data_ptr(), s.cuda_stream):
+            raise RuntimeError("w4a4_peak_hbm_read failed")
+
+    t_m, t_h = best_ms(mfma), best_ms(hbm)
+    del buf
+    return {"int8_mfma": {"unit": "TOPS", "published": PEAK_INT8_TOPS,
+                          "measured": round(lib.w4a4_peak_i8_mfma_ops(iters) / (t_m * 1e-3) / 1e12, 1)},
+            "hbm_read": {"unit": "GB/s", "published": PEAK_HBM_GBPS,
+                         "measured": round(nbytes / (t_h * 1e-3) / 1e9, 1)}}
+
+
+def decode_sweep(torch, np, W, workloads, Ms=(1, 4, 16), rotate=12):
+    """The decode-shaped layer (K=4096, N=14336, R=32) at each M: w4a4_linear's
+    average launch time over a graph of 48 launches cycling through `rotate`
+    weight blobs (more bytes than the last-level cache, so weights stream
+    from HBM), algorithmic bytes / time against the HBM peak."""
+    res = {}
+    blobs = None
+    for M in Ms:
+        case = workloads.generate("decode", M=M)
+        K, N, R = case["K"], case["N"], case["R"]
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        if blobs is None:
+            blobs = []
+            for _ in range(rotate):
+                wb = W.alloc_weight_blob(N, K, R)
+                W.w4a4_pack_weights(N, K, R, wb, w_fp16=dev(case["w"]), lora_down=dev(case["lora_down"]),
+                                    lora_up=dev(case["lora_up"]), col_scale=dev(case["col_scale"]),
+                                    bias=dev(case["bias"]))
+                blobs.append(wb)
+        act = W.alloc_act_blob(M, K, R)
+        W.w4a4_quantize_act(M, K, R, dev(case["x"]), blobs[0], act)
+        y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        ms = graph_avg_ms(torch, lambda i, cs: W.w4a4_linear(M, N, K, R, act, blobs[i % rotate], y, stream=cs), 48)
+        c = algorithmic_counts(M, N, K, R)
+        gbps = c["lin_bytes"] / (ms * 1e-3) / 1e9
+        res[f"M={M}"] = {"linear_us": round(ms * 1e3, 3), "GBps": round(gbps, 1),
+                         "frac_of_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4), "algorithmic_bytes": c["lin_bytes"]}
+    return {"workload": "decode: W4A4+LoRA linear M in {1,4,16} K=4096 N=14336 R=32 group 64, "
+                        f"{rotate} weight blobs rotating", **res}
 
 
 def main(argv=None):
@@ -371,9 +480,11 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="mlp_up")
+    ap.add_argument("--workload", default="prefill")
     ap.add_argument("--m", type=int, default=None, help="row count override (decode sweep)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the measured peaks and the decode sweep (profiling runs)")
     ap.add_argument("--rotate", type=int, default=None,
                     help="distinct weight blobs cycled through (default: 12 for decode, so that the "
                          "weight stream comes from HBM and not the 256 MB MALL; 1 otherwise)")
@@ -600,6 +711,17 @@ def main(argv=None):
             "valu": {"bound": "valu", "achieved": round(lane_tops, 2), "peak": PEAK_VALU_TLANEOPS,
                      "unit": "T lane-ops/s", "frac": round(lane_tops / PEAK_VALU_TLANEOPS, 4)},
         }
+    if not args.no_extras:
+        peaks = measured_peaks(torch, W)
+        out["measured_peaks"] = peaks
+        meas = peaks["hbm_read"]["measured"] if out["roofline"]["bound"] == "hbm" else peaks["int8_mfma"]["measured"]
+        out["roofline"]["frac_of_measured_peak"] = round(out["roofline"]["achieved"] / meas, 4)
+        if args.workload != "decode":
+            sweep = decode_sweep(torch, np, W, workloads)
+            for v in sweep.values():
+                if isinstance(v, dict):
+                    v["frac_of_measured_hbm_read"] = round(v["GBps"] / peaks["hbm_read"]["measured"], 4)
+            out["decode_sweep"] = sweep
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(case)
     print(json.dumps(out), flush=True)

@@ -178,19 +178,35 @@ int w4a4_linear_glu(int64_t M, int64_t N, int64_t K, int32_t R, int32_t r_gate, 
                     const void* wblob, uint16_t* y, int64_t ldy, void* stream);
 
 /* Which GEMM kernel w4a4_linear runs for a shape (host-only):
- * 0 = generic, 1 = decode (M <= 16), 2 = prefill; -W4A4_ERR_SHAPE if the
+ * 1 = decode (M <= 16), 2 = prefill (tiled); -W4A4_ERR_SHAPE if the
  * shape is unsupported.  Lets a caller log the kernel chosen per layer
  * ("INT4 Kernel Architecture, in depth", section "Failure modes"). */
 int w4a4_query_variant(int64_t M, int64_t N, int64_t K, int32_t R);
 
-/* Diagnostic: the exact per-group integer sums P[m,n,g] of a window,
- * computed by the GEMM's own unpack + integer MFMA path.
- * out: int32 device buffer [mc][nc][K/64] (row-major).  m0, mc, n0, nc must be
- * multiples of 16 with m0 + mc <= Mp and n0 + nc <= N. */
+/* Diagnostic: the exact per-group integer sums P[m,n,g] ("W4A4 CUDA Kernel
+ * for Voice Clone", section 3.7: the int32 sum of each 64-group before the
+ * per-group dequant) of a window of the output.  The launch runs the same
+ * kernel, tile shape and variant that w4a4_linear runs for (M, N, K, R) --
+ * its loads, nibble expansion and integer products unchanged -- with only
+ * the per-group scale-accumulate swapped for a store of P, and no LoRA, affine
+ * or output (the LoRA rank only steers which kernel is chosen).  Rows of the
+ * window at or past M are padding and read 0.
+ * act, wblob: as for w4a4_linear.  out: int32 device buffer [mc][nc][K/64]
+ * (row-major), not overlapping act or wblob (else W4A4_ERR_ARG).  m0, mc,
+ * n0, nc must be multiples of 16 with m0 + mc <= Mp and n0 + nc <= N (else
+ * W4A4_ERR_SHAPE). */
 int w4a4_debug_group_psums(int64_t M, int64_t N, int64_t K, int32_t R,
                            const void* act, const void* wblob, int64_t m0,
                            int64_t mc, int64_t n0, int64_t nc, int32_t* out,
                            void* stream);
+
+/* The same for the kernel and tile shape w4a4_linear_glu runs for a gated
+ * layer of N packed columns (N % 32 == 0): P of the packed (interleaved gate
+ * / up) columns, before the gated activation. */
+int w4a4_debug_group_psums_glu(int64_t M, int64_t N, int64_t K, int32_t R,
+                               const void* act, const void* wblob, int64_t m0,
+                               int64_t mc, int64_t n0, int64_t nc, int32_t* out,
+                               void* stream);
 
 /* Captured forward passes ("W4A4 CUDA Kernel for Voice Clone", section 4:
  * launch overhead dominates decode-size calls, so the forward step is

@@ -16,10 +16,14 @@ pytestmark = pytest.mark.skipif(not os.path.exists(W.lib_path()),
                                 reason="libw4a4.so not built (run __graft_entry__.build())")
 
 
-def _declared():
-    src = open(os.path.join(ROOT, "include", "w4a4.h")).read()
+def _declared(header="w4a4.h"):
+    src = open(os.path.join(ROOT, "include", header)).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(w4a4_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_header_is_covered():
+    assert sorted(os.listdir(os.path.join(ROOT, "include"))) == ["w4a4.h", "w4a4_peaks.h"]
 
 
 def test_exports_every_declared_symbol():
@@ -30,6 +34,22 @@ def test_exports_every_declared_symbol():
         assert hasattr(lib, n), n
     assert W.w4a4_status_string(0) == "W4A4_OK"
     assert "SHAPE" in W.w4a4_status_string(2)
+
+
+def test_peaks_library_exports_every_declared_symbol():
+    lib = W.load_peaks_library()
+    names = _declared("w4a4_peaks.h")
+    assert set(names) == set(W.PEAKS_SYMBOLS), names
+    for n in names:
+        assert hasattr(lib, n), n
+    # host-only queries and argument checks (nothing is launched)
+    assert lib.w4a4_peak_i8_mfma_ops(10) == 512 * 4 * 8 * 10 * 2 * 16 * 16 * 64
+    assert lib.w4a4_peak_i8_mfma_out_ints() == 512 * 256
+    assert lib.w4a4_peak_hbm_read_out_ints() > 0
+    assert lib.w4a4_peak_i8_mfma(0, ctypes.c_void_p(1 << 20), None) == 4
+    assert lib.w4a4_peak_i8_mfma(1, None, None) == 4
+    assert lib.w4a4_peak_hbm_read(ctypes.c_void_p(1 << 20), 24, ctypes.c_void_p(1 << 20), None) == 4
+    assert lib.w4a4_peak_hbm_read(ctypes.c_void_p((1 << 20) + 8), 32, ctypes.c_void_p(1 << 20), None) == 4
 
 
 def test_no_unresolved_library_symbols():
@@ -169,11 +189,19 @@ def test_validation_errors_before_any_launch():
     assert lib.w4a4_debug_group_psums(20, 64, 128, 16, FAKE, FAKE, 8, 16, 0, 16, FAKE, None) == 2
     assert lib.w4a4_debug_group_psums(20, 64, 128, 16, FAKE, FAKE, 16, 32, 0, 16, FAKE, None) == 2
     assert lib.w4a4_debug_group_psums(20, 64, 128, 16, FAKE, FAKE, 0, 16, 64, 16, FAKE, None) == 2
+    assert lib.w4a4_debug_group_psums(20, 64, 128, 16, FAKE, FAKE, 0, 16, 0, 16, None, None) == 1
+    # the gated twin: also N % 32 (whole (gate, up) tile pairs)
+    assert lib.w4a4_debug_group_psums_glu(20, 48, 128, 16, FAKE, FAKE, 0, 16, 0, 16, FAKE, None) == 2
+    assert lib.w4a4_debug_group_psums_glu(20, 64, 128, 16, FAKE, FAKE, 8, 16, 0, 16, FAKE, None) == 2
+    # the window must not overlap the blobs
+    _, _ = W.w4a4_weight_layout(64, 128, 16)
+    assert lib.w4a4_debug_group_psums(20, 64, 128, 16, FAKE, FAKE + 1024 * 1024, 0, 16, 0, 16, FAKE + 256,
+                                      None) == 4
 
 
 def test_query_variant_is_host_only():
     for M in (1, 4, 16, 700, 8192):
-        assert W.w4a4_query_variant(M, 4096, 4096, 32) in (0, 1, 2)
+        assert W.w4a4_query_variant(M, 4096, 4096, 32) == (1 if M <= 16 else 2)
 
 
 def test_library_shares_torch_hip_runtime():

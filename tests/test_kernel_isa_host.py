@@ -1,5 +1,6 @@
-"""Check the generated gfx950 code of the tiled GEMM for the invariant its
-k-pair waits rely on (no GPU; compiles gemm.hip to assembly with hipcc).
+"""Checks of the generated gfx950 code (no GPU; compiles the kernels to
+assembly with hipcc): the invariant the tiled GEMM's k-pair waits rely on,
+and the register / LDS / scratch budget of every kernel instance.
 
 The non-lean tiled kernel issues its epilogue-operand loads at k-pair 0
 right behind that iteration's LDS copies, and the waits for stages 1 .. NS-1
@@ -19,7 +20,7 @@ import pytest
 from w4a4_gemm_lora_amd import build as B
 
 NAME = re.compile(r"^(_ZN4w4a417gemm_tiled_kernelI\S*):")
-ARGS = re.compile(r"ILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELb(\d)ELi(\d+)ELi(\d+)E")
+ARGS = re.compile(r"ILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELb(\d)ELi(\d+)ELi(\d+)ELb(\d)E")
 
 
 def _epilogue_loads(wm, wn, tm, tn, rt, spl):
@@ -27,22 +28,37 @@ def _epilogue_loads(wm, wn, tm, tn, rt, spl):
     return 2 * tn + tn * rt + (tm * rt if (not late and rt > 0) else 0)
 
 
-@pytest.mark.skipif(shutil.which(B.HIPCC) is None and not os.path.exists(B.HIPCC), reason="hipcc not installed")
-def test_epilogue_loads_follow_the_first_copies(tmp_path):
-    out = tmp_path / "gemm.s"
-    cmd = [B.HIPCC] + B.COMMON + ["-x", "hip", "--cuda-device-only", "-S",
-                                  os.path.join(B.CSRC, "gemm.hip"), "-o", str(out)]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    assert r.returncode == 0, r.stderr[-2000:]
-    lines = out.read_text().split("\n")
+HAVE_HIPCC = shutil.which(B.HIPCC) is not None or os.path.exists(B.HIPCC)
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    """gfx950 assembly of each .hip source, compiled once for this module."""
+    if not HAVE_HIPCC:
+        pytest.skip("hipcc not installed")
+    d = tmp_path_factory.mktemp("asm")
+    out = {}
+    for src in ("gemm.hip", "quantize.hip"):
+        o = d / (src + ".s")
+        cmd = [B.HIPCC] + B.COMMON + ["-x", "hip", "--cuda-device-only", "-S", os.path.join(B.CSRC, src), "-o", str(o)]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr[-2000:]
+        out[src] = o.read_text()
+    return out
+
+
+def test_epilogue_loads_follow_the_first_copies(asm):
+    lines = asm["gemm.hip"].split("\n")
     checked = 0
     for i, line in enumerate(lines):
         m = NAME.match(line)
         if not m:
             continue
-        wm, wn, tm, tn, rt, ns, spl, glu, occ, ks = map(int, ARGS.search(m.group(1)).groups())
+        wm, wn, tm, tn, rt, ns, spl, glu, occ, ks, psum = map(int, ARGS.search(m.group(1)).groups())
         if occ >= 3:
             continue   # the lean variant loads its epilogue operands after the loop
+        if psum:
+            continue   # the diagnostic instances load no epilogue operands
         body = []
         for t in lines[i + 1:]:
             if t.startswith(".Lfunc_end"):
@@ -61,3 +77,75 @@ def test_epilogue_loads_follow_the_first_copies(tmp_path):
         assert want in waits or ops + want in waits or 2 * ops + want in waits, m.group(1)
         checked += 1
     assert checked >= 100   # every non-lean instance of every tile shape, rank and variant
+
+
+# ---------------------------------------------------------------------------
+# Resource budget of every kernel instance ("High-Performance Kernel Design for
+# W4A4 ... on Blackwell", sections 4-5: a pipeline depth that overruns the
+# on-chip budget fails silently as lost performance, so the budget is checked,
+# not assumed).  gfx950: 512 VGPRs (arch + accumulation, 8-register granules)
+# per SIMD lane shared by the waves on it, 160 KiB of LDS per CU.
+KDESC = re.compile(r"^\s*\.amdhsa_kernel (\S+)$")
+TILED = re.compile(r"gemm_tiled_kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELb(\d)"
+                   r"ELi(\d+)ELi(\d+)ELb(\d)E")
+DECODE = re.compile(r"gemm_decode_(?:dot_)?kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELb(\d)ELi(\d+)ELb(\d)E")
+LDS_PER_CU = 160 * 1024
+
+
+def _descriptors(text):
+    """{kernel name: {field: int}} from the .amdhsa_kernel blocks."""
+    out, cur = {}, None
+    for line in text.split("\n"):
+        m = KDESC.match(line)
+        if m:
+            cur = out.setdefault(m.group(1), {})
+            continue
+        if cur is not None:
+            t = line.split()
+            if t and t[0] == ".end_amdhsa_kernel":
+                cur = None
+            elif len(t) == 2 and t[0].startswith(".amdhsa_"):
+                cur[t[0][len(".amdhsa_"):]] = int(t[1])
+    return out
+
+
+def _waves_per_simd(d):
+    regs = (d["next_free_vgpr"] + 7) // 8 * 8
+    return min(8, 512 // regs)
+
+
+def test_every_instance_fits_its_occupancy(asm):
+    """No instance uses scratch (spills or private arrays), and each fits
+    the occupancy its launch bounds promise.  The bound's second argument is
+    a minimum of waves per SIMD (the compiler's register budget is 512 / it):
+    a tiled instance built for OCC (WM x WN x KS waves per workgroup, KS / 1
+    or 2 waves of it on each SIMD) must keep OCC waves on every SIMD by
+    registers and OCC / (WM WN KS / 4) workgroups per CU by LDS; a decode
+    instance (DW waves, bound 16 / DW) keeps 4 waves per SIMD.  The
+    diagnostic (group-sum) instances are built for one workgroup per CU and
+    checked against that."""
+    seen = {"tiled": 0, "decode": 0, "other": 0}
+    for src, text in asm.items():
+        for name, d in _descriptors(text).items():
+            assert d["private_segment_fixed_size"] == 0, f"{name}: {d['private_segment_fixed_size']} B of scratch"
+            lds = d["group_segment_fixed_size"]
+            m = TILED.search(name)
+            if m:
+                wm, wn, tm, tn, rt, ns, spl, glu, occ, ks, psum = map(int, m.groups())
+                per_wg = max(1, wm * wn * ks // 4)   # waves of one workgroup on each SIMD
+                want = max(per_wg, 1 if psum else occ)
+                assert _waves_per_simd(d) >= want, (name, d["next_free_vgpr"], want)
+                assert (want // per_wg) * lds <= LDS_PER_CU, (name, lds, want)
+                seen["tiled"] += 1
+                continue
+            m = DECODE.search(name)
+            if m:
+                dw, psum = int(m.group(6)), int(m.group(7))
+                blocks = 1 if psum else 16 // dw
+                assert _waves_per_simd(d) >= max(1, blocks * dw // 4), (name, d["next_free_vgpr"])
+                assert blocks * lds <= LDS_PER_CU, (name, lds, dw)
+                seen["decode"] += 1
+                continue
+            assert lds <= LDS_PER_CU, (name, lds)
+            seen["other"] += 1
+    assert seen["tiled"] >= 100 and seen["decode"] >= 40 and seen["other"] >= 5, seen

@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 
 from oracle import w4a4_oracle as O
+from w4a4_gemm_lora_amd import workloads
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -447,3 +448,35 @@ def test_mlp_gate_up_wiring():
     zero = dict(lora_down16=None, lora_up16=None, w16=zero_w, bias=np.zeros(N, np.float32))
     _, _, h0 = O.mlp_gate_up(x, zero, gate)
     assert not np.any(h0.astype(np.float64))
+
+
+def test_linear_on_index_subsets_equals_full_evaluation_restricted():
+    """linear(rows=, cols=) (each row of X and of W is quantized on its own, so
+    a subset evaluates the same definition) against the full evaluation taken
+    at the same indices, for fp16 W and for checkpoint codes: codes, scales,
+    group sums' main term and Y identical; lora_act / LoRA / the fp64 output
+    equal up to the summation order of the library matrix product (a shape-
+    dependent blocking), i.e. within a few fp64 ulps."""
+    rng = np.random.default_rng(5)
+    for use_q in (False, True):
+        c = workloads.random_case(40, 512, 96, 32, seed=77 + use_q)
+        kw = dict(w16=c["w"])
+        if use_q:
+            q = rng.integers(-8, 8, size=(96, 512))
+            nib = (q & 0xF).astype(np.uint8)
+            kw = dict(qweight=(nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8),
+                      w_scales=rng.uniform(1e-3, 1e-2, (96, 8)).astype(np.float16))
+        full = O.linear(c["x"], c["lora_down"], c["lora_up"], c["col_scale"], c["bias"], **kw)
+        rows = np.sort(rng.choice(40, 9, replace=False))
+        cols = np.sort(rng.choice(96, 13, replace=False))
+        sub = O.linear(c["x"], c["lora_down"], c["lora_up"], c["col_scale"], c["bias"], rows=rows, cols=cols, **kw)
+        for k in ("qx", "sx"):
+            assert np.array_equal(sub[k], full[k][rows]), k
+        for k in ("qw", "sw"):
+            assert np.array_equal(sub[k], full[k][cols]), k
+        for k in ("main", "y"):
+            assert np.array_equal(sub[k], full[k][np.ix_(rows, cols)]), k
+        np.testing.assert_allclose(sub["lora_act"], full["lora_act"][rows], rtol=1e-13, atol=1e-15)
+        for k in ("lora", "y64"):
+            ref = full[k][np.ix_(rows, cols)]
+            assert np.max(np.abs(sub[k] - ref)) <= 1e-13 * np.max(np.abs(ref)), k

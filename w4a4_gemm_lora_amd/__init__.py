@@ -15,6 +15,7 @@ Names follow the C ABI in ``include/w4a4.h``::
     w4a4_linear(M, N, K, R, act, wblob, y)
     w4a4_query_variant(M, N, K, R)
     w4a4_debug_group_psums(M, N, K, R, act, wblob, m0, mc, n0, nc, out)
+    w4a4_debug_group_psums_glu(M, N, K, R, act, wblob, m0, mc, n0, nc, out)
 
 plus helpers that allocate the blobs as uint8 CUDA tensors.
 """
@@ -28,8 +29,8 @@ __all__ = [
     "w4a4_weight_layout", "w4a4_act_layout", "w4a4_pack_weights",
     "w4a4_quantize_act", "w4a4_quantize_act_rmsnorm", "w4a4_linear", "w4a4_linear_glu",
     "w4a4_query_variant", "GatedMLPUp",
-    "w4a4_debug_group_psums", "alloc_weight_blob", "alloc_act_blob",
-    "PackedLinear", "LayerGraphs", "EXPORTED_SYMBOLS",
+    "w4a4_debug_group_psums", "w4a4_debug_group_psums_glu", "alloc_weight_blob", "alloc_act_blob",
+    "PackedLinear", "LayerGraphs", "EXPORTED_SYMBOLS", "PEAKS_SYMBOLS", "load_peaks_library",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -37,7 +38,7 @@ EXPORTED_SYMBOLS = (
     "w4a4_status_string", "w4a4_weight_layout", "w4a4_act_layout",
     "w4a4_pack_weights", "w4a4_quantize_act", "w4a4_quantize_act_rmsnorm", "w4a4_linear",
     "w4a4_linear_glu", "w4a4_query_variant", "w4a4_debug_group_psums",
-    "w4a4_graph_begin", "w4a4_graph_end", "w4a4_layer_graph_create", "w4a4_graph_launch",
+    "w4a4_debug_group_psums_glu", "w4a4_graph_begin", "w4a4_graph_end", "w4a4_layer_graph_create", "w4a4_graph_launch",
     "w4a4_graph_destroy",
 )
 
@@ -50,6 +51,38 @@ class W4A4Error(RuntimeError):
 
 def lib_path() -> str:
     return os.path.join(_HERE, "libw4a4.so")
+
+
+# The measurement library (include/w4a4_peaks.h): microbenchmarks of the
+# attainable int8 MFMA and HBM read peaks, used by the benchmark only.
+PEAKS_SYMBOLS = ("w4a4_peak_i8_mfma", "w4a4_peak_i8_mfma_ops", "w4a4_peak_i8_mfma_out_ints",
+                 "w4a4_peak_hbm_read", "w4a4_peak_hbm_read_out_ints")
+_PEAKS = None
+
+
+def load_peaks_library() -> ctypes.CDLL:
+    """libw4a4_peaks.so from the package directory (after torch, like
+    load_library); raises if it is not built."""
+    global _PEAKS
+    if _PEAKS is not None:
+        return _PEAKS
+    path = os.path.join(_HERE, "libw4a4_peaks.so")
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -m w4a4_gemm_lora_amd.build`")
+    import torch  # noqa: F401
+    lib = ctypes.CDLL(path)
+    lib.w4a4_peak_i8_mfma.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    lib.w4a4_peak_i8_mfma.restype = ctypes.c_int
+    lib.w4a4_peak_i8_mfma_ops.argtypes = [ctypes.c_int32]
+    lib.w4a4_peak_i8_mfma_ops.restype = ctypes.c_int64
+    lib.w4a4_peak_i8_mfma_out_ints.argtypes = []
+    lib.w4a4_peak_i8_mfma_out_ints.restype = ctypes.c_int64
+    lib.w4a4_peak_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
+    lib.w4a4_peak_hbm_read.restype = ctypes.c_int
+    lib.w4a4_peak_hbm_read_out_ints.argtypes = []
+    lib.w4a4_peak_hbm_read_out_ints.restype = ctypes.c_int64
+    _PEAKS = lib
+    return lib
 
 
 _LIB = None
@@ -92,6 +125,7 @@ def load_library() -> ctypes.CDLL:
     lib.w4a4_graph_launch.argtypes = [_vp, _vp]
     lib.w4a4_graph_destroy.argtypes = [_vp]
     lib.w4a4_debug_group_psums.argtypes = [_i64, _i64, _i64, _i32, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp]
+    lib.w4a4_debug_group_psums_glu.argtypes = lib.w4a4_debug_group_psums.argtypes
     for name in EXPORTED_SYMBOLS:
         if name != "w4a4_status_string":
             getattr(lib, name).restype = ctypes.c_int
@@ -196,6 +230,12 @@ def w4a4_debug_group_psums(M, N, K, R, act, wblob, m0, mc, n0, nc, out, stream=N
     st = load_library().w4a4_debug_group_psums(M, N, K, R, _ptr(act), _ptr(wblob), m0, mc, n0, nc,
                                                _ptr(out), _stream(stream))
     _check(st, "w4a4_debug_group_psums")
+
+
+def w4a4_debug_group_psums_glu(M, N, K, R, act, wblob, m0, mc, n0, nc, out, stream=None):
+    st = load_library().w4a4_debug_group_psums_glu(M, N, K, R, _ptr(act), _ptr(wblob), m0, mc, n0, nc,
+                                                   _ptr(out), _stream(stream))
+    _check(st, "w4a4_debug_group_psums_glu")
 
 
 # ---- allocation helpers (torch owns the memory) ------------------------------

@@ -15,9 +15,12 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libw4a4.so")
+PEAKS_OUT = os.path.join(PKG, "libw4a4_peaks.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["api.cpp", "graph.cpp", "quantize.hip", "gemm.hip"]
+# measurement-only microbenchmarks (attainable peaks), a library of their own
+PEAKS_SOURCES = ["peaks.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -38,22 +41,35 @@ def _run(cmd):
     return err
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def _objects(sources):
     objs, cmds = [], []
-    for s in SOURCES:
-        src = os.path.join(CSRC, s)
-        obj = os.path.join(BUILD_DIR, os.path.splitext(s)[0] + ".o")
-        lang = ["-x", "hip"] if s.endswith(".hip") else []
-        cmds.append([HIPCC] + COMMON + lang + ["-c", src, "-o", obj])
+    for src in sources:
+        path = os.path.join(CSRC, src)
+        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+        lang = ["-x", "hip"] if src.endswith(".hip") else []
+        cmds.append([HIPCC] + COMMON + lang + ["-c", path, "-o", obj])
         objs.append(obj)
-    with ThreadPoolExecutor(max_workers=min(4, len(cmds))) as ex:
-        for msg in ex.map(_run, cmds):
+    return objs, cmds
+
+
+def _link(objs, out):
+    tmp = out + ".tmp"
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source for gfx950 and link libw4a4.so (the layer)
+    and libw4a4_peaks.so (the peak microbenchmarks); returns libw4a4.so."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    objs, cmds = _objects(SOURCES)
+    pobjs, pcmds = _objects(PEAKS_SOURCES)
+    with ThreadPoolExecutor(max_workers=min(4, len(cmds) + len(pcmds))) as ex:
+        for msg in ex.map(_run, cmds + pcmds):
             if verbose and msg.strip():
                 print(msg, file=sys.stderr)
-    tmp = OUT + ".tmp"
-    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs)
-    os.replace(tmp, OUT)
+    _link(objs, OUT)
+    _link(pobjs, PEAKS_OUT)
     return OUT
 
 

@@ -47,7 +47,7 @@ const char* variant_name(int v) {
   switch (v) {
     case kDecode: return "decode";
     case kPrefill: return "prefill";
-    default: return "generic";
+    default: return "?";
   }
 }
 
@@ -255,11 +255,15 @@ int w4a4_query_variant(int64_t M, int64_t N, int64_t K, int32_t R) {
   return choose_variant(M, N, K, R);
 }
 
-int w4a4_debug_group_psums(int64_t M, int64_t N, int64_t K, int32_t R, const void* act,
-                           const void* wblob, int64_t m0, int64_t mc, int64_t n0,
-                           int64_t nc, int32_t* out, void* stream) {
+// The exact group sums of a window, from the instance of the kernel and tile
+// shape that w4a4_linear (glu = false) or w4a4_linear_glu (glu = true) runs
+// for this shape, with only its per-group epilogue swapped for the store.
+static int group_psums_impl(int64_t M, int64_t N, int64_t K, int32_t R, const void* act,
+                            const void* wblob, int64_t m0, int64_t mc, int64_t n0, int64_t nc,
+                            int32_t* out, void* stream, bool glu) {
   int st = check_nkr(N, K, R);
   if (st) return st;
+  if (glu && N % 32 != 0) return W4A4_ERR_SHAPE;
   if ((st = check_m(M))) return st;
   if (!out) return W4A4_ERR_NULL;
   const int64_t Mp = round_up16(M);
@@ -269,7 +273,39 @@ int w4a4_debug_group_psums(int64_t M, int64_t N, int64_t K, int32_t R, const voi
   if (!aligned(out, 4)) return W4A4_ERR_ALIGN;
   GemmArgs a;
   if ((st = make_gemm_args(M, N, K, R, act, wblob, nullptr, N, &a))) return st;
-  return hip_status(launch_group_psums(a, m0, mc, n0, nc, out, reinterpret_cast<hipStream_t>(stream)));
+  // out must not overlap either blob
+  {
+    const uint8_t* ob = reinterpret_cast<const uint8_t*>(out);
+    const uint8_t* oe = ob + (size_t)mc * nc * (K / kGroup) * 4;
+    const uint8_t* ab = static_cast<const uint8_t*>(act);
+    const uint8_t* wb = static_cast<const uint8_t*>(wblob);
+    const size_t at = act_geom(M, K, R).total, wt = weight_geom(N, K, R).total;
+    if ((ob < ab + at && ab < oe) || (ob < wb + wt && wb < oe)) return W4A4_ERR_ARG;
+  }
+  a.glu = glu ? 1 : 0;
+  a.psum = out;
+  a.ps_m0 = m0;
+  a.ps_mc = mc;
+  a.ps_n0 = n0;
+  a.ps_nc = nc;
+  const int v = choose_variant(M, N, K, R);
+  if (log_enabled())
+    std::fprintf(stderr, "%s M=%lld N=%lld K=%lld R=%d -> %s\n",
+                 glu ? "w4a4_debug_group_psums_glu" : "w4a4_debug_group_psums", (long long)M, (long long)N,
+                 (long long)K, R, variant_name(v));
+  return hip_status(launch_gemm(a, v, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int w4a4_debug_group_psums(int64_t M, int64_t N, int64_t K, int32_t R, const void* act,
+                           const void* wblob, int64_t m0, int64_t mc, int64_t n0,
+                           int64_t nc, int32_t* out, void* stream) {
+  return group_psums_impl(M, N, K, R, act, wblob, m0, mc, n0, nc, out, stream, false);
+}
+
+int w4a4_debug_group_psums_glu(int64_t M, int64_t N, int64_t K, int32_t R, const void* act,
+                               const void* wblob, int64_t m0, int64_t mc, int64_t n0,
+                               int64_t nc, int32_t* out, void* stream) {
+  return group_psums_impl(M, N, K, R, act, wblob, m0, mc, n0, nc, out, stream, true);
 }
 
 }  // extern "C"

@@ -39,179 +39,22 @@
 namespace w4a4 {
 
 // ---------------------------------------------------------------------------
-// Generic kernel: 4 waves in a 2 x 2 arrangement, each wave TM x TN tiles of
-// 16 x 16.  Operand fragments come straight from global memory: the packed
-// layouts are lane-ordered, so each 16 x 128 tile is one coalesced 1 KB read
-// by a wave.  PSUM=true swaps the epilogue for a store of the integer group
-// sums (diagnostic window [mt_base, mt_end) x [nt_base, nt_end) in tiles).
-// ---------------------------------------------------------------------------
-template <int TM, int TN, int RT, bool PSUM>
-__global__ __launch_bounds__(256) void gemm_generic_kernel(
-    GemmArgs g, int64_t mt_base, int64_t mt_end, int64_t nt_base, int64_t nt_end,
-    int32_t* __restrict__ psum, int64_t psum_nc) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int64_t mt0 = mt_base + ((int64_t)blockIdx.y * 2 + wm) * TM;
-  const int64_t nt0 = nt_base + ((int64_t)blockIdx.x * 2 + wn) * TN;
-  const int64_t KP = g.K / kKPair;
-  const int64_t G = g.K / kGroup;
-  const int c = lane >> 4, col_l = lane & 15;
-
-  bool mv[TM], nv[TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i) mv[i] = (mt0 + i) < mt_end;
-#pragma unroll
-  for (int j = 0; j < TN; ++j) nv[j] = (nt0 + j) < nt_end;
-
-  v4f acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  const v4i zero = v4i{0, 0, 0, 0};
-  for (int64_t p = 0; p < KP; ++p) {
-    v4u araw[TM], braw[TN];
-    v8h sxv[TM];
-    uint32_t swv[TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      if (mv[i]) {
-        araw[i] = *reinterpret_cast<const v4u*>(g.xq + ((size_t)(mt0 + i) * KP + p) * kTileBytes + lane * 16);
-        sxv[i] = *reinterpret_cast<const v8h*>(g.sx + ((size_t)(mt0 + i) * KP + p) * 32 + c * 8);
-      } else {
-        araw[i] = v4u{0, 0, 0, 0};
-        sxv[i] = v8h{0, 0, 0, 0, 0, 0, 0, 0};
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      if (nv[j]) {
-        braw[j] = *reinterpret_cast<const v4u*>(g.wq + ((size_t)(nt0 + j) * KP + p) * kTileBytes + lane * 16);
-        swv[j] = *reinterpret_cast<const uint32_t*>(g.sw + ((size_t)(nt0 + j) * KP + p) * 32 + col_l * 2);
-      } else {
-        braw[j] = v4u{0, 0, 0, 0};
-        swv[j] = 0;
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      v4i A[TM], B[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) A[i] = expand_group(araw[i][2 * h], araw[i][2 * h + 1]);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) B[j] = expand_group(braw[j][2 * h], braw[j][2 * h + 1]);
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          v4i P = mfma_i8_16x16x64(A[i], B[j], zero);
-          if constexpr (PSUM) {
-            if (mv[i] && nv[j]) {
-              const int64_t col = (nt0 + j) * 16 + col_l - nt_base * 16;
-#pragma unroll
-              for (int ii = 0; ii < 4; ++ii) {
-                const int64_t row = (mt0 + i) * 16 + c * 4 + ii - mt_base * 16;
-                psum[(row * psum_nc + col) * G + 2 * p + h] = P[ii] >> 8;
-              }
-            }
-          } else {
-            const float swf = half_bits_to_float((uint16_t)(swv[j] >> (16 * h))) * (1.0f / 256.0f);
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-              const float s = (float)sxv[i][ii * 2 + h] * swf;
-              acc[i][j][ii] = fmaf((float)P[ii], s, acc[i][j][ii]);
-            }
-          }
-        }
-      }
-    }
-  }
-  if constexpr (PSUM) return;
-
-  // LoRA-up: acc += lora_act (hi + lo fp16) x L_up^T on f16 MFMA.
-  if constexpr (RT > 0) {
-    const int R = RT * 16;
-#pragma unroll
-    for (int t = 0; t < RT; ++t) {
-      v4h ahi[TM], alo[TM], bl[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        v4f la = v4f{0.f, 0.f, 0.f, 0.f};
-        if (mv[i]) {
-          const size_t mp = (size_t)round_up16(g.M);
-          for (int j = 0; j < g.ks; ++j)
-            la += *reinterpret_cast<const v4f*>(g.la + (j * mp + (size_t)((mt0 + i) * 16 + col_l)) * R + t * 16 + c * 4);
-        }
-        split_f16(la, ahi[i], alo[i]);
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        bl[j] = v4h{0, 0, 0, 0};
-        if (nv[j]) bl[j] = *reinterpret_cast<const v4h*>(g.lup + (((size_t)(nt0 + j) * RT + t) * 64 + lane) * 4);
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          acc[i][j] = mfma_f16_16x16x16(ahi[i], bl[j], acc[i][j]);
-          acc[i][j] = mfma_f16_16x16x16(alo[i], bl[j], acc[i][j]);
-        }
-    }
-  }
-
-  // Affine + fp16 store (rows >= M are padding and never written).
-#pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    if (!nv[j]) continue;
-    const int64_t col = (nt0 + j) * 16 + col_l;
-    const float af = g.ca[col], bf = g.cb[col];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      if (!mv[i]) continue;
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int64_t row = (mt0 + i) * 16 + c * 4 + ii;
-        if (row < g.M) {
-          const _Float16 v = (_Float16)fmaf(af, acc[i][j][ii], bf);
-          g.y[row * g.ldy + col] = __builtin_bit_cast(uint16_t, v);
-        }
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
 // Shared epilogue pieces
 // ---------------------------------------------------------------------------
 
-// lora_act fragment of one 16-row tile for rank tile t: lane (r, c) gets
-// lora_act[row0 + r][16t + 4c .. 16t + 4c + 3], the sum of the ks partials
-// taken in order.
-__device__ __forceinline__ v4f lora_frag(const GemmArgs& g, int64_t row0, int t, int lane) {
-  const int c = lane >> 4, r = lane & 15;
-  const size_t mp = (size_t)round_up16(g.M);
-  v4f l4 = v4f{0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < g.ks; ++j)
-    l4 += *reinterpret_cast<const v4f*>(g.la + (j * mp + (size_t)(row0 + r)) * g.R + t * 16 + c * 4);
-  return l4;
-}
-
-// acc (one 16x16 output tile; lane holds rows 4c+ii, column lane&15) +=
-// lora_act (fp16 hi + lo) x L_up^T over RT rank tiles.
-template <int RT>
-__device__ __forceinline__ v4f lora_up_tile(v4f acc, const GemmArgs& g, int64_t row0, int64_t nt,
-                                            int lane) {
+// Diagnostic epilogue (GemmArgs::psum): the exact integer sums P of one
+// 16 x 16 tile and group grp -- lane (c, r) holds rows 4c + ii of column r --
+// stored where the tile meets the caller's window.
+__device__ __forceinline__ void store_psum_tile(const GemmArgs& g, v4i P, int64_t row0, int64_t col0,
+                                                int64_t grp, int lane) {
+  const int64_t col = col0 + (lane & 15) - g.ps_n0;
+  if (col < 0 || col >= g.ps_nc) return;
+  const int64_t G = g.K / kGroup;
 #pragma unroll
-  for (int t = 0; t < RT; ++t) {
-    v4h hi, lo;
-    split_f16(lora_frag(g, row0, t, lane), hi, lo);
-    const v4h b = *reinterpret_cast<const v4h*>(g.lup + (((size_t)nt * RT + t) * 64 + lane) * 4);
-    acc = mfma_f16_16x16x16(hi, b, acc);
-    acc = mfma_f16_16x16x16(lo, b, acc);
+  for (int ii = 0; ii < 4; ++ii) {
+    const int64_t row = row0 + (lane >> 4) * 4 + ii - g.ps_m0;
+    if (row >= 0 && row < g.ps_mc) g.psum[(row * g.ps_nc + col) * G + grp] = P[ii];
   }
-  return acc;
 }
 
 // The gated activation of one output value: the gate and up projections'
@@ -310,17 +153,6 @@ __device__ __forceinline__ void store_tile4_glu(const GemmArgs& g, v4f gacc, v4f
   store_tile4_bits(g, h, row0, col0, lane);
 }
 
-// One 64-group of one 16x16 tile: an i8 MFMA with a zero C (256 P exactly)
-// followed by acc += P * s_x * s_w / 256 for the MV leading accumulator rows.
-template <int MV>
-__device__ __forceinline__ v4f group_tile(v4f acc, uint32_t a0, uint32_t a1, uint32_t b0,
-                                          uint32_t b1, const float* sxf, float swf) {
-  const v4i P = mfma_i8_16x16x64(expand_group(a0, a1), expand_group(b0, b1), v4i{0, 0, 0, 0});
-#pragma unroll
-  for (int ii = 0; ii < MV; ++ii) acc[ii] = fmaf((float)P[ii], sxf[ii] * swf, acc[ii]);
-  return acc;
-}
-
 typedef __attribute__((address_space(3))) void lds_void;
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
@@ -417,8 +249,13 @@ __device__ __forceinline__ void decode_lora_loads(const GemmArgs& g, int64_t nt0
   }
 }
 
-template <int MV, int RT, int KB, int NTW, bool GLU, int DW>
-__global__ __launch_bounds__(64 * DW, 16 / DW) void gemm_decode_kernel(GemmArgs g) {
+// PSUM: the diagnostic instance -- the same batches, loads, expansion and
+// integer MFMAs, with the per-group scale-accumulate replaced by a store of
+// each group's exact sums (GemmArgs::psum) and no LoRA, reduction or store
+// of Y.
+template <int MV, int RT, int KB, int NTW, bool GLU, int DW, bool PSUM = false>
+__global__ __launch_bounds__(64 * DW, PSUM ? 1 : 16 / DW) void gemm_decode_kernel(GemmArgs g) {
+  static_assert(!PSUM || (RT == 0 && !GLU), "the diagnostic instance has no epilogue");
   constexpr int RTL = RT > 0 ? RT : 1;
   __shared__ v4f red[NTW][DW][64];
   __shared__ v4f lred[RTL][DW][64];
@@ -466,7 +303,7 @@ __global__ __launch_bounds__(64 * DW, 16 / DW) void gemm_decode_kernel(GemmArgs 
   for (int n = 0; n < NTW; ++n) {
     af[n] = 0.f;
     bf[n] = 0.f;
-    if (wave == 0) {
+    if (!PSUM && wave == 0) {
       af[n] = g.ca[(nt0 + n) * 16 + r];
       bf[n] = g.cb[(nt0 + n) * 16 + r];
     }
@@ -546,7 +383,7 @@ __global__ __launch_bounds__(64 * DW, 16 / DW) void gemm_decode_kernel(GemmArgs 
       sxw[u] = *reinterpret_cast<const uint32_t*>(sxq + (size_t)p * 64);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (kEarly && !lora_done) {
+    if (!PSUM && kEarly && !lora_done) {
       lora_early();
       lora_done = true;
     }
@@ -558,20 +395,29 @@ __global__ __launch_bounds__(64 * DW, 16 / DW) void gemm_decode_kernel(GemmArgs 
           const v4i Ae = expand_group(araw[u][2 * h], araw[u][2 * h + 1]);
           v4f S[NTW];
           v4i P[NTW];
+          if constexpr (!PSUM) {
 #pragma unroll
-          for (int n = 0; n < NTW; ++n) S[n] = scale_tile(sxw[u], swv[u][n], h);
+            for (int n = 0; n < NTW; ++n) S[n] = scale_tile(sxw[u], swv[u][n], h);
+          }
 #pragma unroll
           for (int n = 0; n < NTW; ++n)
             P[n] = mfma_i8_16x16x64(Ae, expand_group(braw[u][n][2 * h], braw[u][n][2 * h + 1]),
                                     v4i{0, 0, 0, 0});
+          if constexpr (PSUM) {
+            // the int8 operands carry 16 q each: the MFMA returns 256 P
 #pragma unroll
-          for (int n = 0; n < NTW; ++n)
+            for (int n = 0; n < NTW; ++n) store_psum_tile(g, P[n] >> 8, 0, (nt0 + n) * 16, 2 * (pb + u) + h, lane);
+          } else {
 #pragma unroll
-            for (int ii = 0; ii < MV; ++ii) acc[n][ii] = fmaf((float)P[n][ii], S[n][ii], acc[n][ii]);
+            for (int n = 0; n < NTW; ++n)
+#pragma unroll
+              for (int ii = 0; ii < MV; ++ii) acc[n][ii] = fmaf((float)P[n][ii], S[n][ii], acc[n][ii]);
+          }
         }
       }
     }
   }
+  if constexpr (PSUM) return;
   if constexpr (!kEarly) decode_lora_loads<RT, NTW, LQ, RTL, DW>(g, nt0, wave, lane, lpart, lup);
   if (!lora_done) lora_early();   // a wave with no k-pairs still meets the barrier
 
@@ -682,9 +528,15 @@ __device__ __forceinline__ void dot_stage(const DotBatch<MR, KB, NT>& d, v4u* xs
   }
 }
 
-template <int MR, int KB, int NT, bool TAIL>
+// PSUM (diagnostic): instead of the scale-accumulate, the lane's integer
+// partial (its 16 k of the group) is summed over the group's four k
+// segments (lanes r, r + 16, r + 32, r + 48) and lanes of segment 0 store
+// the group's exact sums for rows < MR of column tile nt0 + n (rows MR..15
+// of the tile are padding, whose codes and sums are 0).
+template <int MR, int KB, int NT, bool TAIL, bool PSUM>
 __device__ __forceinline__ void dot_accumulate(const DotBatch<MR, KB, NT>& d, const v4u* xs,
-                                               float (&acc)[NT][MR], int c, int pb, int p1) {
+                                               float (&acc)[NT][MR], int c, int pb, int p1,
+                                               const GemmArgs& g, int64_t nt0, int lane) {
 #pragma unroll
   for (int u = 0; u < KB; ++u) {
     if (TAIL && pb + u >= p1) break;   // wave-uniform
@@ -696,21 +548,38 @@ __device__ __forceinline__ void dot_accumulate(const DotBatch<MR, KB, NT>& d, co
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
         const float swf = half_bits_to_float((uint16_t)(d.sw[u][n] >> (16 * h)));
+        v4i Pt = v4i{0, 0, 0, 0};   // PSUM: rows 0..3 of the tile in the MFMA accumulator layout
 #pragma unroll
         for (int m = 0; m < MR; ++m) {
           int P = __builtin_amdgcn_sdot8((int)d.w[u][n][2 * h], (int)xv[m][2 * h], 0, false);
           P = __builtin_amdgcn_sdot8((int)d.w[u][n][2 * h + 1], (int)xv[m][2 * h + 1], P, false);
-          // s_x * s_w is exact in fp32; fma with +0 keeps it one mixed-precision op
-          const float sc = __builtin_fmaf(half_bits_to_float((uint16_t)(d.sx[u][m] >> (16 * h))), swf, 0.f);
-          acc[n][m] = fmaf((float)P, sc, acc[n][m]);
+          if constexpr (PSUM) {
+            P += __shfl_xor(P, 16);
+            P += __shfl_xor(P, 32);
+            Pt[m] = P;
+          } else {
+            // s_x * s_w is exact in fp32; fma with +0 keeps it one mixed-precision op
+            const float sc = __builtin_fmaf(half_bits_to_float((uint16_t)(d.sx[u][m] >> (16 * h))), swf, 0.f);
+            acc[n][m] = fmaf((float)P, sc, acc[n][m]);
+          }
+        }
+        if constexpr (PSUM) {
+          // lanes of segment 0 hold rows 0..MR-1 (as lane (c = 0, r) of the
+          // accumulator layout); the other lanes store the zero rows 4c..4c+3
+          if (c != 0) Pt = v4i{0, 0, 0, 0};
+          store_psum_tile(g, Pt, 0, (nt0 + n) * 16, 2 * (int64_t)(pb + u) + h, lane);
         }
       }
     }
   }
 }
 
-template <int MR, int RT, int KB, int NT, bool GLU, int DW>
-__global__ __launch_bounds__(64 * DW, 16 / DW) void gemm_decode_dot_kernel(GemmArgs g) {
+// PSUM: the diagnostic instance (dot_accumulate's PSUM path; no LoRA,
+// reduction or store of Y).
+template <int MR, int RT, int KB, int NT, bool GLU, int DW, bool PSUM = false>
+__global__ __launch_bounds__(64 * DW, PSUM ? 1 : 16 / DW) void gemm_decode_dot_kernel(GemmArgs g) {
+  static_assert(!PSUM || (RT == 0 && !GLU), "the diagnostic instance has no epilogue");
+  static_assert(MR <= 4, "the dot kernel's rows sit in lanes 0..15 of the accumulator layout");
   constexpr int RTL = RT > 0 ? RT : 1;
   __shared__ float red[NT][DW][MR][16];
   __shared__ v4f lred[RTL][DW][64];
@@ -758,7 +627,7 @@ __global__ __launch_bounds__(64 * DW, 16 / DW) void gemm_decode_dot_kernel(GemmA
   for (int n = 0; n < NT; ++n) {
     af[n] = 0.f;
     bf[n] = 0.f;
-    if (wave == 0) {
+    if (!PSUM && wave == 0) {
       af[n] = g.ca[(nt0 + n) * 16 + r];
       bf[n] = g.cb[(nt0 + n) * 16 + r];
     }
@@ -813,7 +682,7 @@ __global__ __launch_bounds__(64 * DW, 16 / DW) void gemm_decode_dot_kernel(GemmA
 #pragma unroll
     for (int m = 0; m < MR; ++m) acc[n][m] = 0.f;
   int pb = p0;
-  bool lora_done = false;
+  bool lora_done = PSUM;   // the diagnostic instance has no LoRA (and no barrier)
   for (; pb + KB <= p1; pb += KB) {
     DotBatch<MR, KB, NT> d;
     dot_load<MR, KB, NT, false>(d, wq, sw, g.xq, sx, lane, pb, p1, KP);
@@ -822,7 +691,7 @@ __global__ __launch_bounds__(64 * DW, 16 / DW) void gemm_decode_dot_kernel(GemmA
       lora_done = true;
     }
     dot_stage(d, xs, lane);
-    dot_accumulate<MR, KB, NT, false>(d, xs, acc, c, pb, p1);
+    dot_accumulate<MR, KB, NT, false, PSUM>(d, xs, acc, c, pb, p1, g, nt0, lane);
   }
   if (pb < p1) {
     DotBatch<MR, KB, NT> d;
@@ -832,8 +701,9 @@ __global__ __launch_bounds__(64 * DW, 16 / DW) void gemm_decode_dot_kernel(GemmA
       lora_done = true;
     }
     dot_stage(d, xs, lane);
-    dot_accumulate<MR, KB, NT, true>(d, xs, acc, c, pb, p1);
+    dot_accumulate<MR, KB, NT, true, PSUM>(d, xs, acc, c, pb, p1, g, nt0, lane);
   }
+  if constexpr (PSUM) return;
   if (!lora_done) lora_early();   // a wave with no k-pairs still meets the barrier
 
   // sum the four k segments of each column (lanes r, r+16, r+32, r+48)
@@ -898,9 +768,17 @@ __global__ __launch_bounds__(64 * DW, 16 / DW) void gemm_decode_dot_kernel(GemmA
 // ---------------------------------------------------------------------------
 constexpr int kTileGroupRows = 8;
 
-template <int WM, int WN, int TM, int TN, int RT, int NS, int SPL, bool GLU, int OCC, int KS>
-__global__ __launch_bounds__(WM * WN * KS * 64, OCC) void gemm_tiled_kernel(GemmArgs g, int64_t mt_count,
+// PSUM: the diagnostic instance -- the same staging, waits, expansion and
+// integer MFMAs, with the per-group scale-accumulate replaced by a store of
+// each group's exact sums, read back from the MFMA's 3.0f-offset result as
+// (bits - kOffsetBits) / 256 (GemmArgs::psum); no LoRA and no store of Y.
+// (A diagnostic launch keeps no occupancy: its instances are built for one
+// workgroup per CU, so the stores of its epilogue never spill.)
+template <int WM, int WN, int TM, int TN, int RT, int NS, int SPL, bool GLU, int OCC, int KS,
+          bool PSUM = false>
+__global__ __launch_bounds__(WM * WN * KS * 64, PSUM ? 1 : OCC) void gemm_tiled_kernel(GemmArgs g, int64_t mt_count,
                                                                         int64_t nt_count) {
+  static_assert(!PSUM || (RT == 0 && SPL == 1 && !GLU), "the diagnostic instance has no epilogue");
   // KS = 2 splits K between two sets of WM x WN waves over the same output
   // tiles (each with its own stage ring, in lockstep), and the second set's
   // accumulators are added to the first's in LDS after the loop: twice the
@@ -1006,7 +884,11 @@ __global__ __launch_bounds__(WM * WN * KS * 64, OCC) void gemm_tiled_kernel(Gemm
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // OCC = workgroups per CU the instance is built for.  OCC = 3 (the lean
+  // OCC = waves per SIMD the instance is built for (the launch bound's
+  // minimum, which the compiler turns into a budget of 512 / OCC registers
+  // per lane).  A KS = 1 workgroup puts one wave on each SIMD, so there OCC is
+  // also the workgroups per CU; a K-split workgroup (KS = 2) puts two, so its
+  // OCC = 2 instances hold one workgroup per CU.  OCC = 3 (the lean
   // variant, 3 waves per SIMD, where the VALU work of the per-group epilogue
   // issues ~1.5x faster than at 2) keeps the loop's registers down: the
   // epilogue operands below are loaded after the loop, lora_act partials too,
@@ -1076,7 +958,7 @@ __global__ __launch_bounds__(WM * WN * KS * 64, OCC) void gemm_tiled_kernel(Gemm
   // complete in issue order, so the count is what the wait may leave
   // outstanding; the conditional lora_act partials (split index >= 1) are
   // not counted -- more younger loads than counted only make a wait longer.
-  constexpr int kEpiLoads = kLean ? 0 : 2 * TN + TN * RT + ((!kLateLora && RT > 0) ? TM * RT : 0);
+  constexpr int kEpiLoads = (kLean || PSUM) ? 0 : 2 * TN + TN * RT + ((!kLateLora && RT > 0) ? TM * RT : 0);
   static_assert(2 * OPS + kEpiLoads <= 63, "vmcnt counts to 63");
   int st = 0;                      // == p % NS
   int st_next = (NS - 1) % NS;     // == (p + NS - 1) % NS
@@ -1107,7 +989,7 @@ __global__ __launch_bounds__(WM * WN * KS * 64, OCC) void gemm_tiled_kernel(Gemm
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if (p + NS - 1 < KP) issue_copy(st_next, p + NS - 1);
-    if constexpr (!kLean) {
+    if constexpr (!kLean && !PSUM) {
       // after every copy of stages <= NS-1 (the fence keeps the compiler
       // from moving these loads ahead of the copies: kEpiLoads relies on it)
       if (p == 0) {
@@ -1129,10 +1011,19 @@ __global__ __launch_bounds__(WM * WN * KS * 64, OCC) void gemm_tiled_kernel(Gemm
     for (int j = 0; j < TN; ++j)
       sww[j] = *reinterpret_cast<const uint32_t*>(sl + (BMT + wn * TN + j) * 64 + (lane & 15) * 4);
     // both groups' offsets leave the accumulators first (see kOffsetBits)
+    if constexpr (!PSUM) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = offset_tile(sxw[i], sww[j], acc[i][j]);
+        for (int j = 0; j < TN; ++j) acc[i][j] = offset_tile(sxw[i], sww[j], acc[i][j]);
+    }
+    // diagnostic epilogue: the group sums of tile (i, j), group h
+    auto psum_tile = [&](int i, int j, int h, v4i P) {
+      const uint32_t mt = mt0 + wm * TM + i, nt = nt0 + wn * TN + j;
+      if (mt < mtc && nt < ntc)
+        store_psum_tile(g, (P - kOffset) >> 8, (int64_t)mt * 16, (int64_t)nt * 16, 2 * ((int64_t)kh * KP + p) + h,
+                        lane);
+    };
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       // A codes stay packed until their row tile comes up (lean: fewer
@@ -1159,17 +1050,23 @@ __global__ __launch_bounds__(WM * WN * KS * 64, OCC) void gemm_tiled_kernel(Gemm
           for (int j0 = 0; j0 < TN; j0 += JP) {
             v4f S[JP];
             v4i P[JP];
+            if constexpr (!PSUM) {
 #pragma unroll
-            for (int q = 0; q < JP; ++q) S[q] = scale_tile(sxw[i], sww[j0 + q], h);
+              for (int q = 0; q < JP; ++q) S[q] = scale_tile(sxw[i], sww[j0 + q], h);
+            }
 #pragma unroll
             for (int q = 0; q < JP; ++q) P[q] = mfma_i8_16x16x64(Ae, Be[j0 + q], kOffset);
 #pragma unroll
             for (int q = 0; q < JP; ++q) {
-              // (cast the whole vector: clang's bit_cast of one element of an
-              // ext_vector reads element 0 whatever the index)
-              const v4f Pf = __builtin_bit_cast(v4f, P[q]);
+              if constexpr (PSUM) {
+                psum_tile(i, j0 + q, h, P[q]);
+              } else {
+                // (cast the whole vector: clang's bit_cast of one element of an
+                // ext_vector reads element 0 whatever the index)
+                const v4f Pf = __builtin_bit_cast(v4f, P[q]);
 #pragma unroll
-              for (int ii = 0; ii < 4; ++ii) acc[i][j0 + q][ii] = fmaf(S[q][ii], Pf[ii], acc[i][j0 + q][ii]);
+                for (int ii = 0; ii < 4; ++ii) acc[i][j0 + q][ii] = fmaf(S[q][ii], Pf[ii], acc[i][j0 + q][ii]);
+              }
             }
           }
         }
@@ -1183,15 +1080,21 @@ __global__ __launch_bounds__(WM * WN * KS * 64, OCC) void gemm_tiled_kernel(Gemm
           const v4i Ae = expand_group(Ar[i][0], Ar[i][1]);
           v4f S[TN];
           v4i P[TN];
+          if constexpr (!PSUM) {
 #pragma unroll
-          for (int j = 0; j < TN; ++j) S[j] = scale_tile(sxw[i], sww[j], h);
+            for (int j = 0; j < TN; ++j) S[j] = scale_tile(sxw[i], sww[j], h);
+          }
 #pragma unroll
           for (int j = 0; j < TN; ++j) P[j] = mfma_i8_16x16x64(Ae, Be[j], kOffset);
 #pragma unroll
           for (int j = 0; j < TN; ++j) {
-            const v4f Pf = __builtin_bit_cast(v4f, P[j]);   // whole-vector cast (see above)
+            if constexpr (PSUM) {
+              psum_tile(i, j, h, P[j]);
+            } else {
+              const v4f Pf = __builtin_bit_cast(v4f, P[j]);   // whole-vector cast (see above)
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) acc[i][j][ii] = fmaf(S[j][ii], Pf[ii], acc[i][j][ii]);
+              for (int ii = 0; ii < 4; ++ii) acc[i][j][ii] = fmaf(S[j][ii], Pf[ii], acc[i][j][ii]);
+            }
           }
         }
       }
@@ -1199,6 +1102,7 @@ __global__ __launch_bounds__(WM * WN * KS * 64, OCC) void gemm_tiled_kernel(Gemm
     st = st + 1 == NS ? 0 : st + 1;
     st_next = st_next + 1 == NS ? 0 : st_next + 1;
   }
+  if constexpr (PSUM) return;
 
   if constexpr (KS > 1) {
     // the second K part's accumulators join the first's, in that order
@@ -1309,15 +1213,26 @@ constexpr int mv_kb(int rt, int ntw) {
   return kTable[ntw - 1][rt];
 }
 
+// The layer's instance, or (a.psum set) the diagnostic instance with the
+// same batch size, column tiles per workgroup and waves.
+template <int MV, int RT, int NTW, bool GLU, int DW>
+static void launch_mv_rt(const GemmArgs& a, dim3 grid, dim3 block, hipStream_t stream) {
+  constexpr int KB = mv_kb(RT, NTW);
+  if (a.psum)
+    gemm_decode_kernel<MV, 0, KB, NTW, false, DW, true><<<grid, block, 0, stream>>>(a);
+  else
+    gemm_decode_kernel<MV, RT, KB, NTW, GLU, DW><<<grid, block, 0, stream>>>(a);
+}
+
 template <int MV, int NTW, bool GLU, int DW>
 static hipError_t launch_decode_mv_dw(const GemmArgs& a, hipStream_t stream) {
   dim3 grid((unsigned)(a.N / 16 / NTW)), block(64 * DW);
   switch (a.R / 16) {
-    case 0: gemm_decode_kernel<MV, 0, mv_kb(0, NTW), NTW, GLU, DW><<<grid, block, 0, stream>>>(a); break;
-    case 1: gemm_decode_kernel<MV, 1, mv_kb(1, NTW), NTW, GLU, DW><<<grid, block, 0, stream>>>(a); break;
-    case 2: gemm_decode_kernel<MV, 2, mv_kb(2, NTW), NTW, GLU, DW><<<grid, block, 0, stream>>>(a); break;
-    case 3: gemm_decode_kernel<MV, 3, mv_kb(3, NTW), NTW, GLU, DW><<<grid, block, 0, stream>>>(a); break;
-    case 4: gemm_decode_kernel<MV, 4, mv_kb(4, NTW), NTW, GLU, DW><<<grid, block, 0, stream>>>(a); break;
+    case 0: launch_mv_rt<MV, 0, NTW, GLU, DW>(a, grid, block, stream); break;
+    case 1: launch_mv_rt<MV, 1, NTW, GLU, DW>(a, grid, block, stream); break;
+    case 2: launch_mv_rt<MV, 2, NTW, GLU, DW>(a, grid, block, stream); break;
+    case 3: launch_mv_rt<MV, 3, NTW, GLU, DW>(a, grid, block, stream); break;
+    case 4: launch_mv_rt<MV, 4, NTW, GLU, DW>(a, grid, block, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1361,10 +1276,17 @@ static void launch_dot_rt_dw(const GemmArgs& a, hipStream_t stream) {
   constexpr int KBS = KB < 4 ? KB : 4;
   const dim3 grid((unsigned)(a.N / 16 / NT)), block(64 * DW);
   const int64_t per = (a.K / kKPair + DW - 1) / DW;
-  if (KBS < KB && per < KB)
+  const bool short_range = KBS < KB && per < KB;
+  if (a.psum) {   // the diagnostic instance of the same batch size
+    if (short_range)
+      gemm_decode_dot_kernel<MR, 0, KBS, NT, false, DW, true><<<grid, block, 0, stream>>>(a);
+    else
+      gemm_decode_dot_kernel<MR, 0, KB, NT, false, DW, true><<<grid, block, 0, stream>>>(a);
+  } else if (short_range) {
     gemm_decode_dot_kernel<MR, RT, KBS, NT, GLU, DW><<<grid, block, 0, stream>>>(a);
-  else
+  } else {
     gemm_decode_dot_kernel<MR, RT, KB, NT, GLU, DW><<<grid, block, 0, stream>>>(a);
+  }
 }
 
 template <int MR, int RT, int NT, bool GLU>
@@ -1426,6 +1348,10 @@ template <int WM, int WN, int TM, int TN, int SPL, bool GLU, int OCC, int KS>
 static hipError_t launch_tiled_spl(const GemmArgs& a, int64_t mt, int64_t nt, dim3 grid, dim3 block,
                                    hipStream_t stream) {
   constexpr int NS = OCC >= 3 ? 3 : 4;
+  if (a.psum) {   // the diagnostic instance of this tile shape and variant
+    gemm_tiled_kernel<WM, WN, TM, TN, 0, NS, 1, false, OCC, KS, true><<<grid, block, 0, stream>>>(a, mt, nt);
+    return hipGetLastError();
+  }
   switch (a.R / 16) {
     case 0: gemm_tiled_kernel<WM, WN, TM, TN, 0, NS, SPL, GLU, OCC, KS><<<grid, block, 0, stream>>>(a, mt, nt); break;
     case 1: gemm_tiled_kernel<WM, WN, TM, TN, 1, NS, SPL, GLU, OCC, KS><<<grid, block, 0, stream>>>(a, mt, nt); break;
@@ -1605,30 +1531,12 @@ static hipError_t launch_tiled_pick(const GemmArgs& a, int cfg, bool lean, hipSt
   return hipErrorInvalidValue;   // no tile shape fits, or one that cannot pair (gate, up) tiles
 }
 
-template <int TM, int TN, bool PSUM>
-static hipError_t launch_generic_rt(const GemmArgs& a, int64_t mt_base, int64_t mt_end,
-                                    int64_t nt_base, int64_t nt_end, int32_t* psum,
-                                    int64_t psum_nc, hipStream_t stream) {
-  const int64_t mtiles = mt_end - mt_base, ntiles = nt_end - nt_base;
-  dim3 grid((unsigned)((ntiles + 2 * TN - 1) / (2 * TN)), (unsigned)((mtiles + 2 * TM - 1) / (2 * TM)));
-  switch (PSUM ? 0 : a.R / 16) {
-    case 0: gemm_generic_kernel<TM, TN, 0, PSUM><<<grid, 256, 0, stream>>>(a, mt_base, mt_end, nt_base, nt_end, psum, psum_nc); break;
-    case 1: gemm_generic_kernel<TM, TN, 1, PSUM><<<grid, 256, 0, stream>>>(a, mt_base, mt_end, nt_base, nt_end, psum, psum_nc); break;
-    case 2: gemm_generic_kernel<TM, TN, 2, PSUM><<<grid, 256, 0, stream>>>(a, mt_base, mt_end, nt_base, nt_end, psum, psum_nc); break;
-    case 3: gemm_generic_kernel<TM, TN, 3, PSUM><<<grid, 256, 0, stream>>>(a, mt_base, mt_end, nt_base, nt_end, psum, psum_nc); break;
-    case 4: gemm_generic_kernel<TM, TN, 4, PSUM><<<grid, 256, 0, stream>>>(a, mt_base, mt_end, nt_base, nt_end, psum, psum_nc); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
 int choose_variant(int64_t M, int64_t N, int64_t K, int R) {
   (void)N; (void)K; (void)R;
   return M <= 16 ? kDecode : kPrefill;
 }
 
 hipError_t launch_gemm(const GemmArgs& a, int variant, hipStream_t stream) {
-  const int64_t mt = round_up16(a.M) / 16, nt = a.N / 16;
   switch (variant) {
     case kDecode:
       return launch_decode(a, stream);
@@ -1640,13 +1548,8 @@ hipError_t launch_gemm(const GemmArgs& a, int variant, hipStream_t stream) {
         return a.glu ? launch_tiled_pick<true>(a, cfg, lean, stream) : launch_tiled_pick<false>(a, cfg, lean, stream);
       }
     default:
-      return launch_generic_rt<2, 2, false>(a, 0, mt, 0, nt, nullptr, 0, stream);
+      return hipErrorInvalidValue;
   }
-}
-
-hipError_t launch_group_psums(const GemmArgs& a, int64_t m0, int64_t mc, int64_t n0,
-                              int64_t nc, int32_t* out, hipStream_t stream) {
-  return launch_generic_rt<2, 2, true>(a, m0 / 16, (m0 + mc) / 16, n0 / 16, (n0 + nc) / 16, out, nc, stream);
 }
 
 }  // namespace w4a4

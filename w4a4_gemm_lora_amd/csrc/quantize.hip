@@ -265,6 +265,21 @@ __global__ __launch_bounds__(NW * 64) void quantize_rows_kernel(
   }
 }
 
+// Sixteen waves leave each lane 128 registers: enough for the plain pass up
+// to rank 32 and for the RMSNorm pass (whose phase-1 fp64 state stays live)
+// up to rank 16; beyond, the instances would spill, so they are not built.
+constexpr int max_rank_16_waves(bool norm) { return norm ? 16 : 32; }
+
+template <int RT, int NW, bool NORM>
+static void launch_quantize_rt(dim3 grid, dim3 block, hipStream_t stream, const uint16_t* src, int64_t ld,
+                               int64_t rows, int64_t rows_padded, int64_t K, const uint16_t* ldown_packed,
+                               uint8_t* codes, uint16_t* scales, float* lora_part, int rh,
+                               const uint16_t* gamma, double eps) {
+  if constexpr (NW < 16 || 16 * RT <= max_rank_16_waves(NORM))
+    quantize_rows_kernel<RT, NW, NORM><<<grid, block, 0, stream>>>(src, ld, rows, rows_padded, K, ldown_packed,
+                                                                   codes, scales, lora_part, rh, gamma, eps);
+}
+
 template <int NW, bool NORM>
 static hipError_t launch_quantize_nw(const uint16_t* src, int64_t ld, int64_t rows,
                                      int64_t rows_padded, int64_t K, int R, int ks,
@@ -275,12 +290,13 @@ static hipError_t launch_quantize_nw(const uint16_t* src, int64_t ld, int64_t ro
   int rh = 16;
   while (rh > 8 && rows_padded / 16 * (16 / rh) * ks < 256) rh /= 2;
   dim3 grid((unsigned)(rows_padded / 16 * (16 / rh)), (unsigned)ks), block(64 * NW);
+  if (NW == 16 && R > max_rank_16_waves(NORM)) return hipErrorInvalidValue;   // not built (see above)
   switch (R / 16) {
-    case 0: quantize_rows_kernel<0, NW, NORM><<<grid, block, 0, stream>>>(src, ld, rows, rows_padded, K, ldown_packed, codes, scales, lora_part, rh, gamma, eps); break;
-    case 1: quantize_rows_kernel<1, NW, NORM><<<grid, block, 0, stream>>>(src, ld, rows, rows_padded, K, ldown_packed, codes, scales, lora_part, rh, gamma, eps); break;
-    case 2: quantize_rows_kernel<2, NW, NORM><<<grid, block, 0, stream>>>(src, ld, rows, rows_padded, K, ldown_packed, codes, scales, lora_part, rh, gamma, eps); break;
-    case 3: quantize_rows_kernel<3, NW, NORM><<<grid, block, 0, stream>>>(src, ld, rows, rows_padded, K, ldown_packed, codes, scales, lora_part, rh, gamma, eps); break;
-    case 4: quantize_rows_kernel<4, NW, NORM><<<grid, block, 0, stream>>>(src, ld, rows, rows_padded, K, ldown_packed, codes, scales, lora_part, rh, gamma, eps); break;
+    case 0: launch_quantize_rt<0, NW, NORM>(grid, block, stream, src, ld, rows, rows_padded, K, ldown_packed, codes, scales, lora_part, rh, gamma, eps); break;
+    case 1: launch_quantize_rt<1, NW, NORM>(grid, block, stream, src, ld, rows, rows_padded, K, ldown_packed, codes, scales, lora_part, rh, gamma, eps); break;
+    case 2: launch_quantize_rt<2, NW, NORM>(grid, block, stream, src, ld, rows, rows_padded, K, ldown_packed, codes, scales, lora_part, rh, gamma, eps); break;
+    case 3: launch_quantize_rt<3, NW, NORM>(grid, block, stream, src, ld, rows, rows_padded, K, ldown_packed, codes, scales, lora_part, rh, gamma, eps); break;
+    case 4: launch_quantize_rt<4, NW, NORM>(grid, block, stream, src, ld, rows, rows_padded, K, ldown_packed, codes, scales, lora_part, rh, gamma, eps); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -294,8 +310,8 @@ static hipError_t launch_quantize_nwsel(const uint16_t* src, int64_t ld, int64_t
                                         double eps, int64_t wgs, int64_t kp_per_wg, hipStream_t stream) {
   // waves per workgroup: as many as the k-pairs of a workgroup allow (<= 16),
   // but 8 when there are enough row tiles to fill the GPU anyway, and at
-  // ranks above 32 (16 waves leave 128 VGPRs, which rank 48 and 64 exceed)
-  if (kp_per_wg >= 16 && wgs < 256 && R <= 32)
+  // ranks whose 16-wave instance would not fit its registers
+  if (kp_per_wg >= 16 && wgs < 256 && R <= max_rank_16_waves(NORM))
     return launch_quantize_nw<16, NORM>(src, ld, rows, rows_padded, K, R, ks, ldown_packed, codes, scales, lora_part, gamma, eps, stream);
   if (kp_per_wg >= 8)
     return launch_quantize_nw<8, NORM>(src, ld, rows, rows_padded, K, R, ks, ldown_packed, codes, scales, lora_part, gamma, eps, stream);

@@ -127,15 +127,23 @@ struct GemmArgs {
   // L_up and [glu_tlo, R/16) the up projection's (blocks wholly inside the
   // other half are zero by the packing and are skipped)
   int glu_tlo = 0, glu_thi = 0;
+  // Diagnostic group sums (psum != nullptr): the launch runs the kernel and
+  // tile shape w4a4_linear would run for this shape, with the per-group
+  // epilogue swapped for a store of the exact integer sums P of every 16 x 16
+  // tile inside the window rows [ps_m0, ps_m0 + ps_mc) x columns [ps_n0,
+  // ps_n0 + ps_nc) into psum[(row - ps_m0) * ps_nc + (col - ps_n0)][K / 64];
+  // nothing else is written (y is not touched).
+  int32_t* psum = nullptr;
+  int64_t ps_m0 = 0, ps_mc = 0, ps_n0 = 0, ps_nc = 0;
 };
 
-enum Variant { kGeneric = 0, kDecode = 1, kPrefill = 2 };
+enum Variant { kDecode = 1, kPrefill = 2 };
 
 int choose_variant(int64_t M, int64_t N, int64_t K, int R);
 
+// Y (a.psum == nullptr) or the diagnostic group sums (a.psum set) of one
+// layer; the kernel, its tile shape and variant depend only on the shape (and
+// the W4A4_TILED_* tuning overrides), never on which of the two is asked.
 hipError_t launch_gemm(const GemmArgs& a, int variant, hipStream_t stream);
-
-hipError_t launch_group_psums(const GemmArgs& a, int64_t m0, int64_t mc, int64_t n0,
-                              int64_t nc, int32_t* out, hipStream_t stream);
 
 }  // namespace w4a4

@@ -125,7 +125,7 @@ def test_glu_strided_output(M):
     assert np.all(np.isnan(h[:, N:].astype(np.float64)))
 
 
-@pytest.mark.parametrize("cfg,lean", [(c, "0") for c in range(9)] + [(c, "1") for c in (0, 1, 2, 3, 8)])
+@pytest.mark.parametrize("cfg,lean", [(c, "0") for c in range(10)] + [(c, "1") for c in (0, 1, 2, 3, 8)])
 def test_glu_every_tile_shape(cfg, lean, monkeypatch):
     """Each M > 16 tile shape forced in turn, in the 4-stage and (where it
     exists) the lean variant (shapes whose waves hold an odd number of

@@ -301,8 +301,8 @@ def test_small_m_decode_shapes(M, K, N, R):
     assert np.all(np.isnan(run.host_y()[M:].astype(np.float64)))
 
 
-@pytest.mark.parametrize("cfg,K,R", [(c, 512, 32) for c in range(9)] + [(c, 2048, 32) for c in range(9)] +
-                         [(c, 2048, 64) for c in range(9)])
+@pytest.mark.parametrize("cfg,K,R", [(c, 512, 32) for c in range(10)] + [(c, 2048, 32) for c in range(10)] +
+                         [(c, 2048, 64) for c in range(10)])
 def test_every_tile_shape(cfg, K, R, monkeypatch):
     """Each M > 16 tile shape (forced) on a shape with ragged row and column
     edges for all of them: M = 130 (9 row tiles), N = 208 (13 column tiles);
@@ -478,10 +478,14 @@ def test_svdquant_checkpoint_layer():
 
 @pytest.mark.parametrize("norm", [False, True])
 def test_layer_graph_buckets_replay_eager(norm):
-    """Bucketed native graphs (LayerGraphs over w4a4_graph_*): requests of several row
-    counts, each padded to its bucket and replayed, give bit for bit the eager
-    two-call result on the same rows; buckets are replayed repeatedly with new
-    data, with the program's own eager work and synchronizations in between."""
+    """Bucketed native graphs (LayerGraphs over w4a4_graph_*; "W4A4 CUDA
+    Kernel for Voice Clone", section 4.3: pad to the bucket, copy in,
+    replay): requests of several row counts, each padded to its bucket and
+    replayed, give bit for bit the eager two-call result on the same rows and
+    are within the layer bar of the oracle on the request's own rows
+    (RMSNorm variant: the oracle's norm-then-layer); buckets are replayed
+    repeatedly with new data, with the program's own eager work and
+    synchronizations in between, every other replay on a side stream."""
     torch = _torch()
     rng = np.random.default_rng(16)
     N, K, R = 96, 1024, 32
@@ -491,9 +495,12 @@ def test_layer_graph_buckets_replay_eager(norm):
                            bias=_to_dev(case["bias"]))
     gamma = _to_dev(rng.uniform(0.5, 2.0, K).astype(np.float16)) if norm else None
     graphs = W.LayerGraphs(layer, [1, 4, 16, 64], gamma=gamma, eps=1e-6)   # a chain of one layer
+    side = torch.cuda.Stream()
+    g_host = None if gamma is None else gamma.cpu().numpy()
     try:
         for it, M in enumerate([1, 3, 16, 40, 1, 64, 3, 40]):
-            x = _to_dev((rng.standard_normal((M, K)) * (1 + it)).astype(np.float16))
+            xh = (rng.standard_normal((M, K)) * (1 + it)).astype(np.float16)
+            x = _to_dev(xh)
             # eager reference at the bucket size (rows past M zero, as the graph sees them)
             B = graphs.bucket_for(M)
             xp = torch.zeros((B, K), dtype=torch.float16, device="cuda")
@@ -506,10 +513,13 @@ def test_layer_graph_buckets_replay_eager(norm):
                 W.w4a4_quantize_act(B, K, R, xp, layer.wblob, act)
             W.w4a4_linear(B, N, K, R, act, layer.wblob, y_ref)
             torch.cuda.synchronize()
-            y = graphs.run(x)
+            y = graphs.run(x, stream=side if it % 2 else None)
             torch.cuda.synchronize()
-            _say(f"[graph] norm={norm} M={M} bucket={B}")
+            _say(f"[graph] norm={norm} M={M} bucket={B} stream={'side' if it % 2 else 'current'}")
             assert torch.equal(y, y_ref[:M]), f"replay {it} (M={M}) differs from eager"
+            xin = xh if gamma is None else O.rms_norm(xh, g_host, 1e-6)
+            ref = O.linear(xin, case["lora_down"], case["lora_up"], case["col_scale"], case["bias"], w16=case["w"])
+            _check_y(y.cpu().numpy(), ref["y"], f"graph replay M={M}", y64=ref["y64"], ref=ref, case=case)
     finally:
         graphs.close()
 
@@ -518,15 +528,18 @@ def test_graph_capture_of_a_layer_chain():
     """w4a4_graph_begin/end around a chain of three layers (the second and
     third reading the previous output) captured on a side stream: every
     replay, with new input written between replays and eager work in between,
-    equals the eager chain bit for bit."""
+    equals the eager chain bit for bit, and each layer's replayed output is
+    within the layer bar of the oracle applied to that layer's replayed
+    input."""
     import ctypes
     torch = _torch()
     lib = W.load_library()
     M, K = 16, 1024
     dims = [(K, 1024, 32), (1024, 1024, 16), (1024, 2048, 0)]   # (K_in, N, R)
-    layers, acts, ys = [], [], []
+    layers, acts, ys, cases = [], [], [], []
     for j, (k_in, n, r) in enumerate(dims):
         c = workloads.random_case(16, k_in, n, r, seed=4400 + j)
+        cases.append(c)
         layers.append(W.PackedLinear(n, k_in, r, w_fp16=_to_dev(c["w"]),
                                      lora_down=_to_dev(c["lora_down"]) if r else None,
                                      lora_up=_to_dev(c["lora_up"]) if r else None,
@@ -559,5 +572,13 @@ def test_graph_capture_of_a_layer_chain():
             assert lib.w4a4_graph_launch(h, torch.cuda.current_stream().cuda_stream) == 0
             torch.cuda.synchronize()
             assert torch.equal(ys[-1], ref), f"replay {it} differs from the eager chain"
+            inp = x.cpu().numpy()
+            for j, (c, y) in enumerate(zip(cases, ys)):
+                r = dims[j][2]
+                o = O.linear(inp, c["lora_down"] if r else None, c["lora_up"] if r else None, c["col_scale"],
+                             c["bias"], w16=c["w"])
+                out = y.cpu().numpy()
+                _check_y(out, o["y"], f"chain replay {it} layer {j}", y64=o["y64"], ref=o, case=c)
+                inp = out
     finally:
         lib.w4a4_graph_destroy(h)

@@ -64,7 +64,7 @@ def _forced(monkeypatch, cfg, lean, ksplit):
     monkeypatch.setenv("W4A4_TILED_KSPLIT", str(int(ksplit)))
 
 
-TILED_INSTANCES = ([(c, False, False) for c in range(9)] + [(c, True, False) for c in (0, 1, 2, 3, 5, 8)]
+TILED_INSTANCES = ([(c, False, False) for c in range(10)] + [(c, True, False) for c in (0, 1, 2, 3, 5, 8)]
                    + [(c, False, True) for c in (3, 4, 5, 7, 8)])
 
 

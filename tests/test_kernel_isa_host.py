@@ -88,6 +88,7 @@ def test_epilogue_loads_follow_the_first_copies(asm):
 KDESC = re.compile(r"^\s*\.amdhsa_kernel (\S+)$")
 TILED = re.compile(r"gemm_tiled_kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELb(\d)"
                    r"ELi(\d+)ELi(\d+)ELb(\d)E")
+WIDE = re.compile(r"gemm_wide_kernelILi(\d+)ELi(\d+)ELb(\d)ELb(\d)E")
 DECODE = re.compile(r"gemm_decode_(?:dot_)?kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELb(\d)ELi(\d+)ELb(\d)E")
 LDS_PER_CU = 160 * 1024
 
@@ -123,8 +124,9 @@ def test_every_instance_fits_its_occupancy(asm):
     registers and OCC / (WM WN KS / 4) workgroups per CU by LDS; a decode
     instance (DW waves, bound 16 / DW) keeps 4 waves per SIMD.  The
     diagnostic (group-sum) instances are built for one workgroup per CU and
-    checked against that."""
-    seen = {"tiled": 0, "decode": 0, "other": 0}
+    checked against that.  The wide kernel (4 waves) is built for two
+    workgroups per CU."""
+    seen = {"tiled": 0, "wide": 0, "decode": 0, "other": 0}
     for src, text in asm.items():
         for name, d in _descriptors(text).items():
             assert d["private_segment_fixed_size"] == 0, f"{name}: {d['private_segment_fixed_size']} B of scratch"
@@ -138,6 +140,13 @@ def test_every_instance_fits_its_occupancy(asm):
                 assert (want // per_wg) * lds <= LDS_PER_CU, (name, lds, want)
                 seen["tiled"] += 1
                 continue
+            m = WIDE.search(name)
+            if m:   # 4 waves, built for 2 workgroups per CU (1 for the diagnostic instance)
+                blocks = 1 if int(m.group(4)) else 2
+                assert _waves_per_simd(d) >= blocks, (name, d["next_free_vgpr"])
+                assert blocks * lds <= LDS_PER_CU, (name, lds)
+                seen["wide"] += 1
+                continue
             m = DECODE.search(name)
             if m:
                 dw, psum = int(m.group(6)), int(m.group(7))
@@ -148,4 +157,4 @@ def test_every_instance_fits_its_occupancy(asm):
                 continue
             assert lds <= LDS_PER_CU, (name, lds)
             seen["other"] += 1
-    assert seen["tiled"] >= 100 and seen["decode"] >= 40 and seen["other"] >= 5, seen
+    assert seen["tiled"] >= 100 and seen["wide"] >= 10 and seen["decode"] >= 40 and seen["other"] >= 5, seen

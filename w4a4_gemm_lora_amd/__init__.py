@@ -405,13 +405,22 @@ class LayerGraphs:
         raise ValueError(f"{M} rows exceed the largest bucket {self.buckets[-1]}")
 
     def run(self, x, stream=None):
+        """Replay the bucket's graph for x on `stream` (default: the current
+        stream).  The copy into the bucket buffer and the zeroing of its
+        padding rows are enqueued on that same stream, ahead of the replay."""
+        import torch
         M = x.shape[0]
         B = self.bucket_for(M)
         xb, _, ys = self._bufs[B]
-        xb[:M].copy_(x)
-        if M < B:
-            xb[M:].zero_()
-        _check(load_library().w4a4_graph_launch(self._g[B], _stream(stream)), "w4a4_graph_launch")
+        st = torch.cuda.current_stream() if stream is None else (
+            stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(stream))
+        if st != torch.cuda.current_stream():
+            st.wait_stream(torch.cuda.current_stream())   # x was produced on the current stream
+        with torch.cuda.stream(st):
+            xb[:M].copy_(x)
+            if M < B:
+                xb[M:].zero_()
+        _check(load_library().w4a4_graph_launch(self._g[B], st.cuda_stream), "w4a4_graph_launch")
         return ys[-1][:M]
 
     def close(self):

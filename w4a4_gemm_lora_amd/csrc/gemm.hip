@@ -768,6 +768,33 @@ __global__ __launch_bounds__(64 * DW, PSUM ? 1 : 16 / DW) void gemm_decode_dot_k
 // ---------------------------------------------------------------------------
 constexpr int kTileGroupRows = 8;
 
+// Workgroup -> (row band bm, column band bn) of an nbm x nbn grid of
+// workgroup tiles (32-bit: the launchers keep nbm * nbn below 2^31).
+// Dispatch places workgroup b on XCD b % 8; each XCD gets a contiguous range
+// of a grouped order, in which kTileGroupRows row bands advance together and
+// column bands are the outer index, so a B column band is reused by the
+// whole group while the group's A bands stay in that XCD's L2.  (With nbm >
+// kTileGroupRows, nbn < nblk / kTileGroupRows, so group_size fits.)
+__device__ __forceinline__ void map_workgroup(uint32_t nbm, uint32_t nbn, uint32_t& bm, uint32_t& bn) {
+  const uint32_t nblk = nbm * nbn;
+  uint32_t b = blockIdx.x;
+  {
+    const uint32_t per_xcd = nblk >> 3, extra = nblk & 7;
+    const uint32_t xcd = b & 7, local = b >> 3;
+    b = xcd * per_xcd + (xcd < extra ? xcd : extra) + local;
+  }
+  uint32_t first_bm = 0, in_g = b, gm = nbm;
+  if (nbm > (uint32_t)kTileGroupRows) {
+    const uint32_t group_size = (uint32_t)kTileGroupRows * nbn;
+    const uint32_t grp = b / group_size;
+    first_bm = grp * kTileGroupRows;
+    in_g = b - grp * group_size;
+    gm = nbm - first_bm < (uint32_t)kTileGroupRows ? nbm - first_bm : (uint32_t)kTileGroupRows;
+  }
+  bn = in_g / gm;
+  bm = first_bm + (in_g - bn * gm);
+}
+
 // PSUM: the diagnostic instance -- the same staging, waits, expansion and
 // integer MFMAs, with the per-group scale-accumulate replaced by a store of
 // each group's exact sums, read back from the MFMA's 3.0f-offset result as
@@ -800,35 +827,10 @@ __global__ __launch_bounds__(WM * WN * KS * 64, PSUM ? 1 : OCC) void gemm_tiled_
   const int c = lane >> 4;
   const v4i kOffset = v4i{kOffsetBits, kOffsetBits, kOffsetBits, kOffsetBits};
 
-  // 32-bit tile arithmetic: the launcher guarantees nblk < 2^31.
   // 32-bit tile counts (the launcher keeps them below 2^31)
   const uint32_t mtc = (uint32_t)mt_count, ntc = (uint32_t)nt_count;
-  const uint32_t nbm = (mtc + BMT - 1) / BMT, nbn = (ntc + BNT - 1) / BNT;
-  const uint32_t nblk = nbm * nbn;
-  uint32_t b = blockIdx.x;
-  {
-    // dispatch places workgroup b on XCD b % 8; give each XCD a contiguous range
-    const uint32_t per_xcd = nblk >> 3, extra = nblk & 7;
-    const uint32_t xcd = b & 7, local = b >> 3;
-    b = xcd * per_xcd + (xcd < extra ? xcd : extra) + local;
-  }
-  // Grouped order inside each XCD's range: kTileGroupRows row bands advance
-  // together and column tiles are the outer index, so a B column tile is
-  // reused by the whole group while the group's A band stays in L2.  (With
-  // nbm > kTileGroupRows, nbn < nblk / kTileGroupRows, so group_size fits.)
   uint32_t bm, bn;
-  {
-    uint32_t first_bm = 0, in_g = b, gm = nbm;
-    if (nbm > (uint32_t)kTileGroupRows) {
-      const uint32_t group_size = (uint32_t)kTileGroupRows * nbn;
-      const uint32_t grp = b / group_size;
-      first_bm = grp * kTileGroupRows;
-      in_g = b - grp * group_size;
-      gm = nbm - first_bm < (uint32_t)kTileGroupRows ? nbm - first_bm : (uint32_t)kTileGroupRows;
-    }
-    bn = in_g / gm;
-    bm = first_bm + (in_g - bn * gm);
-  }
+  map_workgroup((mtc + BMT - 1) / BMT, (ntc + BNT - 1) / BNT, bm, bn);
   const uint32_t mt0 = bm * BMT, nt0 = bn * BNT;
   const int64_t KPT = g.K / kKPair;   // k-pairs of the whole K
   const int64_t KP = KPT / KS;        // k-pairs of this wave's part
@@ -1204,6 +1206,274 @@ __global__ __launch_bounds__(WM * WN * KS * 64, PSUM ? 1 : OCC) void gemm_tiled_
   }
 }
 
+// ---------------------------------------------------------------------------
+// Wide kernel (large launches): 2 x 2 waves of 8 x 4 tiles of 16 x 16 (a
+// 256 x 128 workgroup tile), staged like the tiled kernel: a 3-deep LDS ring
+// of global_load_lds copies, exact vmcnt waits, bare barriers.  The four
+// column tiles of one wave row tile i share one 16-register accumulator,
+// laid out as the output of the 4-block v_mfma_f32_16x16x4_4b_f16 (block b
+// = column tile b, each block in the 16 x 16 accumulator layout), so per
+// k-pair and row tile one such MFMA removes both groups' offsets from all
+// four tiles and, per group, one more forms the four tiles' exact scale
+// products s_x * s_w: 3 MFMAs where the tiled kernel issues 12 of the 4x4x4
+// kind (each 4-block MFMA costs what four 4x4x4 ones do, without their
+// kind-switch stalls).  Eight row tiles per wave expand each B tile once per
+// 8 row tiles: 2.25 expansion VALU ops per 16 x 16 x 64 product instead of 3.
+// The epilogue operands (affine, L_up, lora_act partials) are loaded after
+// the K loop.  PSUM: the diagnostic instance (see gemm_tiled_kernel).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ v4f tile4(const v16f& a, int j) {
+  return v4f{a[4 * j], a[4 * j + 1], a[4 * j + 2], a[4 * j + 3]};
+}
+
+__device__ __forceinline__ void set_tile4(v16f& a, int j, v4f t) {
+  a[4 * j] = t[0];
+  a[4 * j + 1] = t[1];
+  a[4 * j + 2] = t[2];
+  a[4 * j + 3] = t[3];
+}
+
+__device__ __forceinline__ v16f mfma_4b_f16(v4h a, v4h b, v16f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f16(a, b, c, 0, 0, 0);
+}
+
+constexpr int kWideTM = 8, kWideTN = 4;
+// The gated epilogue of the wide kernel fits its 256 registers up to rank 32
+// (16 per projection); above, its instances would spill and are not built.
+constexpr int kWideMaxGatedRank = 32;
+
+template <int RT, int SPL, bool GLU, bool PSUM = false>
+__global__ __launch_bounds__(256, PSUM ? 1 : 2) void gemm_wide_kernel(GemmArgs g, int64_t mt_count,
+                                                                      int64_t nt_count) {
+  static_assert(!PSUM || (RT == 0 && SPL == 1 && !GLU), "the diagnostic instance has no epilogue");
+  constexpr int WN = 2, TM = kWideTM, TN = kWideTN, NW = 4, NS = 3;
+  constexpr int BMT = 2 * TM, BNT = WN * TN;               // 16 row tiles, 8 column tiles
+  constexpr int CHUNKS = BMT + BNT;                        // 1 KB operand tiles per stage
+  constexpr int CPW = CHUNKS / NW;                         // operand copies per wave per stage
+  static_assert(CPW * NW == CHUNKS, "every wave copies the same number of tiles");
+  constexpr int OPS = CPW + 1;                             // + one scale copy
+  constexpr int SCALE_SLOTS = (CHUNKS * 64 + kTileBytes - 1) / kTileBytes;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NS][CHUNKS + SCALE_SLOTS][kTileBytes];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int c = lane >> 4;
+  const v4i kOffset = v4i{kOffsetBits, kOffsetBits, kOffsetBits, kOffsetBits};
+  const uint32_t mtc = (uint32_t)mt_count, ntc = (uint32_t)nt_count;
+  uint32_t bm, bn;
+  map_workgroup((mtc + BMT - 1) / BMT, (ntc + BNT - 1) / BNT, bm, bn);
+  const uint32_t mt0 = bm * BMT, nt0 = bn * BNT;
+  const int64_t KP = g.K / kKPair;
+
+  // operand tile q of a stage: q < BMT -> A tile mt0 + q, else B tile nt0 +
+  // q - BMT; tiles past the edge re-read the last valid tile (never stored)
+  auto tile_index = [&](int q) -> int64_t {
+    if (q < BMT) {
+      const uint32_t t = mt0 + q;
+      return t < mtc ? t : mtc - 1;
+    }
+    const uint32_t t = nt0 + (q - BMT);
+    return t < ntc ? t : ntc - 1;
+  };
+  const uint8_t* src[CPW];
+#pragma unroll
+  for (int u = 0; u < CPW; ++u) {
+    const int q = wave * CPW + u;
+    src[u] = (q < BMT ? g.xq : g.wq) + (size_t)tile_index(q) * KP * kTileBytes;
+  }
+  // lanes l < 4 CPW copy 16 B of the scales of tile wave * CPW + l / 4
+  const uint8_t* ssrc;
+  {
+    const int q = wave * CPW + ((lane >> 2) < CPW ? (lane >> 2) : CPW - 1);
+    ssrc = reinterpret_cast<const uint8_t*>(q < BMT ? g.sx : g.sw) + (size_t)tile_index(q) * KP * 64 +
+           (lane & 3) * 16;
+  }
+  const uint32_t lane_off = lane * 16u;
+  auto issue_copy = [&](int stage, int64_t p) {
+#pragma unroll
+    for (int u = 0; u < CPW; ++u) {
+      const uint8_t* sp = src[u];
+      __builtin_amdgcn_global_load_lds(sp + (size_t)p * kTileBytes + lane_off,
+                                       (lds_void*)&lds[stage][wave * CPW + u][0], 16, 0, 0);
+    }
+    if (lane < 4 * CPW)
+      __builtin_amdgcn_global_load_lds(ssrc + (size_t)p * 64, (lds_void*)(&lds[stage][CHUNKS][0] + wave * CPW * 64),
+                                       16, 0, 0);
+  };
+
+  v16f acc[TM];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) acc[i] = v16f{};
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < KP) issue_copy(s, s);
+
+  int st = 0, st_next = NS - 1;
+  for (int64_t p = 0; p < KP; ++p) {
+    asm volatile("" ::: "memory");
+    if (p + 1 < KP) W4A4_WAIT_VMCNT(OPS);   // stage p + 1 may stay in flight
+    else W4A4_WAIT_VMCNT(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (p + NS - 1 < KP) issue_copy(st_next, p + NS - 1);
+
+    const uint8_t* sl = &lds[st][CHUNKS][0];
+    // the wave's column tiles, both groups, expanded once for its 8 row tiles
+    v4i Be[TN][2];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const v4u r = *reinterpret_cast<const v4u*>(&lds[st][BMT + wn * TN + j][lane * 16]);
+      Be[j][0] = expand_group(r[0], r[1]);
+      Be[j][1] = expand_group(r[2], r[3]);
+    }
+    // B operands of the 4-block MFMAs: block b = the wave's column tile b,
+    // lane l of block b = column l & 15 (s_w of both groups in one dword)
+    const uint32_t swd = *reinterpret_cast<const uint32_t*>(sl + (BMT + wn * TN + c) * 64 + (lane & 15) * 4);
+    const v4h sb[2] = {__builtin_bit_cast(v4h, v2u{swd & 0x0000FFFFu, 0u}),
+                       __builtin_bit_cast(v4h, v2u{swd & 0xFFFF0000u, 0u})};
+    const v4h ob = __builtin_bit_cast(v4h, v2u{swd, swd});
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const v4u ra = *reinterpret_cast<const v4u*>(&lds[st][wm * TM + i][lane * 16]);
+      // s_x of row lane & 15 of row tile i, both groups (every block's A)
+      const uint32_t sxd = *reinterpret_cast<const uint32_t*>(sl + (wm * TM + i) * 64 + (lane & 15) * 4);
+      if constexpr (!PSUM) {
+        // acc' -= 3 (S_0 + S_1) on the four tiles (see kOffsetBits, offset_tile)
+        typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+        const uint32_t nsx = sxd ^ 0x80008000u;
+        const v2h nsxh = __builtin_bit_cast(v2h, nsx);
+        acc[i] = mfma_4b_f16(__builtin_bit_cast(v4h, v2u{nsx, __builtin_bit_cast(uint32_t, nsxh + nsxh)}), ob,
+                             acc[i]);
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const v4i Ae = expand_group(ra[2 * h], ra[2 * h + 1]);
+        v16f S;
+        if constexpr (!PSUM) S = mfma_4b_f16(__builtin_bit_cast(v4h, v2u{sxd, 0u}), sb[h], v16f{});
+        v4i P[TN];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) P[j] = mfma_i8_16x16x64(Ae, Be[j][h], kOffset);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          if constexpr (PSUM) {
+            const uint32_t mt = mt0 + wm * TM + i, nt = nt0 + wn * TN + j;
+            if (mt < mtc && nt < ntc)
+              store_psum_tile(g, (P[j] - kOffset) >> 8, (int64_t)mt * 16, (int64_t)nt * 16, 2 * p + h, lane);
+          } else {
+            const v4f Pf = __builtin_bit_cast(v4f, P[j]);   // whole-vector cast
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) acc[i][4 * j + ii] = fmaf(S[4 * j + ii], Pf[ii], acc[i][4 * j + ii]);
+          }
+        }
+      }
+    }
+    st = st + 1 == NS ? 0 : st + 1;
+    st_next = st_next + 1 == NS ? 0 : st_next + 1;
+  }
+  if constexpr (PSUM) return;
+
+  // acc holds main * 2^-14 (see kOffsetBits)
+#pragma unroll
+  for (int i = 0; i < TM; ++i) acc[i] *= 16384.0f;
+  // LoRA-up, one rank block at a time (its L_up fragments of the wave's
+  // column tiles, then per row tile the lora_act rows -- partials summed in
+  // order, split fp16 hi + lo -- times each fragment); gated layers skip the
+  // other half's zero blocks
+  if constexpr (RT > 0) {
+    const size_t part = (size_t)round_up16(g.M) * g.R;
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      v4h lu_f[TN];
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        lu_f[j] = *reinterpret_cast<const v4h*>(g.lup + (((size_t)tile_index(BMT + wn * TN + j) * RT + t) * 64 +
+                                                         lane) * 4);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const float* lp = g.la + (size_t)(tile_index(wm * TM + i) * 16 + (lane & 15)) * g.R + t * 16 + c * 4;
+        v4f l4 = *reinterpret_cast<const v4f*>(lp);
+#pragma unroll
+        for (int jj = 1; jj < SPL; ++jj)
+          if (jj < g.ks) l4 += *reinterpret_cast<const v4f*>(lp + jj * part);
+        v4h hi, lo;
+        split_f16(l4, hi, lo);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          if (GLU && ((j & 1) ? t < g.glu_tlo : t >= g.glu_thi)) continue;
+          v4f a4 = tile4(acc[i], j);
+          a4 = mfma_f16_16x16x16(hi, lu_f[j], a4);
+          a4 = mfma_f16_16x16x16(lo, lu_f[j], a4);
+          set_tile4(acc[i], j, a4);
+        }
+      }
+    }
+  }
+  // affine of the wave's column tiles
+  float af[TN], bf[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int64_t nt = tile_index(BMT + wn * TN + j);
+    af[j] = g.ca[nt * 16 + (lane & 15)];
+    bf[j] = g.cb[nt * 16 + (lane & 15)];
+  }
+  if constexpr (!GLU) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const uint32_t nt = nt0 + wn * TN + j;
+      if (nt >= ntc) continue;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const uint32_t mt = mt0 + wm * TM + i;
+        if (mt < mtc) store_tile4(g, tile4(acc[i], j), (int64_t)mt * 16, (int64_t)nt * 16, af[j], bf[j], lane);
+      }
+    }
+  } else {   // (gate, up) pairs: the wave's column tiles start on an even tile
+#pragma unroll
+    for (int j = 0; j < TN; j += 2) {
+      const uint32_t nt = nt0 + wn * TN + j;
+      if (nt >= ntc) continue;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const uint32_t mt = mt0 + wm * TM + i;
+        if (mt < mtc)
+          store_tile4_glu(g, tile4(acc[i], j), tile4(acc[i], j + 1), (int64_t)mt * 16, (int64_t)(nt / 2) * 16,
+                          af[j], bf[j], af[j + 1], bf[j + 1], lane);
+      }
+    }
+  }
+}
+
+template <bool GLU>
+static hipError_t launch_wide(const GemmArgs& a, hipStream_t stream) {
+  const int64_t mt = round_up16(a.M) / 16, nt = a.N / 16;
+  const int64_t nblk = ((mt + 2 * kWideTM - 1) / (2 * kWideTM)) * ((nt + 2 * kWideTN - 1) / (2 * kWideTN));
+  if (nblk >= ((int64_t)1 << 31)) return hipErrorInvalidValue;   // 32-bit tile arithmetic
+  const dim3 grid((unsigned)nblk), block(256);
+  if (a.psum) {
+    gemm_wide_kernel<0, 1, false, true><<<grid, block, 0, stream>>>(a, mt, nt);
+    return hipGetLastError();
+  }
+  const bool split = a.ks > 1;
+  switch (a.R / 16) {
+#define W4A4_WIDE_CASE(rt)                                                                              \
+  case rt:                                                                                              \
+    if constexpr (GLU && rt > kWideMaxGatedRank / 16) return hipErrorInvalidValue;                     \
+    else if (split) gemm_wide_kernel<rt, kMaxTiledLoraSplits, GLU><<<grid, block, 0, stream>>>(a, mt, nt); \
+    else gemm_wide_kernel<rt, 1, GLU><<<grid, block, 0, stream>>>(a, mt, nt);                           \
+    break;
+    W4A4_WIDE_CASE(0)
+    W4A4_WIDE_CASE(1)
+    W4A4_WIDE_CASE(2)
+    W4A4_WIDE_CASE(3)
+    W4A4_WIDE_CASE(4)
+#undef W4A4_WIDE_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 // Weight k-pairs per batch of the MFMA decode kernel, by R / 16.  Within the
 // 128-VGPR budget (with the LoRA-down partials held across the first batch)
 // small batches measured best: the per-k-pair arithmetic here is heavy enough
@@ -1392,7 +1662,9 @@ constexpr TiledCfg kTiledCfgs[] = {
     {1, 4, 3, 1, 4},   //  48 x  64
     {4, 1, 1, 2, 4},   //  64 x  32
     {4, 1, 1, 4, 4},   //  64 x  64, one row tile per wave
+    {2, 2, 8, 4, 2},   // 256 x 128, the wide kernel (gemm_wide_kernel)
 };
+constexpr int kWideCfg = 9;
 constexpr int kNumTiledCfgs = (int)(sizeof(kTiledCfgs) / sizeof(kTiledCfgs[0]));
 
 // W4A4_TILED_CFG=<index into kTiledCfgs> forces a tile shape (tuning and
@@ -1427,19 +1699,34 @@ static double tiled_cost(const TiledCfg& c, int64_t mt, int64_t nt, int64_t kp) 
   return (double)waves_per_simd * (tiles * per_tile * (double)kp + fixed);
 }
 
+// Per-tile cost of the wide kernel relative to the model's figure for its
+// shape: measured 192.6 against 209.3 us for the 128 x 128 lean kernel at
+// M = 8192, K = N = 4096, where the model puts the two within 3% of each
+// other.
+constexpr double kWideCostScale = 0.95;
+
 static int pick_tiled(int64_t M, int64_t N, int64_t K, int R, int ks, bool glu) {
   // gated output: a wave's column tiles must hold whole (gate, up) pairs
-  (void)R;
   (void)ks;
-  auto ok = [&](const TiledCfg& c) { return !glu || c.tn % 2 == 0; };
+  auto ok = [&](int i) {
+    return (!glu || kTiledCfgs[i].tn % 2 == 0) && !(glu && i == kWideCfg && R > kWideMaxGatedRank);
+  };
   const int ov = tiled_override();
-  if (ov >= 0 && ok(kTiledCfgs[ov])) return ov;
+  if (ov >= 0 && ok(ov)) return ov;
   const int64_t mt = round_up16(M) / 16, nt = N / 16, kp = K / kKPair;
   int best = -1;
   double best_c = 0;
   for (int i = 0; i < kNumTiledCfgs; ++i) {
-    if (!ok(kTiledCfgs[i])) continue;
-    const double c = tiled_cost(kTiledCfgs[i], mt, nt, kp);
+    if (!ok(i)) continue;
+    double c = tiled_cost(kTiledCfgs[i], mt, nt, kp);
+    if (i == kWideCfg) {
+      // the wide kernel keeps two workgroups per CU; with fewer a SIMD runs
+      // one wave at a time, which this loop cannot keep busy
+      const TiledCfg& w = kTiledCfgs[i];
+      const int64_t nblk = ((mt + w.wm * w.tm - 1) / (w.wm * w.tm)) * ((nt + w.wn * w.tn - 1) / (w.wn * w.tn));
+      if (nblk < 512) continue;
+      c *= kWideCostScale;
+    }
     if (best < 0 || c < best_c) {
       best_c = c;
       best = i;
@@ -1458,7 +1745,7 @@ static int pick_tiled(int64_t M, int64_t N, int64_t K, int R, int ks, bool glu) 
 // the shapes that carry large launches.
 // W4A4_TILED_LEAN=0 / 1 forces the choice where the shape has both (tuning
 // and test aid, read at every launch like W4A4_TILED_CFG).
-constexpr bool kLeanCfg[kNumTiledCfgs] = {true, true, true, true, false, true, false, false, true};
+constexpr bool kLeanCfg[kNumTiledCfgs] = {true, true, true, true, false, true, false, false, true, false};
 static bool tiled_lean(int cfg, int64_t M, int64_t N, int64_t K) {
   if (cfg < 0 || cfg >= kNumTiledCfgs || !kLeanCfg[cfg]) return false;
   const char* e = std::getenv("W4A4_TILED_LEAN");
@@ -1471,7 +1758,7 @@ static bool tiled_lean(int cfg, int64_t M, int64_t N, int64_t K) {
 // SIMD fewer than two waves, on the small tile shapes such launches pick,
 // when K has >= 16 k-pairs in an even count.  W4A4_TILED_KSPLIT=0 / 1
 // forces the choice where both exist (tuning and test aid).
-constexpr bool kKSplitCfg[kNumTiledCfgs] = {false, false, false, true, true, true, false, true, true};
+constexpr bool kKSplitCfg[kNumTiledCfgs] = {false, false, false, true, true, true, false, true, true, false};
 static bool tiled_ksplit(int cfg, int64_t M, int64_t N, int64_t K) {
   if (cfg < 0 || cfg >= kNumTiledCfgs || !kKSplitCfg[cfg]) return false;
   const int64_t kp = K / kKPair;
@@ -1486,6 +1773,7 @@ static bool tiled_ksplit(int cfg, int64_t M, int64_t N, int64_t K) {
 
 template <bool GLU>
 static hipError_t launch_tiled_pick(const GemmArgs& a, int cfg, bool lean, hipStream_t stream) {
+  if (cfg == kWideCfg) return launch_wide<GLU>(a, stream);
   if constexpr (!GLU) {
     if (!lean && tiled_ksplit(cfg, a.M, a.N, a.K)) {
       switch (cfg) {

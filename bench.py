@@ -246,9 +246,11 @@ def launch_overhead(args, W, torch, M, N, K, R, x, blobs, act, y, sh, quant):
     return 0
 
 
-def graph_avg_ms(torch, fn, n):
+def graph_avg_ms(torch, fn, n, settle_ms=100.0):
     """Average duration of one fn(i, stream) over a graph of n back-to-back
-    calls, bracketed by two events on the launch stream (3 replays)."""
+    calls, bracketed by two events on the launch stream (3 replays), after
+    replaying the graph untimed for settle_ms (the clocks follow the kind of
+    load over tens of milliseconds)."""
     gk = torch.cuda.CUDAGraph()
     with torch.cuda.graph(gk):
         cs = torch.cuda.current_stream().cuda_stream
@@ -256,6 +258,10 @@ def graph_avg_ms(torch, fn, n):
             fn(i, cs)
     gk.replay()
     torch.cuda.synchronize()
+    t_end = time.perf_counter() + settle_ms * 1e-3
+    while time.perf_counter() < t_end:
+        gk.replay()
+        torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s = torch.cuda.current_stream()
     e0.record(s)
@@ -438,17 +444,58 @@ def measured_peaks(torch, W):
 
     t_m, t_h = best_ms(mfma), best_ms(hbm)
     del buf
+
+    # one MFMA wave and one FMA wave per SIMD, alone and together
+    rit_m, rit_f = 20000, 16000
+
+    def roles(a, b, ia, ib):
+        def fn():
+            if lib.w4a4_peak_roles(a, b, ia, ib, out.data_ptr(), s.cuda_stream):
+                raise RuntimeError("w4a4_peak_roles failed")
+        return best_ms(fn)
+
+    r_m, r_f = roles(1, 0, rit_m, 0), roles(2, 0, rit_f, 0)
+    r_ff, r_mf = roles(2, 2, rit_f, rit_f), roles(1, 2, rit_m, rit_f)
+    fma_rate = 2 * lib.w4a4_peak_roles_ops(2, rit_f) / (r_ff * 1e-3) / 1e12
     return {"int8_mfma": {"unit": "TOPS", "published": PEAK_INT8_TOPS,
                           "measured": round(lib.w4a4_peak_i8_mfma_ops(iters) / (t_m * 1e-3) / 1e12, 1)},
             "hbm_read": {"unit": "GB/s", "published": PEAK_HBM_GBPS,
-                         "measured": round(nbytes / (t_h * 1e-3) / 1e9, 1)}}
+                         "measured": round(nbytes / (t_h * 1e-3) / 1e9, 1)},
+            "fp32_fma_valu": {"unit": "T lane-ops/s", "published_unpacked": PEAK_VALU_TLANEOPS,
+                              "measured": round(fma_rate, 2),
+                              "note": "two waves of independent wave64 v_fma_f32 per SIMD"},
+            "mfma_beside_fma": {"mfma_wave_alone_ms": round(r_m, 3), "fma_wave_alone_ms": round(r_f, 3),
+                                "both_on_every_simd_ms": round(r_mf, 3),
+                                "overlap_of_shorter": round((r_m + r_f - r_mf) / min(r_m, r_f), 3),
+                                "note": "one int8-MFMA wave and one fp32-FMA wave on each SIMD; overlap 1 = "
+                                        "the shorter one hidden entirely, 0 = run one after the other"}}
+
+
+def read_floor_us(torch, W, nbytes, rotate=12, n=48):
+    """The plain streaming read of nbytes (libw4a4_peaks' read kernel) timed
+    like a decode launch: a graph of n back-to-back launches cycling through
+    `rotate` buffers of that size -- what any single launch that only reads
+    those bytes from HBM takes in this setting."""
+    lib = W.load_peaks_library()
+    nb = (nbytes + 15) // 16 * 16
+    bufs = [torch.empty(nb, dtype=torch.uint8, device="cuda").fill_(3) for _ in range(rotate)]
+    out = torch.empty(lib.w4a4_peak_hbm_read_out_ints(), dtype=torch.int32, device="cuda")
+
+    def launch(i, cs):
+        if lib.w4a4_peak_hbm_read(bufs[i % rotate].data_ptr(), nb, out.data_ptr(), cs):
+            raise RuntimeError("w4a4_peak_hbm_read failed")
+
+    us = graph_avg_ms(torch, launch, n) * 1e3
+    del bufs
+    return us
 
 
 def decode_sweep(torch, np, W, workloads, Ms=(1, 4, 16), rotate=12):
     """The decode-shaped layer (K=4096, N=14336, R=32) at each M: w4a4_linear's
     average launch time over a graph of 48 launches cycling through `rotate`
     weight blobs (more bytes than the last-level cache, so weights stream
-    from HBM), algorithmic bytes / time against the HBM peak."""
+    from HBM), algorithmic bytes / time against the HBM peak, and against
+    the time a plain read of the same bytes takes in the same setting."""
     res = {}
     blobs = None
     for M in Ms:
@@ -469,8 +516,12 @@ def decode_sweep(torch, np, W, workloads, Ms=(1, 4, 16), rotate=12):
         ms = graph_avg_ms(torch, lambda i, cs: W.w4a4_linear(M, N, K, R, act, blobs[i % rotate], y, stream=cs), 48)
         c = algorithmic_counts(M, N, K, R)
         gbps = c["lin_bytes"] / (ms * 1e-3) / 1e9
+        floor = read_floor_us(torch, W, c["lin_bytes"], rotate)
         res[f"M={M}"] = {"linear_us": round(ms * 1e3, 3), "GBps": round(gbps, 1),
-                         "frac_of_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4), "algorithmic_bytes": c["lin_bytes"]}
+                         "frac_of_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4), "algorithmic_bytes": c["lin_bytes"],
+                         "plain_read_same_bytes_us": round(floor, 3),
+                         "plain_read_frac_of_hbm_peak": round(c["lin_bytes"] / (floor * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+                         "linear_over_plain_read": round(ms * 1e3 / floor, 3)}
     return {"workload": "decode: W4A4+LoRA linear M in {1,4,16} K=4096 N=14336 R=32 group 64, "
                         f"{rotate} weight blobs rotating", **res}
 
@@ -483,6 +534,9 @@ def main(argv=None):
     ap.add_argument("--workload", default="prefill")
     ap.add_argument("--m", type=int, default=None, help="row count override (decode sweep)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--settle-ms", type=float, default=1000.0,
+                    help="replay the step graph untimed for this long before the timed steps, so that the "
+                         "GPU's clocks have left their idle-to-busy ramp")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the measured peaks and the decode sweep (profiling runs)")
     ap.add_argument("--rotate", type=int, default=None,
@@ -575,50 +629,49 @@ def main(argv=None):
     torch.cuda.synchronize()
 
     # One graph holds `per_graph` whole steps (weight blobs rotate through
-    # them); the timed region replays it, so the figure is GPU throughput and
-    # not Python/launch overhead.  Graph replay is checked bit-exact against
-    # the eager result first.
+    # them), a second one the remainder of K steps; the timed region replays
+    # them, so the figure is GPU throughput and not Python/launch overhead.
+    # Graph replay is checked bit-exact against the eager result first.
     per_graph = max(1, min(args.steps, args.per_graph))
+
+    def capture(nsteps):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            cs = torch.cuda.current_stream().cuda_stream
+            for i in range(nsteps):
+                wb = blobs[i % len(blobs)]
+                quant(wb, cs)
+                W.w4a4_linear(M, N, K, R, act, wb, y, stream=cs)
+        return gr
+
     y_eager = y.clone()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        cs = torch.cuda.current_stream().cuda_stream
-        for i in range(per_graph):
-            wb = blobs[i % len(blobs)]
-            quant(wb, cs)
-            W.w4a4_linear(M, N, K, R, act, wb, y, stream=cs)
+    g = capture(per_graph)
+    reps, rest = divmod(args.steps, per_graph)
+    g_rest = capture(rest) if rest else None
     g.replay()
     torch.cuda.synchronize()
     if not torch.equal(y, y_eager):   # every blob holds the same packed weights
         raise RuntimeError("graph replay differs from the eager result")
-    reps = max(1, args.steps // per_graph)
-    steps = reps * per_graph
+    # Settle (untimed): the GPU's clocks take tens of milliseconds of
+    # sustained load to leave their idle-to-busy ramp (a step timed within
+    # ~10 ms of idle ran ~20% slower than at steady state); replaying the
+    # step graph for settle_ms first makes the K timed steps measure the
+    # sustained rate.
+    settle_steps, t_end = 0, time.perf_counter() + args.settle_ms * 1e-3
+    while time.perf_counter() < t_end:
+        g.replay()
+        settle_steps += per_graph
+        torch.cuda.synchronize()
+    steps = reps * per_graph + rest
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(reps):
         g.replay()
+    if g_rest is not None:
+        g_rest.replay()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / steps
-
-    # Per-kernel durations: HIP events on the launch stream around every
-    # kernel; a sleep kernel queued first lets the host enqueue everything
-    # before the GPU reaches it, so the events bracket kernel time only.
-    nk = min(args.steps, 200)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nk)]
-    torch.cuda.synchronize()
-    if hasattr(torch.cuda, "_sleep"):
-        torch.cuda._sleep(int(2e8))
-    for i in range(nk):
-        wb = blobs[i % len(blobs)]
-        ev[i][0].record(stream)
-        quant(wb, sh)
-        ev[i][1].record(stream)
-        W.w4a4_linear(M, N, K, R, act, wb, y, stream=sh)
-        ev[i][2].record(stream)
-    torch.cuda.synchronize()
-    q_ms_ev = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    l_ms_ev = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
 
     # Kernel-only figures: a graph of `nk_g` back-to-back launches of one
     # kernel, bracketed by two events on the launch stream; the average
@@ -652,6 +705,7 @@ def main(argv=None):
         "n_gpus": 1,
         "steps": steps,
         "warmup": args.warmup,
+        "settle": {"ms": args.settle_ms, "steps": settle_steps},
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -665,12 +719,10 @@ def main(argv=None):
         "hbm_gbps_step": round((c["lin_bytes"] + c["q_bytes"]) / (ms_per_step * 1e-3) / 1e9, 1),
         "kernels": {
             "w4a4_linear": {"avg_us": round(l_ms * 1e3, 3), "TOPS": round(lin_tops, 2),
-                             "GBps": round(c["lin_bytes"] / (l_ms * 1e-3) / 1e9, 1),
-                             "event_bracketed_us": round(l_ms_ev * 1e3, 3)},
+                             "GBps": round(c["lin_bytes"] / (l_ms * 1e-3) / 1e9, 1)},
             ("w4a4_quantize_act_rmsnorm" if args.rmsnorm else "w4a4_quantize_act"): {
                 "avg_us": round(q_ms * 1e3, 3),
-                "GBps": round(c["q_bytes"] / (q_ms * 1e-3) / 1e9, 1),
-                "event_bracketed_us": round(q_ms_ev * 1e3, 3)},
+                "GBps": round(c["q_bytes"] / (q_ms * 1e-3) / 1e9, 1)},
         },
         **({"unfused_norm_reference": unfused} if unfused else {}),
         "roofline": None,

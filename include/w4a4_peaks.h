@@ -1,8 +1,9 @@
 /*
  * w4a4_peaks.h -- C ABI of libw4a4_peaks.so: microbenchmarks that measure the
- * attainable peak of the two resources the W4A4 + LoRA linear layer is bound
- * by on MI355X (gfx950) -- dense int8 MFMA issue for large row counts, HBM
- * read bandwidth for decode-sized ones ("W4A4 CUDA Kernel for Voice Clone",
+ * attainable peak of the resources the W4A4 + LoRA linear layer is bound by
+ * on MI355X (gfx950) -- dense int8 MFMA issue for large row counts (with the
+ * fp32 VALU work of its per-group epilogue beside it), HBM read bandwidth
+ * for decode-sized ones ("W4A4 CUDA Kernel for Voice Clone",
  * section 1.2: a kernel is judged against the roofline of the resource that
  * bounds it; "INT4 Kernel Architecture, in depth", "Why INT4 kernels exist":
  * small batches stream weights, large ones are compute-bound).  They stand
@@ -37,6 +38,22 @@ int64_t w4a4_peak_i8_mfma_out_ints(void);
  * w4a4_peak_hbm_read_out_ints() entries (written). */
 int w4a4_peak_hbm_read(const void* src, uint64_t bytes, uint32_t* out, void* stream);
 int64_t w4a4_peak_hbm_read_out_ints(void);
+
+/* Two kinds of work on the same SIMDs ("W4A4 CUDA Kernel for Voice Clone",
+ * section 3.7: each group's integer sum is followed by its fp32 dequant on
+ * the vector ALUs): one workgroup of 8 waves per CU, waves 0..3 (one per
+ * SIMD) doing role_a for iters_a iterations and waves 4..7 role_b for
+ * iters_b.  Roles: 0 nothing, 1 = 8 independent v_mfma_i32_16x16x64_i8 per
+ * iteration, 2 = 32 independent wave64 v_fma_f32 per iteration.  Timing one
+ * role alone and both together gives the unpacked fp32 VALU rate and how
+ * far the two overlap.  out: int32 device buffer of
+ * w4a4_peak_roles_out_ints() entries.  w4a4_peak_roles_ops(role, iters):
+ * int8 operations (role 1) or fp32 FMA lane operations (role 2) of the
+ * four waves of one role on every CU. */
+int w4a4_peak_roles(int32_t role_a, int32_t role_b, int32_t iters_a, int32_t iters_b,
+                    int32_t* out, void* stream);
+int64_t w4a4_peak_roles_ops(int32_t role, int32_t iters);
+int64_t w4a4_peak_roles_out_ints(void);
 
 #ifdef __cplusplus
 }

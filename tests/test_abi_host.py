@@ -50,6 +50,11 @@ def test_peaks_library_exports_every_declared_symbol():
     assert lib.w4a4_peak_i8_mfma(1, None, None) == 4
     assert lib.w4a4_peak_hbm_read(ctypes.c_void_p(1 << 20), 24, ctypes.c_void_p(1 << 20), None) == 4
     assert lib.w4a4_peak_hbm_read(ctypes.c_void_p((1 << 20) + 8), 32, ctypes.c_void_p(1 << 20), None) == 4
+    assert lib.w4a4_peak_roles_out_ints() == 256 * 512
+    assert lib.w4a4_peak_roles_ops(1, 10) == 256 * 4 * 8 * 10 * 2 * 16 * 16 * 64
+    assert lib.w4a4_peak_roles_ops(2, 10) == 256 * 4 * 32 * 10 * 64
+    assert lib.w4a4_peak_roles(3, 0, 1, 1, ctypes.c_void_p(1 << 20), None) == 4
+    assert lib.w4a4_peak_roles(1, 2, 1, 1, None, None) == 4
 
 
 def test_no_unresolved_library_symbols():

@@ -56,7 +56,8 @@ def lib_path() -> str:
 # The measurement library (include/w4a4_peaks.h): microbenchmarks of the
 # attainable int8 MFMA and HBM read peaks, used by the benchmark only.
 PEAKS_SYMBOLS = ("w4a4_peak_i8_mfma", "w4a4_peak_i8_mfma_ops", "w4a4_peak_i8_mfma_out_ints",
-                 "w4a4_peak_hbm_read", "w4a4_peak_hbm_read_out_ints")
+                 "w4a4_peak_hbm_read", "w4a4_peak_hbm_read_out_ints", "w4a4_peak_roles", "w4a4_peak_roles_ops",
+                 "w4a4_peak_roles_out_ints")
 _PEAKS = None
 
 
@@ -81,6 +82,12 @@ def load_peaks_library() -> ctypes.CDLL:
     lib.w4a4_peak_hbm_read.restype = ctypes.c_int
     lib.w4a4_peak_hbm_read_out_ints.argtypes = []
     lib.w4a4_peak_hbm_read_out_ints.restype = ctypes.c_int64
+    lib.w4a4_peak_roles.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_void_p, ctypes.c_void_p]
+    lib.w4a4_peak_roles.restype = ctypes.c_int
+    lib.w4a4_peak_roles_ops.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    lib.w4a4_peak_roles_ops.restype = ctypes.c_int64
+    lib.w4a4_peak_roles_out_ints.argtypes = []
+    lib.w4a4_peak_roles_out_ints.restype = ctypes.c_int64
     _PEAKS = lib
     return lib
 

@@ -216,7 +216,17 @@ __device__ __forceinline__ v4f offset_tile(uint32_t sx_pair, uint32_t sw_pair, v
 // k-pairs), which otherwise leaves one wave per SIMD: K = 14336, N = 4096
 // measured 7.87 -> 7.19 us at M = 1 and 14.4 -> 9.6 us at M = 16, while at
 // 448 workgroups or K = 4096 eight waves were no faster or slower.
+// W4A4_DECODE_WAVES=4 / 8 and W4A4_DECODE_TILES=1 / 2 (column tiles per
+// workgroup, where the shape allows two) force the decode kernels' shape
+// (tuning and test aids, read at every launch like W4A4_TILED_*).
+static int decode_env(const char* name) {
+  const char* e = std::getenv(name);
+  return (e && e[0]) ? std::atoi(e) : 0;
+}
+
 static int decode_waves(int64_t workgroups, int64_t K) {
+  const int ov = decode_env("W4A4_DECODE_WAVES");
+  if (ov == 4 || ov == 8) return ov;
   return (workgroups <= 256 && K / kKPair >= 64) ? 8 : 4;
 }
 
@@ -1418,26 +1428,28 @@ __global__ __launch_bounds__(256, PSUM ? 1 : 2) void gemm_wide_kernel(GemmArgs g
     af[j] = g.ca[nt * 16 + (lane & 15)];
     bf[j] = g.cb[nt * 16 + (lane & 15)];
   }
+  // stores row tile by row tile: a row's 4 column tiles (128 contiguous
+  // bytes of Y) go out back to back, so the L2 writes whole lines
   if constexpr (!GLU) {
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const uint32_t nt = nt0 + wn * TN + j;
-      if (nt >= ntc) continue;
+    for (int i = 0; i < TM; ++i) {
+      const uint32_t mt = mt0 + wm * TM + i;
+      if (mt >= mtc) continue;
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const uint32_t mt = mt0 + wm * TM + i;
-        if (mt < mtc) store_tile4(g, tile4(acc[i], j), (int64_t)mt * 16, (int64_t)nt * 16, af[j], bf[j], lane);
+      for (int j = 0; j < TN; ++j) {
+        const uint32_t nt = nt0 + wn * TN + j;
+        if (nt < ntc) store_tile4(g, tile4(acc[i], j), (int64_t)mt * 16, (int64_t)nt * 16, af[j], bf[j], lane);
       }
     }
   } else {   // (gate, up) pairs: the wave's column tiles start on an even tile
 #pragma unroll
-    for (int j = 0; j < TN; j += 2) {
-      const uint32_t nt = nt0 + wn * TN + j;
-      if (nt >= ntc) continue;
+    for (int i = 0; i < TM; ++i) {
+      const uint32_t mt = mt0 + wm * TM + i;
+      if (mt >= mtc) continue;
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const uint32_t mt = mt0 + wm * TM + i;
-        if (mt < mtc)
+      for (int j = 0; j < TN; j += 2) {
+        const uint32_t nt = nt0 + wn * TN + j;
+        if (nt < ntc)
           store_tile4_glu(g, tile4(acc[i], j), tile4(acc[i], j + 1), (int64_t)mt * 16, (int64_t)(nt / 2) * 16,
                           af[j], bf[j], af[j + 1], bf[j + 1], lane);
       }
@@ -1522,7 +1534,9 @@ template <int MV>
 static hipError_t launch_decode_mv(const GemmArgs& a, hipStream_t stream) {
   const int64_t ntiles = a.N / 16;
   if (a.glu) return launch_decode_mv_n<MV, 2, true>(a, stream);
-  if (ntiles % 2 == 0 && ntiles / 2 >= 256 && a.R <= 48) return launch_decode_mv_n<MV, 2, false>(a, stream);
+  const int ov = decode_env("W4A4_DECODE_TILES");
+  const bool two = ntiles % 2 == 0 && a.R <= 48 && (ov ? ov == 2 : ntiles / 2 >= 256);
+  if (two) return launch_decode_mv_n<MV, 2, false>(a, stream);
   return launch_decode_mv_n<MV, 1, false>(a, stream);
 }
 
@@ -1588,7 +1602,8 @@ template <int MR>
 static hipError_t launch_decode_dot(const GemmArgs& a, hipStream_t stream) {
   const int64_t ntiles = a.N / 16;
   if (a.glu) return launch_decode_dot_n<MR, 2, true>(a, stream);
-  if (ntiles % 2 == 0 && ntiles / 2 >= 256) return launch_decode_dot_n<MR, 2, false>(a, stream);
+  const int ov = decode_env("W4A4_DECODE_TILES");
+  if (ntiles % 2 == 0 && (ov ? ov == 2 : ntiles / 2 >= 256)) return launch_decode_dot_n<MR, 2, false>(a, stream);
   return launch_decode_dot_n<MR, 1, false>(a, stream);
 }
 

@@ -337,6 +337,79 @@ def mlp_gate_up(args, W, torch, np, workloads):
     return 0
 
 
+def mlp_chain(args, W, torch, np, workloads):
+    """The whole gated MLP at the MLP workloads' shapes (M tokens, hidden
+    mlp_up's K, intermediate mlp_up's N = mlp_down's K, rank R on gate, up
+    and down): the activation pass of x, the gated GEMM with h quantized in
+    its epilogue straight into the down layer's activation blob
+    (w4a4_linear_glu_quant: GEMM + the kernel that sums the per-group
+    LoRA-down shares), the down GEMM -- against the same chain with h
+    through memory (w4a4_linear_glu, then the activation pass of h).  Prints
+    one line."""
+    g = workloads.generate("mlp_up", M=args.m)
+    u = workloads.generate("mlp_up", M=args.m, seed=workloads.WORKLOADS["mlp_up"].seed + 7)
+    d = workloads.generate("mlp_down", M=args.m)
+    M, K, H, R, Nd, Rd = g["M"], g["K"], g["N"], g["R"], d["N"], d["R"]
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    up = W.GatedMLPUp(H, K, dev(g["w"]), dev(u["w"]), dev(g["lora_down"]), dev(g["lora_up"]),
+                      dev(u["lora_down"]), dev(u["lora_up"]), dev(g["col_scale"]), dev(g["bias"]),
+                      dev(u["col_scale"]), dev(u["bias"]))
+    down = W.PackedLinear(Nd, H, Rd, w_fp16=dev(d["w"]), lora_down=dev(d["lora_down"]),
+                          lora_up=dev(d["lora_up"]), col_scale=dev(d["col_scale"]), bias=dev(d["bias"]))
+    mlp = W.GatedMLP(up, down)
+    x = dev(g["x"])
+    act, act_h, ws, y = mlp.buffers(M)
+    h = torch.empty((M, H), dtype=torch.float16, device="cuda")
+    act_h2 = W.alloc_act_blob(M, H, Rd)
+    y2 = torch.empty_like(y)
+
+    def quant_x(i, cs):
+        W.w4a4_quantize_act(M, K, up.R, x, up.wblob, act, stream=cs)
+
+    def glu_quant(i, cs):
+        W.w4a4_linear_glu_quant(M, 2 * H, K, up.R, up.r_gate, act, up.wblob, Rd, down.wblob, act_h, ws, stream=cs)
+
+    def down_gemm(i, cs):
+        W.w4a4_linear(M, Nd, H, Rd, act_h, down.wblob, y, stream=cs)
+
+    def fused(i, cs):
+        mlp.forward(x, (act, act_h, ws, y), stream=cs)
+
+    def glu_gemm(i, cs):
+        W.w4a4_linear_glu(M, 2 * H, K, up.R, up.r_gate, act, up.wblob, h, stream=cs)
+
+    def quant_h(i, cs):
+        W.w4a4_quantize_act(M, H, Rd, h, down.wblob, act_h2, stream=cs)
+
+    def unfused(i, cs):
+        quant_x(i, cs)
+        glu_gemm(i, cs)
+        quant_h(i, cs)
+        W.w4a4_linear(M, Nd, H, Rd, act_h2, down.wblob, y2, stream=cs)
+
+    fused(0, torch.cuda.current_stream().cuda_stream)
+    unfused(0, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    n = 50
+    t = {k: graph_avg_ms(torch, f, n) * 1e3 for k, f in
+         [("fused_step", fused), ("activation_pass_x", quant_x), ("glu_quant", glu_quant),
+          ("down_gemm", down_gemm), ("unfused_step", unfused), ("glu_gemm_h_to_memory", glu_gemm),
+          ("activation_pass_h", quant_h)]}
+    ops = 2 * algorithmic_counts(M, H, K, R)["layer_ops"] + algorithmic_counts(M, Nd, H, Rd)["layer_ops"]
+    yd = (y.float() - y2.float()).abs()
+    print(json.dumps({"metric": "gated MLP (gate + up + SiLU*mul + down), TOPS at 1 GPU", "unit": "TOPS",
+                      "value": round(ops / (t["fused_step"] * 1e-6) / 1e12, 3),
+                      "config": {"workload": f"gated MLP: M={M} hidden={K} intermediate={H} out={Nd}, "
+                                             f"R={R} on gate, up and down, group 64",
+                                 "M": M, "K": K, "H": H, "N_down": Nd, "R": R, "R_down": Rd},
+                      **{k + "_us": round(v, 3) for k, v in t.items()},
+                      "fused_over_unfused": round(t["unfused_step"] / t["fused_step"], 3),
+                      "h_bytes_kept_from_memory": 2 * 2 * M * H,
+                      "max_abs_diff_y_vs_unfused_over_rms": round(float(yd.max() / y2.float().pow(2).mean().sqrt()),
+                                                                   6)}), flush=True)
+    return 0
+
+
 def algorithmic_counts(M, N, K, R):
     """Ops and bytes the method must do / move (not those of an fp16 GEMM).
 
@@ -557,6 +630,9 @@ def main(argv=None):
     ap.add_argument("--mlp", action="store_true",
                     help="time the gated MLP front half (gate + up fused with SiLU*mul in the epilogue) "
                          "at --workload's shape against the unfused path, and print that line")
+    ap.add_argument("--mlp-chain", action="store_true",
+                    help="time the whole gated MLP at the MLP workloads' shapes with h quantized in the gated "
+                         "GEMM's epilogue against the chain with h through memory, and print that line")
     ap.add_argument("--ingest-sq", metavar="DIR",
                     help="record a rocprofv3 SQ instruction-mix counter run (DIR) for --workload")
     args = ap.parse_args(argv)
@@ -587,6 +663,8 @@ def main(argv=None):
         return 0
     if args.mlp:
         return mlp_gate_up(args, W, torch, np, workloads)
+    if args.mlp_chain:
+        return mlp_chain(args, W, torch, np, workloads)
     if args.rotate is None:
         args.rotate = 12 if args.workload == "decode" else 1
     case = workloads.generate(args.workload, M=args.m)

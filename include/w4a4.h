@@ -177,6 +177,42 @@ int w4a4_linear(int64_t M, int64_t N, int64_t K, int32_t R, const void* act,
 int w4a4_linear_glu(int64_t M, int64_t N, int64_t K, int32_t R, int32_t r_gate, const void* act,
                     const void* wblob, uint16_t* y, int64_t ldy, void* stream);
 
+/* The gated layer whose output goes straight into the next layer's
+ * activation blob ("W4A4 CUDA Kernel for Voice Clone", section 3.1: the MLP
+ * computes SiLU(gate) * up and feeds it to the W4A4 down projection; section
+ * 3.6: that projection's activation pass).  h = fp16(SiLU(g) * u) is
+ * exactly what w4a4_linear_glu(M, N, K, R, r_gate, act, wblob, ...) would
+ * store, and act_out becomes what w4a4_quantize_act(M, N/2, R_down, h, N/2,
+ * down_wblob, act_out) would write from it: codes and scales bit for bit,
+ * lora_act equal up to the order of its fp32 sums.  Where the grid is large
+ * enough (M > 16 and ceil(M/64) * N/128 >= 128) h never goes to memory in
+ * fp16: the GEMM's epilogue quantizes each 64-column group of h and computes
+ * that group's share of LoRA-down (into workspace), and a second kernel sums
+ * the shares in group order into lora_act (deterministic).  Otherwise
+ * (decode sizes, small grids) the call runs w4a4_linear_glu into workspace,
+ * then the activation pass.
+ * N: packed gate/up columns as for w4a4_linear_glu, with N/2 % 128 == 0 (N/2
+ * is the next layer's K).  R_down: the next layer's LoRA rank (0..64, % 16);
+ * down_wblob: its weight blob (w4a4_weight_layout(N_down, N/2, R_down));
+ * only its L_down section is read, NULL allowed when R_down == 0.
+ * act_out: activation blob of w4a4_act_layout(M, N/2, R_down), 256-byte
+ * aligned.  workspace: device buffer of w4a4_glu_quant_workspace bytes,
+ * 256-byte aligned (NULL allowed when that is 0); its contents are scratch.
+ * act_out and workspace must not overlap each other or any input
+ * (W4A4_ERR_ARG).  Other arguments and errors as w4a4_linear_glu
+ * (W4A4_ERR_SHAPE also when N/2 % 128 != 0 or R_down is invalid). */
+int w4a4_linear_glu_quant(int64_t M, int64_t N, int64_t K, int32_t R, int32_t r_gate,
+                          const void* act, const void* wblob, int32_t R_down,
+                          const void* down_wblob, void* act_out, void* workspace,
+                          void* stream);
+
+/* Bytes of workspace w4a4_linear_glu_quant needs for (M, N, R_down)
+ * (host-only): the larger of 4 * (N/128) * Mp * R_down (the LoRA-down
+ * shares) and 2 * M * N/2 (h), rounded up to 256; 0 for M = 0.
+ * W4A4_ERR_SHAPE for N not a positive multiple of 256, an invalid R_down or
+ * M out of range. */
+int w4a4_glu_quant_workspace(int64_t M, int64_t N, int32_t R_down, size_t* bytes);
+
 /* Which GEMM kernel w4a4_linear runs for a shape (host-only):
  * 1 = decode (M <= 16), 2 = prefill (tiled); -W4A4_ERR_SHAPE if the
  * shape is unsupported.  Lets a caller log the kernel chosen per layer

@@ -204,6 +204,50 @@ def test_validation_errors_before_any_launch():
                                       None) == 4
 
 
+def test_glu_quant_workspace_and_validation():
+    """The quantized gated output: workspace sizes, and every argument error
+    returned on the host (nothing launched)."""
+    lib = _lib()
+    ws = W.w4a4_glu_quant_workspace
+    # the larger of the per-group LoRA-down partials, 4 * (N/128) * Mp * R_down
+    # bytes, and h, 2 * M * N/2 bytes (rounded up to 256)
+    assert ws(700, 6144, 32) == 4 * 48 * 704 * 32
+    assert ws(17, 256, 16) == 2 * 17 * 128   # h (4352 B, a multiple of 256) over 4096 B of shares
+    assert ws(700, 6144, 0) == 2 * 700 * 3072
+    assert ws(1, 6144, 32) == 4 * 48 * 16 * 32
+    assert ws(5, 256, 0) == 2 * 5 * 128
+    assert ws(0, 6144, 32) == 0
+    n = ctypes.c_size_t()
+    assert lib.w4a4_glu_quant_workspace(4, 6144, 32, None) == 1
+    assert lib.w4a4_glu_quant_workspace(4, 6016, 32, ctypes.byref(n)) == 2   # N/2 not a multiple of 128
+    assert lib.w4a4_glu_quant_workspace(4, 6144, 24, ctypes.byref(n)) == 2
+    assert lib.w4a4_glu_quant_workspace(-1, 6144, 32, ctypes.byref(n)) == 2
+    big = 1 << 30   # far from FAKE: no overlap between the fake buffers
+    q = lib.w4a4_linear_glu_quant
+    args = lambda **kw: [kw.get(k, v) for k, v in (
+        ("M", 40), ("N", 256), ("K", 128), ("R", 32), ("rg", 16), ("act", FAKE), ("wb", 2 * big),
+        ("Rd", 16), ("dwb", 3 * big), ("out", 4 * big), ("ws", 5 * big), ("s", None))]
+    assert q(*args(N=192)) == 2            # N/2 not a multiple of 128
+    assert q(*args(N=240)) == 2            # not whole (gate, up) pairs
+    assert q(*args(rg=48)) == 2            # gate rank above R
+    assert q(*args(Rd=8)) == 2             # down rank not a multiple of 16
+    assert q(*args(Rd=80)) == 2
+    assert q(*args(K=100)) == 2
+    assert q(*args(M=-1)) == 2
+    assert q(*args(M=0, act=None, wb=None, dwb=None, out=None, ws=None)) == 0
+    assert q(*args(out=None)) == 1
+    assert q(*args(dwb=None)) == 1         # needed for R_down > 0
+    assert q(*args(ws=None)) == 1
+    assert q(*args(act=None)) == 1
+    assert q(*args(out=4 * big + 16)) == 3
+    assert q(*args(ws=5 * big + 128)) == 3
+    assert q(*args(dwb=3 * big + 8)) == 3
+    # overlaps: the output blob with the input blob, the workspace with the output
+    assert q(*args(out=FAKE + 256)) == 4
+    assert q(*args(ws=4 * big + 256)) == 4
+    assert q(*args(ws=3 * big)) == 4       # the workspace over the down layer's L_down
+
+
 def test_query_variant_is_host_only():
     for M in (1, 4, 16, 700, 8192):
         assert W.w4a4_query_variant(M, 4096, 4096, 32) == (1 if M <= 16 else 2)

@@ -176,3 +176,27 @@ def test_psums_gated_layer_dispatch(M):
     qx, _ = O.quantize_groups(g["x"])
     qw, _ = O.quantize_groups(w)
     _check_window(out.cpu().numpy(), qx, qw, 0, 0, M, f"gated M={M}")
+
+
+@pytest.mark.parametrize("M", [1, 4, 16])
+@pytest.mark.parametrize("waves", [4, 8])
+@pytest.mark.parametrize("tiles", [1, 2])
+def test_psums_every_decode_shape_forced(M, waves, tiles, monkeypatch):
+    """Each decode workgroup shape forced (W4A4_DECODE_WAVES: K split 4 or 8
+    ways; W4A4_DECODE_TILES: one or two column tiles per workgroup) on a
+    shape where all of them apply (K = 1664: 13 k-pairs, so with 8 waves the
+    last wave has none; N = 8192): all of P bit-exact and Y within the
+    layer bar, for the dot kernel (M = 1) and the MFMA decode kernel (M = 4,
+    16)."""
+    K, N, R = 1664, 8192, 32
+    monkeypatch.setenv("W4A4_DECODE_WAVES", str(waves))
+    monkeypatch.setenv("W4A4_DECODE_TILES", str(tiles))
+    case = workloads.random_case(M, K, N, R, seed=6500 + M + 10 * waves + tiles)
+    _say(f"[psums decode forced] M={M} waves={waves} tiles={tiles}")
+    run = GpuRun(case)
+    qx, _ = O.quantize_groups(case["x"])
+    qw, _ = O.quantize_groups(case["w"])
+    _check_window(_full_psums(run), qx, qw, 0, 0, M, f"decode forced M={M} waves={waves} tiles={tiles}")
+    ref = O.linear(case["x"], case["lora_down"], case["lora_up"], case["col_scale"], case["bias"], w16=case["w"])
+    _check_y(run.host_y()[:M, :N], ref["y"], f"decode forced M={M} waves={waves} tiles={tiles}",
+             y64=ref["y64"], ref=ref, case=case)

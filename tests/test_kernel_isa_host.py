@@ -20,11 +20,11 @@ import pytest
 from w4a4_gemm_lora_amd import build as B
 
 NAME = re.compile(r"^(_ZN4w4a417gemm_tiled_kernelI\S*):")
-ARGS = re.compile(r"ILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELb(\d)ELi(\d+)ELi(\d+)ELb(\d)E")
+ARGS = re.compile(r"ILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELb(\d)ELi(\d+)ELi(\d+)ELb(\d)ELb(\d)E")
 
 
-def _epilogue_loads(wm, wn, tm, tn, rt, spl):
-    late = tm * rt * spl > 16 or tm * rt >= 16
+def _epilogue_loads(wm, wn, tm, tn, rt, spl, qout=0):
+    late = tm * rt * spl > 16 or tm * rt >= 16 or (qout and tm * rt * spl >= 16)
     return 2 * tn + tn * rt + (tm * rt if (not late and rt > 0) else 0)
 
 
@@ -54,7 +54,7 @@ def test_epilogue_loads_follow_the_first_copies(asm):
         m = NAME.match(line)
         if not m:
             continue
-        wm, wn, tm, tn, rt, ns, spl, glu, occ, ks, psum = map(int, ARGS.search(m.group(1)).groups())
+        wm, wn, tm, tn, rt, ns, spl, glu, occ, ks, psum, qout = map(int, ARGS.search(m.group(1)).groups())
         if occ >= 3:
             continue   # the lean variant loads its epilogue operands after the loop
         if psum:
@@ -69,7 +69,7 @@ def test_epilogue_loads_follow_the_first_copies(asm):
         seg = body[barriers[0]:barriers[1]]   # k-pair 0: after its barrier, up to k-pair 1's
         last_copy = max(k for k, t in enumerate(seg) if "global_load_lds" in t)
         loads = [t for t in seg[last_copy:] if t.startswith("global_load_dword") and "lds" not in t]
-        want = _epilogue_loads(wm, wn, tm, tn, rt, spl)
+        want = _epilogue_loads(wm, wn, tm, tn, rt, spl, qout)
         assert len(loads) >= want, (m.group(1), len(loads), want)
         nw = wm * wn
         ops = (wm * tm + wn * tn + nw - 1) // nw + 1
@@ -87,7 +87,7 @@ def test_epilogue_loads_follow_the_first_copies(asm):
 # per SIMD lane shared by the waves on it, 160 KiB of LDS per CU.
 KDESC = re.compile(r"^\s*\.amdhsa_kernel (\S+)$")
 TILED = re.compile(r"gemm_tiled_kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELb(\d)"
-                   r"ELi(\d+)ELi(\d+)ELb(\d)E")
+                   r"ELi(\d+)ELi(\d+)ELb(\d)ELb(\d)E")
 WIDE = re.compile(r"gemm_wide_kernelILi(\d+)ELi(\d+)ELb(\d)ELb(\d)E")
 DECODE = re.compile(r"gemm_decode_(?:dot_)?kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELb(\d)ELi(\d+)ELb(\d)E")
 LDS_PER_CU = 160 * 1024
@@ -123,22 +123,25 @@ def test_every_instance_fits_its_occupancy(asm):
     or 2 waves of it on each SIMD) must keep OCC waves on every SIMD by
     registers and OCC / (WM WN KS / 4) workgroups per CU by LDS; a decode
     instance (DW waves, bound 16 / DW) keeps 4 waves per SIMD.  The
+    instances with the quantized gated output are held to their tile
+    shape's occupancy like the others.  The
     diagnostic (group-sum) instances are built for one workgroup per CU and
     checked against that.  The wide kernel (4 waves) is built for two
     workgroups per CU."""
-    seen = {"tiled": 0, "wide": 0, "decode": 0, "other": 0}
+    seen = {"tiled": 0, "tiled_qout": 0, "wide": 0, "decode": 0, "other": 0}
     for src, text in asm.items():
         for name, d in _descriptors(text).items():
             assert d["private_segment_fixed_size"] == 0, f"{name}: {d['private_segment_fixed_size']} B of scratch"
             lds = d["group_segment_fixed_size"]
             m = TILED.search(name)
             if m:
-                wm, wn, tm, tn, rt, ns, spl, glu, occ, ks, psum = map(int, m.groups())
+                wm, wn, tm, tn, rt, ns, spl, glu, occ, ks, psum, qout = map(int, m.groups())
                 per_wg = max(1, wm * wn * ks // 4)   # waves of one workgroup on each SIMD
                 want = max(per_wg, 1 if psum else occ)
                 assert _waves_per_simd(d) >= want, (name, d["next_free_vgpr"], want)
                 assert (want // per_wg) * lds <= LDS_PER_CU, (name, lds, want)
                 seen["tiled"] += 1
+                seen["tiled_qout"] += qout
                 continue
             m = WIDE.search(name)
             if m:   # 4 waves, built for 2 workgroups per CU (1 for the diagnostic instance)
@@ -158,3 +161,5 @@ def test_every_instance_fits_its_occupancy(asm):
             assert lds <= LDS_PER_CU, (name, lds)
             seen["other"] += 1
     assert seen["tiled"] >= 100 and seen["wide"] >= 10 and seen["decode"] >= 40 and seen["other"] >= 5, seen
+    # the quantized gated output: 128 x 128 and 64 x 128, both occupancies, every rank, 1 or 4 partials
+    assert seen["tiled_qout"] == 2 * 2 * 5 * 2, seen

@@ -28,7 +28,8 @@ __all__ = [
     "W4A4Error", "lib_path", "load_library", "w4a4_status_string",
     "w4a4_weight_layout", "w4a4_act_layout", "w4a4_pack_weights",
     "w4a4_quantize_act", "w4a4_quantize_act_rmsnorm", "w4a4_linear", "w4a4_linear_glu",
-    "w4a4_query_variant", "GatedMLPUp",
+    "w4a4_linear_glu_quant", "w4a4_glu_quant_workspace",
+    "w4a4_query_variant", "GatedMLPUp", "GatedMLP",
     "w4a4_debug_group_psums", "w4a4_debug_group_psums_glu", "alloc_weight_blob", "alloc_act_blob",
     "PackedLinear", "LayerGraphs", "EXPORTED_SYMBOLS", "PEAKS_SYMBOLS", "load_peaks_library",
 ]
@@ -37,7 +38,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 EXPORTED_SYMBOLS = (
     "w4a4_status_string", "w4a4_weight_layout", "w4a4_act_layout",
     "w4a4_pack_weights", "w4a4_quantize_act", "w4a4_quantize_act_rmsnorm", "w4a4_linear",
-    "w4a4_linear_glu", "w4a4_query_variant", "w4a4_debug_group_psums",
+    "w4a4_linear_glu", "w4a4_linear_glu_quant", "w4a4_glu_quant_workspace", "w4a4_query_variant",
+    "w4a4_debug_group_psums",
     "w4a4_debug_group_psums_glu", "w4a4_graph_begin", "w4a4_graph_end", "w4a4_layer_graph_create", "w4a4_graph_launch",
     "w4a4_graph_destroy",
 )
@@ -124,6 +126,8 @@ def load_library() -> ctypes.CDLL:
                                               _vp, _vp, _vp]
     lib.w4a4_linear.argtypes = [_i64, _i64, _i64, _i32, _vp, _vp, _vp, _i64, _vp]
     lib.w4a4_linear_glu.argtypes = [_i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _i64, _vp]
+    lib.w4a4_linear_glu_quant.argtypes = [_i64, _i64, _i64, _i32, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp]
+    lib.w4a4_glu_quant_workspace.argtypes = [_i64, _i64, _i32, ctypes.POINTER(_sz)]
     lib.w4a4_query_variant.argtypes = [_i64, _i64, _i64, _i32]
     lib.w4a4_layer_graph_create.argtypes = [_i64, _i64, _i64, _i32, _vp, _i64, _vp, ctypes.c_double,
                                             _vp, _vp, _vp, _i64, ctypes.POINTER(_vp)]
@@ -231,6 +235,21 @@ def w4a4_linear_glu(M, N, K, R, r_gate, act, wblob, y, ldy=None, stream=None):
     st = load_library().w4a4_linear_glu(M, N, K, R, r_gate, _ptr(act), _ptr(wblob), _ptr(y), ldy,
                                         _stream(stream))
     _check(st, "w4a4_linear_glu")
+
+
+def w4a4_glu_quant_workspace(M, N, R_down):
+    """Bytes of workspace w4a4_linear_glu_quant needs (host-only)."""
+    n = _sz()
+    _check(load_library().w4a4_glu_quant_workspace(M, N, R_down, ctypes.byref(n)), "w4a4_glu_quant_workspace")
+    return n.value
+
+
+def w4a4_linear_glu_quant(M, N, K, R, r_gate, act, wblob, R_down, down_wblob, act_out, workspace,
+                          stream=None):
+    st = load_library().w4a4_linear_glu_quant(M, N, K, R, r_gate, _ptr(act), _ptr(wblob), R_down,
+                                              _ptr(down_wblob), _ptr(act_out), _ptr(workspace),
+                                              _stream(stream))
+    _check(st, "w4a4_linear_glu_quant")
 
 
 def w4a4_debug_group_psums(M, N, K, R, act, wblob, m0, mc, n0, nc, out, stream=None):
@@ -344,6 +363,39 @@ class GatedMLPUp:
         w4a4_quantize_act(M, self.K, self.R, x, self.wblob, act, stream=stream)
         w4a4_linear_glu(M, 2 * self.N, self.K, self.R, self.r_gate, act, self.wblob, h, stream=stream)
         return h
+
+
+class GatedMLP:
+    """A whole gated MLP: gate and up projections packed as one layer
+    (GatedMLPUp) and the down projection (PackedLinear with K = the up
+    layer's N).  forward(x) runs the activation pass of x, then the gated
+    GEMM with its output quantized straight into the down layer's
+    activation blob (w4a4_linear_glu_quant: h never goes to memory in fp16
+    for M > 16), then the down GEMM; returns y [M, down.N]."""
+
+    def __init__(self, up: "GatedMLPUp", down: PackedLinear):
+        if down.K != up.N or up.N % 128:
+            raise ValueError("the down projection's K must be the up layer's N, a multiple of 128")
+        self.up, self.down = up, down
+
+    def buffers(self, M, device="cuda"):
+        """(act, act_h, workspace, y) for M rows."""
+        import torch
+        ws = w4a4_glu_quant_workspace(M, 2 * self.up.N, self.down.R)
+        return (alloc_act_blob(M, self.up.K, self.up.R, device=device),
+                alloc_act_blob(M, self.up.N, self.down.R, device=device),
+                torch.empty(max(ws, 256), dtype=torch.uint8, device=device),
+                torch.empty((M, self.down.N), dtype=torch.float16, device=device))
+
+    def forward(self, x, bufs=None, stream=None):
+        M = x.shape[0]
+        act, act_h, ws, y = self.buffers(M, device=x.device) if bufs is None else bufs
+        u, d = self.up, self.down
+        w4a4_quantize_act(M, u.K, u.R, x, u.wblob, act, stream=stream)
+        w4a4_linear_glu_quant(M, 2 * u.N, u.K, u.R, u.r_gate, act, u.wblob, d.R, d.wblob if d.R else None,
+                              act_h, ws, stream=stream)
+        w4a4_linear(M, d.N, d.K, d.R, act_h, d.wblob, y, stream=stream)
+        return y
 
 
 class LayerGraphs:

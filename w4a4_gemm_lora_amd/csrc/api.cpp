@@ -250,6 +250,108 @@ int w4a4_linear_glu(int64_t M, int64_t N, int64_t K, int32_t R, int32_t r_gate, 
   return linear_impl(M, N, K, R, act, wblob, y, ldy, stream, true, r_gate);
 }
 
+// Workspace of w4a4_linear_glu_quant: room for either route -- the
+// per-group LoRA-down partials [H/64][Mp][R_down] fp32 of the quantizing
+// epilogue, or h itself [M][H] fp16 on the way through the activation pass.
+static size_t glu_quant_workspace(int64_t M, int64_t N, int32_t R_down) {
+  const int64_t H = N / 2;
+  if (M <= 0) return 0;
+  const size_t parts = (size_t)(H / kGroup) * round_up16(M) * R_down * 4, h = (size_t)M * H * 2;
+  return align256(parts > h ? parts : h);
+}
+
+// The quantizing epilogue needs workgroups that each hold a 64-column group
+// of h: ceil(M/64) x H/64 of them at 64 rows.  Below 128 such workgroups (M
+// <= 128 at H = 3072) the chip is too empty for it to pay: h goes through
+// the workspace and the activation pass instead (measured at H = 3072, K =
+// 1024: M = 64, 13.5 against 10.8 us; M = 256, 14.4 against 15.2 us).  M <=
+// 16 always takes that route (the decode kernels' workgroups hold 16 or 32
+// columns of h).  W4A4_GLU_QUANT_EPILOGUE=0 / 1 forces the route for M > 16
+// (tuning and test aid, read at every call like the W4A4_TILED_* overrides).
+static bool glu_quant_in_epilogue(int64_t M, int64_t H) {
+  if (M <= 16) return false;
+  const char* e = std::getenv("W4A4_GLU_QUANT_EPILOGUE");
+  if (e && (e[0] == '0' || e[0] == '1')) return e[0] == '1';
+  return ((M + 63) / 64) * (H / kGroup) >= 128;
+}
+
+static bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uint8_t* pa = static_cast<const uint8_t*>(a);
+  const uint8_t* pb = static_cast<const uint8_t*>(b);
+  return na > 0 && nb > 0 && pa < pb + nb && pb < pa + na;
+}
+
+static int check_glu_quant(int64_t M, int64_t N, int64_t K, int32_t R, int32_t r_gate, int32_t R_down) {
+  int st = check_nkr(N, K, R);
+  if (st) return st;
+  if (N % 32 != 0 || r_gate < 0 || r_gate > R) return W4A4_ERR_SHAPE;
+  if ((N / 2) % kKPair != 0) return W4A4_ERR_SHAPE;   // h is the next layer's K
+  if ((st = check_nkr(16, N / 2, R_down))) return st;
+  return check_m(M);
+}
+
+int w4a4_glu_quant_workspace(int64_t M, int64_t N, int32_t R_down, size_t* bytes) {
+  if (!bytes) return W4A4_ERR_NULL;
+  *bytes = 0;
+  if (N < 256 || N % 256 != 0 || R_down < 0 || R_down > kMaxRank || R_down % 16 != 0) return W4A4_ERR_SHAPE;
+  int st = check_m(M);
+  if (st) return st;
+  *bytes = glu_quant_workspace(M, N, R_down);
+  return W4A4_OK;
+}
+
+int w4a4_linear_glu_quant(int64_t M, int64_t N, int64_t K, int32_t R, int32_t r_gate, const void* act,
+                          const void* wblob, int32_t R_down, const void* down_wblob, void* act_out,
+                          void* workspace, void* stream) {
+  int st = check_glu_quant(M, N, K, R, r_gate, R_down);
+  if (st) return st;
+  if (M == 0) return W4A4_OK;
+  const int64_t H = N / 2;
+  const size_t ws = glu_quant_workspace(M, N, R_down);
+  if (!act || !wblob || !act_out || (R_down > 0 && !down_wblob) || (ws > 0 && !workspace)) return W4A4_ERR_NULL;
+  if (!aligned(act, 256) || !aligned(wblob, 256) || !aligned(act_out, 256) ||
+      (down_wblob && !aligned(down_wblob, 256)) || (workspace && !aligned(workspace, 256)))
+    return W4A4_ERR_ALIGN;
+  const ActGeom og = act_geom(M, H, R_down);
+  const size_t at = act_geom(M, K, R).total, wt = weight_geom(N, K, R).total;
+  // the down layer's blob is read only for L_down, its first section
+  const size_t dt = R_down > 0 ? (size_t)H * R_down * 2 : 0;
+  if (overlaps(act_out, og.total, act, at) || overlaps(act_out, og.total, wblob, wt) ||
+      overlaps(act_out, og.total, down_wblob, dt) || overlaps(act_out, og.total, workspace, ws) ||
+      overlaps(workspace, ws, act, at) || overlaps(workspace, ws, wblob, wt) || overlaps(workspace, ws, down_wblob, dt))
+    return W4A4_ERR_ARG;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const bool in_epilogue = glu_quant_in_epilogue(M, H);
+  if (log_enabled())
+    std::fprintf(stderr, "w4a4_linear_glu_quant M=%lld N=%lld K=%lld R=%d R_down=%d -> %s\n", (long long)M,
+                 (long long)N, (long long)K, R, R_down,
+                 in_epilogue ? "prefill, quantized in the epilogue" : "gated GEMM + activation pass");
+  if (!in_epilogue) {
+    uint16_t* h = static_cast<uint16_t*>(workspace);
+    if ((st = linear_impl(M, N, K, R, act, wblob, h, H, stream, true, r_gate))) return st;
+    return quantize_act_impl(M, H, R_down, h, H, nullptr, 0.0, down_wblob, act_out, stream);
+  }
+  GemmArgs a;
+  if ((st = make_gemm_args(M, N, K, R, act, wblob, nullptr, N, &a))) return st;
+  a.glu = 1;
+  a.glu_tlo = r_gate / 16;
+  a.glu_thi = (r_gate + 15) / 16;
+  uint8_t* ob = static_cast<uint8_t*>(act_out);
+  a.qo_xq = ob + og.off_xq;
+  a.qo_sx = reinterpret_cast<uint16_t*>(ob + og.off_sx);
+  a.qo_part = static_cast<float*>(workspace);
+  a.qo_ldown = R_down > 0 ? reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(down_wblob) +
+                                                              weight_geom(16, H, R_down).off_ldown)
+                          : nullptr;
+  a.qo_R = R_down;
+  a.qo_kp = H / kKPair;
+  hipError_t e = launch_gemm_glu_quant(a, s);
+  if (e == hipSuccess && R_down > 0)
+    e = launch_lora_group_sum(static_cast<const float*>(workspace), og.Mp, R_down, H, og.ks,
+                              reinterpret_cast<float*>(ob + og.off_la), s);
+  return hip_status(e);
+}
+
 int w4a4_query_variant(int64_t M, int64_t N, int64_t K, int32_t R) {
   if (check_nkr(N, K, R) || check_m(M)) return -W4A4_ERR_SHAPE;
   return choose_variant(M, N, K, R);

@@ -34,6 +34,7 @@
 #include <cstdlib>
 
 #include "device_common.hpp"
+#include "quant_common.hpp"
 #include "w4a4_internal.hpp"
 
 namespace w4a4 {
@@ -811,11 +812,19 @@ __device__ __forceinline__ void map_workgroup(uint32_t nbm, uint32_t nbn, uint32
 // (bits - kOffsetBits) / 256 (GemmArgs::psum); no LoRA and no store of Y.
 // (A diagnostic launch keeps no occupancy: its instances are built for one
 // workgroup per CU, so the stores of its epilogue never spill.)
+//
+// QOUT: the gated layer's output quantized for the next layer (GemmArgs::
+// qo_xq): the workgroup's 8 packed column tiles are one 64-column group of h,
+// so the activation pass's per-group work -- absmax, scale, codes, and the
+// group's share of LoRA-down -- runs in the epilogue and h never goes to
+// memory in fp16 ("W4A4 CUDA Kernel for Voice Clone", section 3.1: SiLU(gate)
+// * up feeds the W4A4 down projection; section 3.6: its quantizer).
 template <int WM, int WN, int TM, int TN, int RT, int NS, int SPL, bool GLU, int OCC, int KS,
-          bool PSUM = false>
+          bool PSUM = false, bool QOUT = false>
 __global__ __launch_bounds__(WM * WN * KS * 64, PSUM ? 1 : OCC) void gemm_tiled_kernel(GemmArgs g, int64_t mt_count,
                                                                         int64_t nt_count) {
   static_assert(!PSUM || (RT == 0 && SPL == 1 && !GLU), "the diagnostic instance has no epilogue");
+  static_assert(!QOUT || (GLU && WN * TN == 8 && KS == 1 && !PSUM), "one 64-column group of h per workgroup");
   // KS = 2 splits K between two sets of WM x WN waves over the same output
   // tiles (each with its own stage ring, in lockstep), and the second set's
   // accumulators are added to the first's in LDS after the loop: twice the
@@ -939,7 +948,9 @@ __global__ __launch_bounds__(WM * WN * KS * 64, PSUM ? 1 : OCC) void gemm_tiled_
   // unless they would take more than 64 registers through the loop, or 64
   // beside 4 x 4 accumulator tiles: then the epilogue loads them rank block
   // by rank block (one more memory round trip per workgroup).
-  constexpr bool kLateLora = kLean || TM * RT * SPL > 16 || TM * RT >= 16;
+  // (The quantizing gated epilogue needs more registers after the loop: its
+  // instances load 64 registers' worth late as well.)
+  constexpr bool kLateLora = kLean || TM * RT * SPL > 16 || TM * RT >= 16 || (QOUT && TM * RT * SPL >= 16);
   v4f la_p[kLateLora ? 1 : SPL][TM][RTL];
   auto load_lora_partials = [&]() {
     if constexpr (!kLateLora && RT > 0) {
@@ -1197,7 +1208,7 @@ __global__ __launch_bounds__(WM * WN * KS * 64, PSUM ? 1 : OCC) void gemm_tiled_
         if (mt < mt_count) store_tile4(g, lora_tile(i, j), mt * 16, nt * 16, af[j], bf[j], lane);
       }
     }
-  } else {
+  } else if constexpr (!QOUT) {
     // (gate, up) tile pairs: a wave's column tiles start on an even tile, so
     // pairs never straddle waves
     static_assert(TN % 2 == 0, "a gated output needs whole tile pairs per wave");
@@ -1211,6 +1222,80 @@ __global__ __launch_bounds__(WM * WN * KS * 64, PSUM ? 1 : OCC) void gemm_tiled_
         if (mt < mt_count)
           store_tile4_glu(g, lora_tile(i, j), lora_tile(i, j + 1), mt * 16, (nt / 2) * 16, af[j], bf[j],
                           af[j + 1], bf[j + 1], lane);
+      }
+    }
+  } else {
+    // h of the workgroup's rows x its 64 columns (group gq = bn of h, all
+    // inside N since N/2 % 128 == 0) is staged in LDS as fp16 bits -- the
+    // values w4a4_linear_glu would store; rows >= M as 0, as the activation
+    // pass zeroes them.  Then each wave takes whole 16-row tiles in the
+    // activation pass's lane layout (lane r + 16c: row r, columns 16c ..
+    // 16c + 15): group absmax and scale, codes, and those registers times the
+    // group's L_down fragments on the f16 MFMA.
+    constexpr int HST = 72;   // fp16 per staged row: 64 + 8 (rows stay 16-byte aligned, banks spread)
+    static_assert(BMT * 16 * HST * 2 <= sizeof(lds), "the h tile fits the stage ring");
+    uint16_t* hs = reinterpret_cast<uint16_t*>(&lds[0][0][0][0]);
+    __syncthreads();   // every wave is done with the stage ring
+#pragma unroll
+    for (int j = 0; j < TN; j += 2) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const v4f ga = lora_tile(i, j), ua = lora_tile(i, j + 1);
+        const int lr = (wm * TM + i) * 16 + c * 4;                      // row in the workgroup tile
+        const int64_t row = (int64_t)(mt0 + wm * TM + i) * 16 + c * 4;  // row of h
+        const int col = ((wn * TN + j) / 2) * 16 + (lane & 15);          // column in the group
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const uint32_t hb = glu_bits(af[j], ga[ii], bf[j], af[j + 1], ua[ii], bf[j + 1]);
+          hs[(lr + ii) * HST + col] = row + ii < g.M ? (uint16_t)hb : (uint16_t)0;
+        }
+      }
+    }
+    const int64_t gq = bn, pq = gq >> 1;
+    const int hq = (int)(gq & 1), r = lane & 15;
+    const size_t Mp = (size_t)mtc * 16;
+    const int rt_down = g.qo_R / 16;
+    // the group's L_down fragments (fragments s = 2 hq, 2 hq + 1 of k-pair pq
+    // in the packed L_down [KP][R/16][4][64][8]), issued before the barrier
+    // so that their latency passes during it and the group arithmetic
+    constexpr int RTD = kMaxRank / 16;
+    v8h lb[RTD][2];
+#pragma unroll
+    for (int t = 0; t < RTD; ++t) {
+      if (t < rt_down) {   // uniform
+        const _Float16* lp = reinterpret_cast<const _Float16*>(g.qo_ldown) +
+                             (((size_t)pq * rt_down + t) * 4 + 2 * hq) * 64 * 8 + lane * 8;
+        lb[t][0] = *reinterpret_cast<const v8h*>(lp);
+        lb[t][1] = *reinterpret_cast<const v8h*>(lp + 64 * 8);
+      }
+    }
+    // a bare barrier after this wave's LDS writes (__syncthreads would also
+    // wait for the loads just issued)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes are done
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    for (int q = wave; q < BMT; q += NW) {
+      const uint32_t mt = mt0 + q;
+      if (mt >= mtc) break;   // wave-uniform; later q lie further out
+      const uint16_t* hr = hs + (q * 16 + r) * HST + c * 16;
+      const v8h lo = *reinterpret_cast<const v8h*>(hr);
+      const v8h hi = *reinterpret_cast<const v8h*>(hr + 8);
+      uint32_t d0, d1;
+      const _Float16 s = quantize_group_row4(lo, hi, d0, d1);
+      const size_t tix = (size_t)mt * g.qo_kp + pq;   // code tile (row tile, k-pair)
+      *reinterpret_cast<v2u*>(g.qo_xq + tix * kTileBytes + lane * 16 + hq * 8) = v2u{d0, d1};
+      if (c == 0)
+        g.qo_sx[(tix * 16 + r) * 2 + hq] = (int64_t)mt * 16 + r < g.M ? __builtin_bit_cast(uint16_t, s) : 0;
+      // the group's share of LoRA-down: lo then hi
+#pragma unroll
+      for (int t = 0; t < RTD; ++t) {
+        if (t >= rt_down) break;   // uniform
+        v4f d = mfma_f16_16x16x32(lo, lb[t][0], v4f{0.f, 0.f, 0.f, 0.f});
+        d = mfma_f16_16x16x32(hi, lb[t][1], d);
+        float* out = g.qo_part + ((size_t)gq * Mp + (size_t)mt * 16 + c * 4) * g.qo_R + t * 16 + r;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) out[(size_t)ii * g.qo_R] = d[ii];
       }
     }
   }
@@ -1637,6 +1722,20 @@ static hipError_t launch_tiled_spl(const GemmArgs& a, int64_t mt, int64_t nt, di
     gemm_tiled_kernel<WM, WN, TM, TN, 0, NS, 1, false, OCC, KS, true><<<grid, block, 0, stream>>>(a, mt, nt);
     return hipGetLastError();
   }
+  if (a.qo_xq) {   // the gated output quantized for the next layer
+    if constexpr (GLU && WN * TN == 8 && KS == 1) {
+      switch (a.R / 16) {
+        case 0: gemm_tiled_kernel<WM, WN, TM, TN, 0, NS, SPL, true, OCC, 1, false, true><<<grid, block, 0, stream>>>(a, mt, nt); break;
+        case 1: gemm_tiled_kernel<WM, WN, TM, TN, 1, NS, SPL, true, OCC, 1, false, true><<<grid, block, 0, stream>>>(a, mt, nt); break;
+        case 2: gemm_tiled_kernel<WM, WN, TM, TN, 2, NS, SPL, true, OCC, 1, false, true><<<grid, block, 0, stream>>>(a, mt, nt); break;
+        case 3: gemm_tiled_kernel<WM, WN, TM, TN, 3, NS, SPL, true, OCC, 1, false, true><<<grid, block, 0, stream>>>(a, mt, nt); break;
+        case 4: gemm_tiled_kernel<WM, WN, TM, TN, 4, NS, SPL, true, OCC, 1, false, true><<<grid, block, 0, stream>>>(a, mt, nt); break;
+        default: return hipErrorInvalidValue;
+      }
+      return hipGetLastError();
+    }
+    return hipErrorInvalidValue;   // this tile shape does not hold whole groups of h
+  }
   switch (a.R / 16) {
     case 0: gemm_tiled_kernel<WM, WN, TM, TN, 0, NS, SPL, GLU, OCC, KS><<<grid, block, 0, stream>>>(a, mt, nt); break;
     case 1: gemm_tiled_kernel<WM, WN, TM, TN, 1, NS, SPL, GLU, OCC, KS><<<grid, block, 0, stream>>>(a, mt, nt); break;
@@ -1832,6 +1931,41 @@ static hipError_t launch_tiled_pick(const GemmArgs& a, int cfg, bool lean, hipSt
     default: break;
   }
   return hipErrorInvalidValue;   // no tile shape fits, or one that cannot pair (gate, up) tiles
+}
+
+// The quantized gated output needs workgroups of 8 packed column tiles (one
+// 64-column group of h): the 128 x 128 and 64 x 128 shapes, chosen by the
+// same cost model (W4A4_TILED_CFG forces one of the two).  The lean variant
+// is also taken once the grid exceeds two workgroups per CU: its epilogue
+// then costs less than a second round of workgroups (measured over the MLP
+// shapes at M = 64 .. 8192: 24.0 against 26.6 us at M = 700, 15.5 against
+// 13.9 us at M = 64, where the grid is 48 workgroups).
+constexpr int kQuantOutCfgs[] = {0, 1};
+
+hipError_t launch_gemm_glu_quant(const GemmArgs& a, hipStream_t stream) {
+  if (!a.glu || !a.qo_xq || a.M <= 16 || a.ks < 1 || a.ks > kMaxTiledLoraSplits || (a.N / 2) % kKPair != 0)
+    return hipErrorInvalidValue;
+  const int64_t mt = round_up16(a.M) / 16, nt = a.N / 16, kp = a.K / kKPair;
+  int cfg = -1;
+  const int ov = tiled_override();
+  for (int i : kQuantOutCfgs)
+    if (i == ov) cfg = ov;
+  if (cfg < 0) {
+    double best_c = 0;
+    for (int i : kQuantOutCfgs) {
+      const double c = tiled_cost(kTiledCfgs[i], mt, nt, kp);
+      if (cfg < 0 || c < best_c) {
+        best_c = c;
+        cfg = i;
+      }
+    }
+  }
+  const TiledCfg& c = kTiledCfgs[cfg];
+  const int64_t nblk = ((mt + c.wm * c.tm - 1) / (c.wm * c.tm)) * ((nt + c.wn * c.tn - 1) / (c.wn * c.tn));
+  const char* e = std::getenv("W4A4_TILED_LEAN");
+  const bool forced = e && (e[0] == '0' || e[0] == '1');
+  const bool lean = tiled_lean(cfg, a.M, a.N, a.K) || (!forced && nblk > 2 * 256);
+  return launch_tiled_pick<true>(a, cfg, lean, stream);
 }
 
 int choose_variant(int64_t M, int64_t N, int64_t K, int R) {

@@ -18,81 +18,10 @@
 // in LDS in a fixed wave order, so results are deterministic (no atomics and
 // no separate repack kernel for lora_act).
 #include "device_common.hpp"
+#include "quant_common.hpp"
 #include "w4a4_internal.hpp"
 
 namespace w4a4 {
-
-// Codes for 8 values (one dword): q = clamp(rint(fl32(x / s)), -8, 7) with
-// round-half-to-even, where s is the group's fp16 scale (sf, exact in fp32)
-// and rs ~ 1/s (v_rcp_f32, ~1 ulp).
-//
-// No IEEE division is needed.  x and s are fp16 values, so x/s is a ratio of
-// two integers of at most 11 bits times a power of two; unless it is exactly
-// a half-integer, it lies at least 2^-13 away from every half-integer, far
-// beyond the error of t = x * rs (< 2^-19 for |x/s| <= 8.5), so rint(t) is the
-// nearest integer to x/s -- the same as the nearest integer to fl32(x/s).
-// When x/s is exactly a half-integer, fl32(x/s) is that half-integer and the
-// rule rounds it to the even neighbour.  The residual f = x - n*s is exact
-// (n*s has <= 15 significant bits and |f| <= s/2, so f needs <= 12 bits), and
-// x/s is a half-integer exactly when |f| == s/2.  Such ties are rare, so the
-// fix-up runs on a wave-uniform branch taken only when some lane has one.
-//
-// Packing: for an integer n in [-8, 7] and j < 4, n + 1.5 * 2^(23 - 4j) is
-// exact and its bit pattern holds n << 4j (two's complement) in bits
-// [4j, 4j + 4), so one and-or puts a code in place within a 16-bit half.
-__device__ __forceinline__ uint32_t quantize8(v8h v, float sf, float rs) {
-  float n[8], f[8];
-  bool tie = false;
-  const float half_s = 0.5f * sf;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float x = (float)v[i];
-    n[i] = __builtin_rintf(x * rs);
-    f[i] = __builtin_fmaf(-n[i], sf, x);
-    tie |= __builtin_fabsf(f[i]) == half_s;
-  }
-  if (__builtin_amdgcn_ballot_w64(tie) != 0) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const bool fix = (__builtin_fabsf(f[i]) == half_s) & ((((int)n[i]) & 1) != 0);
-      n[i] = fix ? n[i] + __builtin_copysignf(1.0f, f[i]) : n[i];
-    }
-  }
-  // two 16-bit halves, each built with the biases 1.5 * 2^(23 - 4j), j < 4,
-  // whose own set bits (22 and up) stay clear of bits [0, 16)
-  uint32_t half[2] = {0u, 0u};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int j = i & 3;
-    const float q = __builtin_amdgcn_fmed3f(n[i], -8.0f, 7.0f);
-    const float biased = q + __builtin_ldexpf(1.5f, 23 - 4 * j);   // constant per i
-    half[i >> 2] |= __builtin_bit_cast(uint32_t, biased) & (0xFu << (4 * j));
-  }
-  return half[0] | (half[1] << 16);
-}
-
-// max |x| over 8 fp16 values: for fp16, |x| orders like (bits & 0x7fff) as
-// unsigned integers, so the max is taken on the bit patterns.
-__device__ __forceinline__ uint32_t absmax8_bits(v8h v, uint32_t m) {
-  const v4u w = __builtin_bit_cast(v4u, v);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t a = w[i] & 0x7FFF7FFFu;
-    const uint32_t lo = a & 0xFFFFu, hi = a >> 16;
-    m = m > lo ? m : lo;
-    m = m > hi ? m : hi;
-  }
-  return m;
-}
-
-// Scale of a group from its absmax: fp16(fp32(amax / 7)) with the IEEE fp32
-// division (one per group); a zero scale becomes 2^-24.
-__device__ __forceinline__ _Float16 group_scale(float amax) {
-  float s32 = amax / 7.0f;
-  _Float16 s = (_Float16)s32;
-  if (s == (_Float16)0.0f) s = __builtin_bit_cast(_Float16, (uint16_t)1);
-  return s;
-}
 
 // Grid (rows_padded/16 * 16/rh, ks) x NW waves.  Workgroup (x, j) handles
 // rows [r0, r0 + rh) of the 16-row tile rt = x / (16/rh), r0 = (x % (16/rh)) *
@@ -211,19 +140,7 @@ __global__ __launch_bounds__(NW * 64) void quantize_rows_kernel(
     _Float16 sc[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      uint32_t amb = absmax8_bits(v[2 * h + 1], absmax8_bits(v[2 * h], 0u));
-      // each shuffle is taken once, by every lane (a shuffle under a lane
-      // mask reads 0 from inactive source lanes)
-      const uint32_t o16 = (uint32_t)__shfl_xor((int)amb, 16);
-      amb = amb > o16 ? amb : o16;
-      const uint32_t o32 = (uint32_t)__shfl_xor((int)amb, 32);
-      amb = amb > o32 ? amb : o32;
-      const float am = half_bits_to_float((uint16_t)amb);
-      const _Float16 s = group_scale(am);
-      const float sf = (float)s;
-      const float rs = __builtin_amdgcn_rcpf(sf);
-      d[2 * h] = quantize8(v[2 * h], sf, rs);
-      d[2 * h + 1] = quantize8(v[2 * h + 1], sf, rs);
+      const _Float16 s = quantize_group_row4(v[2 * h], v[2 * h + 1], d[2 * h], d[2 * h + 1]);
       sc[h] = valid ? s : (_Float16)0.0f;
     }
     uint8_t* tile = codes + (size_t)(rt * KP + p) * kTileBytes;
@@ -420,6 +337,40 @@ __global__ void pack_affine_kernel(const float* __restrict__ cs, const float* __
 hipError_t launch_pack_affine(const float* col_scale, const float* bias, int64_t N,
                               float* a, float* b, hipStream_t stream) {
   pack_affine_kernel<<<(unsigned)((N + 255) / 256), 256, 0, stream>>>(col_scale, bias, N, a, b);
+  return hipGetLastError();
+}
+
+// lora_act partials of an activation blob from per-64-group LoRA-down
+// partials (the gated GEMM's quantized output writes them): thread e owns one
+// float of [Mp][R]; split j = blockIdx.y sums its groups in increasing order
+// starting from 0, so the result does not depend on scheduling.  Up to 32
+// loads are in flight at a time (one memory round trip per 32 groups: the
+// pass is bound by latency, not bandwidth), and one thread per float (not
+// per four) puts more of them in flight overall.
+__global__ __launch_bounds__(256) void lora_group_sum_kernel(const float* __restrict__ part, int64_t n,
+                                                             int64_t KP, int ks, float* __restrict__ la) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= n) return;
+  const int64_t j = blockIdx.y;
+  const int64_t g0 = 2 * (j * KP / ks), g1 = 2 * ((j + 1) * KP / ks);
+  constexpr int B = 32;
+  float s = 0.f;
+  for (int64_t b = g0; b < g1; b += B) {
+    float v[B];
+#pragma unroll
+    for (int q = 0; q < B; ++q) v[q] = b + q < g1 ? part[(b + q) * n + e] : 0.f;
+#pragma unroll
+    for (int q = 0; q < B; ++q) s += v[q];
+  }
+  la[j * n + e] = s;
+}
+
+hipError_t launch_lora_group_sum(const float* part, int64_t Mp, int R, int64_t K, int ks, float* la,
+                                 hipStream_t stream) {
+  const int64_t KP = K / kKPair, n = Mp * R;
+  if (R <= 0 || R % 16 != 0 || Mp % 16 != 0 || ks < 1 || ks > KP || KP < 1) return hipErrorInvalidValue;
+  dim3 grid((unsigned)((n + 255) / 256), (unsigned)ks), block(256);
+  lora_group_sum_kernel<<<grid, block, 0, stream>>>(part, n, KP, ks, la);
   return hipGetLastError();
 }
 

@@ -135,6 +135,19 @@ struct GemmArgs {
   // nothing else is written (y is not touched).
   int32_t* psum = nullptr;
   int64_t ps_m0 = 0, ps_mc = 0, ps_n0 = 0, ps_nc = 0;
+  // Quantized gated output (qo_xq != nullptr; gated layers with M > 16, a
+  // tile shape of 8 packed column tiles per workgroup): in place of h the
+  // epilogue writes the next layer's activation blob pieces for h (K' = N/2
+  // columns, qo_kp = K'/128 k-pairs, Mp/16 row tiles) -- codes qo_xq and
+  // scales qo_sx, as the activation pass would write them -- and the
+  // LoRA-down partial of every 64-column group of h, qo_part[g][Mp][qo_R]
+  // (fp32), from the next layer's packed L_down qo_ldown (rank qo_R).
+  uint8_t* qo_xq = nullptr;
+  uint16_t* qo_sx = nullptr;
+  float* qo_part = nullptr;
+  const uint16_t* qo_ldown = nullptr;
+  int qo_R = 0;
+  int64_t qo_kp = 0;
 };
 
 enum Variant { kDecode = 1, kPrefill = 2 };
@@ -145,5 +158,16 @@ int choose_variant(int64_t M, int64_t N, int64_t K, int R);
 // layer; the kernel, its tile shape and variant depend only on the shape (and
 // the W4A4_TILED_* tuning overrides), never on which of the two is asked.
 hipError_t launch_gemm(const GemmArgs& a, int variant, hipStream_t stream);
+
+// The gated GEMM with the quantized output (a.qo_xq set, a.glu = 1, M > 16),
+// on the tile shapes whose workgroups hold one 64-column group of h.
+hipError_t launch_gemm_glu_quant(const GemmArgs& a, hipStream_t stream);
+
+// lora_act of an activation blob from per-64-group LoRA-down partials
+// part[g][Mp][R] (G = K/64 groups): partial j of the blob's ks K-range
+// splits (k-pairs [j*KP/ks, (j+1)*KP/ks)) is the sum of its groups' partials
+// taken in increasing g.
+hipError_t launch_lora_group_sum(const float* part, int64_t Mp, int R, int64_t K, int ks, float* la,
+                                 hipStream_t stream);
 
 }  // namespace w4a4

@@ -213,6 +213,23 @@ int w4a4_linear_glu_quant(int64_t M, int64_t N, int64_t K, int32_t R, int32_t r_
  * M out of range. */
 int w4a4_glu_quant_workspace(int64_t M, int64_t N, int32_t R_down, size_t* bytes);
 
+/* w4a4_linear_glu_quant for callers that cannot allocate (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same call and results, with the workspace taken from a library-owned
+ * device array of W4A4_NOALLOC_SCRATCH_BYTES bytes per GPU (file-scope
+ * device memory, held by every GPU the library runs on until the process
+ * ends) instead of an argument.  Allocates nothing.  The array keeps the
+ * last call's contents (no call needs them cleared); calls that overlap on
+ * one GPU -- on different streams or from different host threads -- share
+ * it and race.  W4A4_ERR_SHAPE when w4a4_glu_quant_workspace(M, N, R_down)
+ * exceeds the array (use w4a4_linear_glu_quant with a workspace of its own
+ * then); W4A4_ERR_HIP if the array's device address cannot be obtained.
+ * Other arguments and errors as w4a4_linear_glu_quant. */
+#define W4A4_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int w4a4_linear_glu_quant_noalloc(int64_t M, int64_t N, int64_t K, int32_t R, int32_t r_gate,
+                                  const void* act, const void* wblob, int32_t R_down,
+                                  const void* down_wblob, void* act_out, void* stream);
+
 /* Which GEMM kernel w4a4_linear runs for a shape (host-only):
  * 1 = decode (M <= 16), 2 = prefill (tiled); -W4A4_ERR_SHAPE if the
  * shape is unsupported.  Lets a caller log the kernel chosen per layer

@@ -248,6 +248,30 @@ def test_glu_quant_workspace_and_validation():
     assert q(*args(ws=3 * big)) == 4       # the workspace over the down layer's L_down
 
 
+def test_glu_quant_noalloc_validation():
+    """The allocation-free variant: the size limit of its array and every
+    argument error are returned on the host before any device call."""
+    lib = _lib()
+    assert W.NOALLOC_SCRATCH_BYTES == 32 << 20
+    big = 1 << 30
+    q = lib.w4a4_linear_glu_quant_noalloc
+    args = lambda **kw: [kw.get(k, v) for k, v in (
+        ("M", 40), ("N", 256), ("K", 128), ("R", 32), ("rg", 16), ("act", FAKE), ("wb", 2 * big),
+        ("Rd", 16), ("dwb", 3 * big), ("out", 4 * big), ("s", None))]
+    assert q(*args(N=192)) == 2
+    assert q(*args(Rd=8)) == 2
+    assert q(*args(out=None)) == 1
+    assert q(*args(dwb=None)) == 1
+    assert q(*args(act=FAKE + 16)) == 3
+    assert q(*args(out=FAKE + 256)) == 4
+    assert q(*args(M=0, act=None, wb=None, dwb=None, out=None)) == 0
+    # a workspace need above the array (M=8192, 3072 columns of h, rank 32:
+    # 48 MiB of LoRA-down shares) is a shape error
+    assert W.w4a4_glu_quant_workspace(8192, 6144, 32) > W.NOALLOC_SCRATCH_BYTES
+    assert q(*args(M=8192, N=6144, K=1024, wb=2 * big, dwb=3 * big, out=4 * big)) == 2
+    assert W.w4a4_glu_quant_workspace(4096, 6144, 32) <= W.NOALLOC_SCRATCH_BYTES
+
+
 def test_query_variant_is_host_only():
     for M in (1, 4, 16, 700, 8192):
         assert W.w4a4_query_variant(M, 4096, 4096, 32) == (1 if M <= 16 else 2)

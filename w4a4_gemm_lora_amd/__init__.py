@@ -28,7 +28,7 @@ __all__ = [
     "W4A4Error", "lib_path", "load_library", "w4a4_status_string",
     "w4a4_weight_layout", "w4a4_act_layout", "w4a4_pack_weights",
     "w4a4_quantize_act", "w4a4_quantize_act_rmsnorm", "w4a4_linear", "w4a4_linear_glu",
-    "w4a4_linear_glu_quant", "w4a4_glu_quant_workspace",
+    "w4a4_linear_glu_quant", "w4a4_glu_quant_workspace", "w4a4_linear_glu_quant_noalloc",
     "w4a4_query_variant", "GatedMLPUp", "GatedMLP",
     "w4a4_debug_group_psums", "w4a4_debug_group_psums_glu", "alloc_weight_blob", "alloc_act_blob",
     "PackedLinear", "LayerGraphs", "EXPORTED_SYMBOLS", "PEAKS_SYMBOLS", "load_peaks_library",
@@ -38,7 +38,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 EXPORTED_SYMBOLS = (
     "w4a4_status_string", "w4a4_weight_layout", "w4a4_act_layout",
     "w4a4_pack_weights", "w4a4_quantize_act", "w4a4_quantize_act_rmsnorm", "w4a4_linear",
-    "w4a4_linear_glu", "w4a4_linear_glu_quant", "w4a4_glu_quant_workspace", "w4a4_query_variant",
+    "w4a4_linear_glu", "w4a4_linear_glu_quant", "w4a4_glu_quant_workspace", "w4a4_linear_glu_quant_noalloc",
+    "w4a4_query_variant",
     "w4a4_debug_group_psums",
     "w4a4_debug_group_psums_glu", "w4a4_graph_begin", "w4a4_graph_end", "w4a4_layer_graph_create", "w4a4_graph_launch",
     "w4a4_graph_destroy",
@@ -128,6 +129,7 @@ def load_library() -> ctypes.CDLL:
     lib.w4a4_linear_glu.argtypes = [_i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _i64, _vp]
     lib.w4a4_linear_glu_quant.argtypes = [_i64, _i64, _i64, _i32, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp]
     lib.w4a4_glu_quant_workspace.argtypes = [_i64, _i64, _i32, ctypes.POINTER(_sz)]
+    lib.w4a4_linear_glu_quant_noalloc.argtypes = [_i64, _i64, _i64, _i32, _i32, _vp, _vp, _i32, _vp, _vp, _vp]
     lib.w4a4_query_variant.argtypes = [_i64, _i64, _i64, _i32]
     lib.w4a4_layer_graph_create.argtypes = [_i64, _i64, _i64, _i32, _vp, _i64, _vp, ctypes.c_double,
                                             _vp, _vp, _vp, _i64, ctypes.POINTER(_vp)]
@@ -250,6 +252,16 @@ def w4a4_linear_glu_quant(M, N, K, R, r_gate, act, wblob, R_down, down_wblob, ac
                                               _ptr(down_wblob), _ptr(act_out), _ptr(workspace),
                                               _stream(stream))
     _check(st, "w4a4_linear_glu_quant")
+
+
+# Bytes of the library-owned array w4a4_linear_glu_quant_noalloc uses per GPU
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def w4a4_linear_glu_quant_noalloc(M, N, K, R, r_gate, act, wblob, R_down, down_wblob, act_out, stream=None):
+    st = load_library().w4a4_linear_glu_quant_noalloc(M, N, K, R, r_gate, _ptr(act), _ptr(wblob), R_down,
+                                                      _ptr(down_wblob), _ptr(act_out), _stream(stream))
+    _check(st, "w4a4_linear_glu_quant_noalloc")
 
 
 def w4a4_debug_group_psums(M, N, K, R, act, wblob, m0, mc, n0, nc, out, stream=None):

@@ -18,7 +18,7 @@ OUT = os.path.join(PKG, "libw4a4.so")
 PEAKS_OUT = os.path.join(PKG, "libw4a4_peaks.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.cpp", "graph.cpp", "quantize.hip", "gemm.hip"]
+SOURCES = ["api.cpp", "graph.cpp", "quantize.hip", "gemm.hip", "noalloc.hip"]
 # measurement-only microbenchmarks (attainable peaks), a library of their own
 PEAKS_SOURCES = ["peaks.hip"]
 

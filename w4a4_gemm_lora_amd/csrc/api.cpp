@@ -275,10 +275,11 @@ static bool glu_quant_in_epilogue(int64_t M, int64_t H) {
   return ((M + 63) / 64) * (H / kGroup) >= 128;
 }
 
+// [a, a + na) and [b, b + nb) share a byte (a NULL pointer covers nothing)
 static bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   const uint8_t* pa = static_cast<const uint8_t*>(a);
   const uint8_t* pb = static_cast<const uint8_t*>(b);
-  return na > 0 && nb > 0 && pa < pb + nb && pb < pa + na;
+  return pa && pb && na > 0 && nb > 0 && pa < pb + nb && pb < pa + na;
 }
 
 static int check_glu_quant(int64_t M, int64_t N, int64_t K, int32_t R, int32_t r_gate, int32_t R_down) {
@@ -300,15 +301,20 @@ int w4a4_glu_quant_workspace(int64_t M, int64_t N, int32_t R_down, size_t* bytes
   return W4A4_OK;
 }
 
-int w4a4_linear_glu_quant(int64_t M, int64_t N, int64_t K, int32_t R, int32_t r_gate, const void* act,
-                          const void* wblob, int32_t R_down, const void* down_wblob, void* act_out,
-                          void* workspace, void* stream) {
+}  // extern "C"
+
+// w4a4_linear_glu_quant, or with validate_only its argument checks alone
+// (the workspace may then be NULL: it is not checked).
+int w4a4::glu_quant_call(int64_t M, int64_t N, int64_t K, int32_t R, int32_t r_gate, const void* act,
+                         const void* wblob, int32_t R_down, const void* down_wblob, void* act_out,
+                         void* workspace, void* stream, bool validate_only) {
   int st = check_glu_quant(M, N, K, R, r_gate, R_down);
   if (st) return st;
   if (M == 0) return W4A4_OK;
   const int64_t H = N / 2;
   const size_t ws = glu_quant_workspace(M, N, R_down);
-  if (!act || !wblob || !act_out || (R_down > 0 && !down_wblob) || (ws > 0 && !workspace)) return W4A4_ERR_NULL;
+  if (!act || !wblob || !act_out || (R_down > 0 && !down_wblob) || (ws > 0 && !workspace && !validate_only))
+    return W4A4_ERR_NULL;
   if (!aligned(act, 256) || !aligned(wblob, 256) || !aligned(act_out, 256) ||
       (down_wblob && !aligned(down_wblob, 256)) || (workspace && !aligned(workspace, 256)))
     return W4A4_ERR_ALIGN;
@@ -320,6 +326,7 @@ int w4a4_linear_glu_quant(int64_t M, int64_t N, int64_t K, int32_t R, int32_t r_
       overlaps(act_out, og.total, down_wblob, dt) || overlaps(act_out, og.total, workspace, ws) ||
       overlaps(workspace, ws, act, at) || overlaps(workspace, ws, wblob, wt) || overlaps(workspace, ws, down_wblob, dt))
     return W4A4_ERR_ARG;
+  if (validate_only) return W4A4_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool in_epilogue = glu_quant_in_epilogue(M, H);
   if (log_enabled())
@@ -350,6 +357,14 @@ int w4a4_linear_glu_quant(int64_t M, int64_t N, int64_t K, int32_t R, int32_t r_
     e = launch_lora_group_sum(static_cast<const float*>(workspace), og.Mp, R_down, H, og.ks,
                               reinterpret_cast<float*>(ob + og.off_la), s);
   return hip_status(e);
+}
+
+extern "C" {
+
+int w4a4_linear_glu_quant(int64_t M, int64_t N, int64_t K, int32_t R, int32_t r_gate, const void* act,
+                          const void* wblob, int32_t R_down, const void* down_wblob, void* act_out,
+                          void* workspace, void* stream) {
+  return glu_quant_call(M, N, K, R, r_gate, act, wblob, R_down, down_wblob, act_out, workspace, stream, false);
 }
 
 int w4a4_query_variant(int64_t M, int64_t N, int64_t K, int32_t R) {

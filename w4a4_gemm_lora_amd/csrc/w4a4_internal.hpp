@@ -167,6 +167,12 @@ hipError_t launch_gemm_glu_quant(const GemmArgs& a, hipStream_t stream);
 // part[g][Mp][R] (G = K/64 groups): partial j of the blob's ks K-range
 // splits (k-pairs [j*KP/ks, (j+1)*KP/ks)) is the sum of its groups' partials
 // taken in increasing g.
+// w4a4_linear_glu_quant's body; with validate_only, its host-side argument
+// checks alone (nothing is enqueued; the workspace is not checked).
+int glu_quant_call(int64_t M, int64_t N, int64_t K, int32_t R, int32_t r_gate, const void* act,
+                   const void* wblob, int32_t R_down, const void* down_wblob, void* act_out,
+                   void* workspace, void* stream, bool validate_only);
+
 hipError_t launch_lora_group_sum(const float* part, int64_t Mp, int R, int64_t K, int ks, float* la,
                                  hipStream_t stream);
 

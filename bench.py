@@ -604,7 +604,8 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="prefill")
+    ap.add_argument("--workload", default=None,
+                    help="prefill (default), decode, mlp_up, mlp_down, small; --mlp defaults to mlp_up")
     ap.add_argument("--m", type=int, default=None, help="row count override (decode sweep)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--settle-ms", type=float, default=1000.0,
@@ -636,6 +637,8 @@ def main(argv=None):
     ap.add_argument("--ingest-sq", metavar="DIR",
                     help="record a rocprofv3 SQ instruction-mix counter run (DIR) for --workload")
     args = ap.parse_args(argv)
+    if args.workload is None:
+        args.workload = "mlp_up" if args.mlp else "prefill"
     if args.ingest_pmc:
         ingest_pmc(args.workload, *args.ingest_pmc, command=args.pmc_command)
         return 0

@@ -2,8 +2,10 @@
 
 Bar: packed codes, scales and per-group integer sums bit-exact; lora_act
 within 1e-4 * rms; Y within max|dY| <= 2e-2 * rms(Y_oracle) and
-mean|dY| <= 2e-3 * rms(Y_oracle).  Full-size workloads compare every output
-the oracle finishes in seconds and sampled windows of the largest one.
+mean|dY| <= 2e-3 * rms(Y_oracle), rms over every compared output; an output
+beyond the max bar passes only as the other correct fp16 rounding of a near
+tie (tests/parity_bar.py).  Every workload is compared output by output,
+the largest (M=8192, K=N=4096) too.
 """
 import json
 import os

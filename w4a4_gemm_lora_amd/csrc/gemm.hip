@@ -1981,7 +1981,18 @@ hipError_t launch_gemm(const GemmArgs& a, int variant, hipStream_t stream) {
       if (a.ks < 1 || a.ks > kMaxTiledLoraSplits) return hipErrorInvalidValue;   // lora_splits() for M > 16
       {
         const int cfg = pick_tiled(a.M, a.N, a.K, a.R, a.ks, a.glu != 0);
-        const bool lean = tiled_lean(cfg, a.M, a.N, a.K);
+        bool lean = tiled_lean(cfg, a.M, a.N, a.K);
+        if (a.glu && !lean && kLeanCfg[cfg]) {
+          // a gated grid beyond one round of resident workgroups takes the
+          // lean variant (M=700, 6144 packed columns, K=1024: 1056 workgroups
+          // of 64 x 64 for 1024 slots, 18.7 -> 17.3 us; its extra epilogue
+          // round trip costs less than the second round)
+          const TiledCfg& c = kTiledCfgs[cfg];
+          const int64_t nblk = ((round_up16(a.M) / 16 + c.wm * c.tm - 1) / (c.wm * c.tm)) *
+                               ((a.N / 16 + c.wn * c.tn - 1) / (c.wn * c.tn));
+          const char* e = std::getenv("W4A4_TILED_LEAN");
+          if (!(e && (e[0] == '0' || e[0] == '1')) && nblk > (int64_t)c.occ * 256) lean = true;
+        }
         return a.glu ? launch_tiled_pick<true>(a, cfg, lean, stream) : launch_tiled_pick<false>(a, cfg, lean, stream);
       }
     default:

@@ -18,17 +18,25 @@
 // parts, accumulating straight into the main accumulator; the affine and the
 // fp16 rounding follow in registers.
 //
+// Kernels: gemm_tiled_kernel (M > 16, nine tile shapes, lean and K-split
+// variants), gemm_wide_kernel (M > 16 on large grids: 256 x 128 with the
+// accumulators laid out for the 4-block f16 MFMA), gemm_decode_kernel (MFMA
+// decode, M <= 16) and gemm_decode_dot_kernel (v_dot8 on the packed nibbles,
+// M <= 4).  Each has a diagnostic instance (PSUM) that stores the exact group
+// sums in place of the scale-accumulate.
+//
 // Gated variant (GLU template flag): for the MLP's gate and up projections
 // packed as one layer with their rows interleaved by 16-row tiles (voice-
 // clone article, section 3.1: the Qwen3 MLP computes SiLU(gate) * up), a
 // wave or workgroup always holds a (gate, up) tile pair, rounds both to fp16
 // as the two layers would store them, and writes fp16(SiLU(g) * u) to one
-// output tile (glu_bits).
+// output tile (glu_bits) -- or, with QOUT, quantizes it for the next layer.
 //
 // Cost model measured on MI355X: one v_mfma_i32_16x16x64_i8 occupies a SIMD
-// for ~16.5 cycles and a wave64 fp32 VALU op for ~2.6-2.9 cycles, and the two
-// barely overlap, so the per-group epilogue (convert, scale product, fma on
-// four accumulators per lane) costs about twice the MFMA itself; the tiled
+// for ~16.5 cycles and a wave64 fp32 VALU op for ~4.2-4.8 cycles (16 lanes
+// per clock), and inside these loops the two barely overlap, so the
+// per-group epilogue (scale product, fma on four accumulators per lane, and
+// the nibble expansion) costs about as much as the integer MFMAs; the tiled
 // kernel trades the four conversions for half of one more 4x4x4 MFMA.  Large-M
 // kernels are therefore bound by issue of MFMA + VALU, not by HBM.
 #include <cstdlib>

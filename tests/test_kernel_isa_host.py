@@ -163,3 +163,23 @@ def test_every_instance_fits_its_occupancy(asm):
     assert seen["tiled"] >= 100 and seen["wide"] >= 10 and seen["decode"] >= 40 and seen["other"] >= 5, seen
     # the quantized gated output: 128 x 128 and 64 x 128, both occupancies, every rank, 1 or 4 partials
     assert seen["tiled_qout"] == 2 * 2 * 5 * 2, seen
+
+
+def test_rmsnorm_conversion_keeps_its_fp32_step(asm):
+    """The fused RMSNorm pass rounds its fp64 value to fp32 and then to fp16
+    (two hardware conversions per value).  Under fp contraction the backend
+    may merge the two into one software fp64 -> fp16 rounding, recognisable
+    by its extraction of the double's exponent field (bits 20..30 of the
+    high dword); that rounding differs from the two-step one at fp16 ties of
+    the fp32 value, so no instance may contain it."""
+    lines = asm["quantize.hip"].split("\n")
+    name, checked = None, 0
+    for line in lines:
+        m = re.match(r"^(_ZN4w4a420quantize_rows_kernelILi\d+ELi\d+ELb(\d)E\S*):", line)
+        if m:
+            name = m.group(1) if m.group(2) == "1" else None
+            checked += name is not None
+            continue
+        if name and re.search(r"v_bfe_u32\s+v\d+, v\d+, 20, 11\b", line):
+            raise AssertionError(f"{name}: one-step fp64 -> fp16 conversion")
+    assert checked >= 15   # every RMSNorm instance (rank 0..64, 2..16 waves)

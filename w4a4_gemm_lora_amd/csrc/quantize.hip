@@ -106,6 +106,11 @@ __global__ __launch_bounds__(NW * 64) void quantize_rows_kernel(
   auto load_x = [&](int64_t p, v8h* v) {
     load_raw(p, v);
     if constexpr (NORM) {
+      // No contraction here: under it the backend may merge the two
+      // conversions fp64 -> fp32 -> fp16 into one rounding fp64 -> fp16,
+      // which differs from the two-step rounding where the first lands on an
+      // fp16 tie.
+#pragma clang fp contract(off)
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int64_t k = p * kKPair + (s >> 1) * kGroup + c * 16 + (s & 1) * 8;

@@ -43,7 +43,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # sources that define the GEMM kernels: a measured traffic figure is only
 # reported while they are unchanged
 KERNEL_SOURCES = ["w4a4_gemm_lora_amd/csrc/gemm.hip", "w4a4_gemm_lora_amd/csrc/device_common.hpp",
-                  "w4a4_gemm_lora_amd/csrc/w4a4_internal.hpp"]
+                  "w4a4_gemm_lora_amd/csrc/w4a4_internal.hpp", "w4a4_gemm_lora_amd/csrc/quant_common.hpp"]
 COPY_BYTES = 256 << 20      # the calibration copy moves this many bytes each way
 
 

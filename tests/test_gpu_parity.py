@@ -173,6 +173,57 @@ def test_quantizer_golden_groups_on_gpu():
     assert np.array_equal(a["qx"][:M], qx)
 
 
+def _every_quotient_groups():
+    """fp16 rows whose 64-groups put every fp16 x against many scales: each
+    group holds its absmax A first (so s = fp16(A / 7)) and then 63 values
+    taken in order, with alternating signs, from every fp16 value in
+    [A / 28, A] (smaller values quantize to 0).  A runs over every fp16 value
+    in [7, 14) (s over [1, 2)) and every 16th one below 7 * 2^-14 (subnormal
+    scales, from the 2^-24 floor up)."""
+    allv = np.arange(1, 0x7C00, dtype=np.uint16).view(np.float16)
+    a_norm = allv[(allv >= 7) & (allv < 14)]
+    a_sub = allv[allv < np.float16(7 * 2.0 ** -14)][::16]
+    groups = []
+    for A in np.concatenate([a_norm, a_sub]):
+        x = allv[(allv >= np.float16(A / 28)) & (allv <= A)]
+        x = np.where(np.arange(x.size) % 2 == 1, -x, x).astype(np.float16)
+        n = -(-x.size // 63)
+        body = np.zeros(n * 63, np.float16)
+        body[: x.size] = x
+        g = np.empty((n, 64), np.float16)
+        g[:, 0] = A
+        g[:, 1:] = body.reshape(n, 63)
+        groups.append(g)
+    return np.concatenate(groups)
+
+
+def test_quantizer_every_quotient_on_gpu():
+    """Codes and scales bit-exact against the oracle's IEEE-division
+    quantizer over every fp16 value against ~1500 scales: the activation
+    pass divides by no scale (one Newton step from the hardware reciprocal
+    gives the quotient), and ties, the clamp at -8 (A's negated neighbours
+    never reach it, the subnormal scales do) and the 2^-24 floor must come
+    out as the rule has them."""
+    g = _every_quotient_groups()
+    K = 4096
+    M = -(-g.shape[0] // (K // 64))
+    x = np.zeros((M * (K // 64), 64), np.float16)
+    x[: g.shape[0]] = g
+    x = x.reshape(M, K)
+    _say(f"[quant] every quotient: {g.shape[0]} groups, M={M} K={K}")
+    torch = _torch()
+    act = W.alloc_act_blob(M, K, 0)
+    W.w4a4_quantize_act(M, K, 0, _to_dev(x), None, act)
+    torch.cuda.synchronize()
+    _, offs = W.w4a4_act_layout(M, K, 0)
+    a = split_act_blob(act.cpu().numpy(), M, K, 0, offs)
+    qx, sx = O.quantize_groups(x)
+    assert np.array_equal(a["sx"][:M].view(np.uint16), sx.view(np.uint16))
+    bad = np.argwhere(a["qx"][:M] != qx)
+    assert bad.size == 0, (f"{len(bad)} codes differ, first at {bad[:3].tolist()}: x="
+                           f"{[float(x[r, c]) for r, c in bad[:3]]}")
+
+
 WORKLOAD_CASES = ["small", "mlp_up", "mlp_down", "decode-1", "decode-2", "decode-4", "decode-16"]
 
 
@@ -455,6 +506,57 @@ def test_rmsnorm_quantize(M, K, N, R, eps):
     ref = O.linear(xn, case["lora_down"] if R else None, case["lora_up"] if R else None,
                    case["col_scale"], case["bias"], w16=case["w"])
     _check_y(run.host_y()[:M, :N], ref["y"], f"rmsnorm M={M} K={K} R={R}", y64=ref["y64"], ref=ref, case=case)
+
+
+def _double_rounding_rows(M=64, K=8192, eps=1e-6, seed=4300):
+    """RMSNorm inputs that expose a one-step fp64 -> fp16 conversion: each
+    64-group of row r has one dominant element (|x| in [2, 8], at column
+    64 G + r; the rest in [2^-4, 2^-2]), and each column's gamma is picked,
+    where one exists in [0.5, 2), so that the element's normalized value t =
+    (x inv) gamma rounds to a different fp16 directly than through fp32 --
+    the group's scale then shows which rounding the kernel took.  Every
+    |x| >= 2^-4 makes the row's sum of squares exact in any order, so the
+    kernel's inv is the oracle's."""
+    rng = np.random.default_rng(seed)
+    G = K // 64
+    x = (rng.uniform(2.0 ** -4, 2.0 ** -2, (M, K)) * rng.choice([-1.0, 1.0], (M, K))).astype(np.float16)
+    rows = np.arange(M)[:, None]
+    tcol = np.arange(G)[None, :] * 64 + rows % 64
+    x[rows, tcol] = (rng.uniform(2.0, 8.0, (M, G)) * rng.choice([-1.0, 1.0], (M, G))).astype(np.float16)
+    xd = x.astype(np.float64)
+    inv = 1.0 / np.sqrt((xd * xd).sum(axis=1) / K + eps)
+    gamma = rng.uniform(0.5, 2.0, K).astype(np.float16)
+    cand = np.arange(0x3800, 0x4000, dtype=np.uint16).view(np.float16)
+    k = np.arange(K)
+    base = xd[k % 64, k] * inv[k % 64]                              # x * inv, first rounding
+    t = base[:, None] * cand.astype(np.float64)[None, :]            # times gamma, second
+    hit = t.astype(np.float32).astype(np.float16) != t.astype(np.float16)
+    first = np.argmax(hit, axis=1)
+    has = hit[k, first]
+    gamma[has] = cand[first[has]]
+    return x, gamma, eps, int(has.sum())
+
+
+def test_rmsnorm_fp32_step_of_the_fp16_conversion():
+    """The normalized value is fp16(fp32(t)), two roundings: on inputs built
+    so that ~1000 group maxima round differently in one step
+    (_double_rounding_rows), codes and scales stay bit-exact.  The same
+    check on the CPU shows that a one-step conversion changes many scales,
+    so the test can tell the two apart."""
+    M, K, N, R = 64, 8192, 64, 16
+    x, gamma, eps, hits = _double_rounding_rows(M, K)
+    case = workloads.random_case(M, K, N, R, seed=4301)
+    case["x"] = x
+    xn, qx, sx, la = O.quantize_act_rmsnorm(x, gamma, eps, case["lora_down"])
+    xd = x.astype(np.float64)
+    t = (xd * (1.0 / np.sqrt((xd * xd).sum(axis=1) / K + eps))[:, None]) * gamma.astype(np.float64)[None, :]
+    _, sx_one_step = O.quantize_groups(t.astype(np.float16))
+    changed = int(np.sum(sx_one_step.view(np.uint16) != sx.view(np.uint16)))
+    _say(f"[rmsnorm double rounding] M={M} K={K}: {hits} targeted maxima, {changed} scales differ in one step")
+    assert hits > 400 and changed > 100
+    run = GpuRun(case, norm=(gamma, eps))
+    a = _check_quant(run, case, qx, sx)
+    _check_lora_act(a, la, M)
 
 
 def test_svdquant_checkpoint_layer():

@@ -10,66 +10,56 @@
 
 namespace w4a4 {
 
+typedef uint16_t v2u16 __attribute__((ext_vector_type(2)));
+
 // Codes for 8 values (one dword): q = clamp(rint(fl32(x / s)), -8, 7) with
 // round-half-to-even, where s is the group's fp16 scale (sf, exact in fp32)
-// and rs ~ 1/s (v_rcp_f32, ~1 ulp).
+// and rs ~ 1/s (v_rcp_f32, within 1 ulp).
 //
-// No IEEE division is needed.  x and s are fp16 values, so x/s is a ratio of
-// two integers of at most 11 bits times a power of two; unless it is exactly
-// a half-integer, it lies at least 2^-13 away from every half-integer, far
-// beyond the error of t = x * rs (< 2^-19 for |x/s| <= 8.5), so rint(t) is the
-// nearest integer to x/s -- the same as the nearest integer to fl32(x/s).
-// When x/s is exactly a half-integer, fl32(x/s) is that half-integer and the
-// rule rounds it to the even neighbour.  The residual f = x - n*s is exact
-// (n*s has <= 15 significant bits and |f| <= s/2, so f needs <= 12 bits), and
-// x/s is a half-integer exactly when |f| == s/2.  Such ties are rare, so the
-// fix-up runs on a wave-uniform branch taken only when some lane has one.
+// The quotient takes no division, only one Newton step from rs:
+//   t0 = fl(x rs),  e = fma(-t0, s, x),  t = fma(e, rs, t0).
+// * e is exact: x is a multiple of 2^(E-10) (its fp16 ulp) and t0 s of
+//   2^(E-34) (t0 ~ x/s), and |e| = s |x/s - t0| < |x| 2^-22 < 2^(E-21),
+//   so e needs fewer than 14 significant bits.
+// * t is fl32 of t0 + e rs = x/s + e (rs - 1/s), whose second term is below
+//   |x/s| 2^-45: a 2^-20 fraction of t's ulp.
+// * If x/s is a half-integer h, it is an fp32 value, so t == h exactly, and
+//   rint's ties-to-even rounds it as the rule does.
+// * Otherwise, where |x/s| >= 1/4, x/s lies at least 2^-15 from every
+//   half-integer (x = a 2^p, s = b 2^r with integers a, b < 2^11; the gap is
+//   a nonzero multiple of min(2^p, 2^r) / (2 b 2^r), and p - r >= -3 there),
+//   while |x/s| < 11 puts t within 2^-20 of it: rint(t) is the integer
+//   nearest x/s, which is rint(fl32(x/s)).  Where |x/s| < 1/4 both give 0.
+// No compare, select or branch is needed for ties.
 //
 // Packing: for an integer n in [-8, 7] and j < 4, n + 1.5 * 2^(23 - 4j) is
 // exact and its bit pattern holds n << 4j (two's complement) in bits
 // [4j, 4j + 4), so one and-or puts a code in place within a 16-bit half.
 __device__ __forceinline__ uint32_t quantize8(v8h v, float sf, float rs) {
-  float n[8], f[8];
-  bool tie = false;
-  const float half_s = 0.5f * sf;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float x = (float)v[i];
-    n[i] = __builtin_rintf(x * rs);
-    f[i] = __builtin_fmaf(-n[i], sf, x);
-    tie |= __builtin_fabsf(f[i]) == half_s;
-  }
-  if (__builtin_amdgcn_ballot_w64(tie) != 0) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const bool fix = (__builtin_fabsf(f[i]) == half_s) & ((((int)n[i]) & 1) != 0);
-      n[i] = fix ? n[i] + __builtin_copysignf(1.0f, f[i]) : n[i];
-    }
-  }
   // two 16-bit halves, each built with the biases 1.5 * 2^(23 - 4j), j < 4,
   // whose own set bits (22 and up) stay clear of bits [0, 16)
   uint32_t half[2] = {0u, 0u};
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int j = i & 3;
-    const float q = __builtin_amdgcn_fmed3f(n[i], -8.0f, 7.0f);
+    const float x = (float)v[i];
+    const float t0 = x * rs;
+    const float e = __builtin_fmaf(-t0, sf, x);
+    const float t = __builtin_fmaf(e, rs, t0);
+    const float q = __builtin_amdgcn_fmed3f(__builtin_rintf(t), -8.0f, 7.0f);
     const float biased = q + __builtin_ldexpf(1.5f, 23 - 4 * j);   // constant per i
     half[i >> 2] |= __builtin_bit_cast(uint32_t, biased) & (0xFu << (4 * j));
   }
   return half[0] | (half[1] << 16);
 }
 
-// max |x| over 8 fp16 values: for fp16, |x| orders like (bits & 0x7fff) as
-// unsigned integers, so the max is taken on the bit patterns.
-__device__ __forceinline__ uint32_t absmax8_bits(v8h v, uint32_t m) {
+// max |x| over 8 fp16 values, two lanes of 16 bits at a time: for fp16, |x|
+// orders like (bits & 0x7fff) as unsigned integers, so the max is taken on the
+// bit patterns (packed u16 max).
+__device__ __forceinline__ v2u16 absmax8_pk(v8h v, v2u16 m) {
   const v4u w = __builtin_bit_cast(v4u, v);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t a = w[i] & 0x7FFF7FFFu;
-    const uint32_t lo = a & 0xFFFFu, hi = a >> 16;
-    m = m > lo ? m : lo;
-    m = m > hi ? m : hi;
-  }
+  for (int i = 0; i < 4; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(v2u16, w[i] & 0x7FFF7FFFu));
   return m;
 }
 
@@ -89,7 +79,8 @@ __device__ __forceinline__ _Float16 group_scale(float amax) {
 // fp16 scale, and the lane's 16 codes as two dwords (d0: values 16c .. 16c+7).
 // Every lane of the wave must call it.
 __device__ __forceinline__ _Float16 quantize_group_row4(v8h lo, v8h hi, uint32_t& d0, uint32_t& d1) {
-  uint32_t amb = absmax8_bits(hi, absmax8_bits(lo, 0u));
+  const v2u16 pk = absmax8_pk(hi, absmax8_pk(lo, v2u16{0, 0}));
+  uint32_t amb = pk[0] > pk[1] ? pk[0] : pk[1];
   const uint32_t o16 = (uint32_t)__shfl_xor((int)amb, 16);
   amb = amb > o16 ? amb : o16;
   const uint32_t o32 = (uint32_t)__shfl_xor((int)amb, 32);

@@ -49,7 +49,7 @@ __global__ __launch_bounds__(NW * 64) void quantize_rows_kernel(
     uint16_t* __restrict__ scales, float* __restrict__ lora_part, int rh,
     const uint16_t* __restrict__ gamma, double eps) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar loop control
   const int r = lane & 15, c = lane >> 4;
   const int64_t rt = blockIdx.x / (16 / rh);
   const int r0 = (int)(blockIdx.x % (16 / rh)) * rh;
@@ -68,14 +68,20 @@ __global__ __launch_bounds__(NW * 64) void quantize_rows_kernel(
   // Unconditional loads (lanes of rows this workgroup does not own, or past
   // M, read row 0 of X and are zeroed afterwards): no lane-divergent branch
   // around the loads, so the compiler's vmcnt waits stay exact.
-  auto load_raw = [&](int64_t p, v8h* v) {
+  auto issue_x = [&](int64_t p, v8h* v) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int64_t k = p * kKPair + (s >> 1) * kGroup + c * 16 + (s & 1) * 8;
       v[s] = *reinterpret_cast<const v8h*>(xrow + k);   // (non-temporal loads measured 16% slower at 8192 x 4096)
     }
+  };
+  auto mask_x = [&](v8h* v) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) v[s] = valid ? v[s] : v8h{0, 0, 0, 0, 0, 0, 0, 0};
+  };
+  auto load_raw = [&](int64_t p, v8h* v) {
+    issue_x(p, v);
+    mask_x(v);
   };
 
   double inv = 1.0;   // 1/rms of row r (NORM)
@@ -103,8 +109,10 @@ __global__ __launch_bounds__(NW * 64) void quantize_rows_kernel(
     inv = 1.0 / __builtin_sqrt(tot / (double)K + eps);
   }
 
-  auto load_x = [&](int64_t p, v8h* v) {
-    load_raw(p, v);
+  // the loaded k-pair of X as the quantizer takes it: masked, and
+  // normalized under NORM (gm: gamma at the lane's 32 columns)
+  auto finish_x = [&](const v8h* gm, v8h* v) {
+    mask_x(v);
     if constexpr (NORM) {
       // No contraction here: under it the backend may merge the two
       // conversions fp64 -> fp32 -> fp16 into one rounding fp64 -> fp16,
@@ -112,26 +120,21 @@ __global__ __launch_bounds__(NW * 64) void quantize_rows_kernel(
       // fp16 tie.
 #pragma clang fp contract(off)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int64_t k = p * kKPair + (s >> 1) * kGroup + c * 16 + (s & 1) * 8;
-        const v8h gm = *reinterpret_cast<const v8h*>(reinterpret_cast<const _Float16*>(gamma) + k);
+      for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const double t = ((double)(float)v[s][i] * inv) * (double)(float)gm[i];
+          const double t = ((double)(float)v[s][i] * inv) * (double)(float)gm[s][i];
           v[s][i] = (_Float16)(float)t;
         }
-      }
     }
   };
 
-  v8h v[4];
-  int64_t p = pbeg + wave;
-  for (; p < pend; p += NW) {
-    // this k-pair's X, then its L_down fragments (L2-resident, shared by
-    // every row tile): the LoRA MFMAs wait for the latter while the quantizer
-    // arithmetic runs.  No prefetch of the next k-pair's X: the registers it
-    // needs cost more occupancy than the latency it hides (measured).
-    load_x(p, v);
+  // One k-pair: its L_down fragments (L2-resident, shared by every row tile)
+  // and, under NORM, gamma are loaded first, then the next k-pair's X into `nxt` (its index clamped
+  // to a k-pair of the range, so the loads need no branch; on a wave's last
+  // k-pair it re-reads the current one, from cache), so that the LoRA MFMAs'
+  // wait for L_down leaves the next X in flight while this one is quantized.
+  auto step = [&](int64_t p, v8h* cur, v8h* nxt) {
     constexpr int RTL = RT > 0 ? RT : 1;
     v8h lb[RTL][4];
     if constexpr (RT > 0) {
@@ -141,11 +144,25 @@ __global__ __launch_bounds__(NW * 64) void quantize_rows_kernel(
 #pragma unroll
         for (int s = 0; s < 4; ++s) lb[t][s] = *reinterpret_cast<const v8h*>(lp + ((size_t)(t * 4 + s) * 64 + lane) * 8);
     }
+    v8h gm[NORM ? 4 : 1];
+    if constexpr (NORM) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int64_t k = p * kKPair + (s >> 1) * kGroup + c * 16 + (s & 1) * 8;
+        gm[s] = *reinterpret_cast<const v8h*>(reinterpret_cast<const _Float16*>(gamma) + k);
+      }
+    }
+    // every L_down and gamma load ahead of the X loads, and those ahead of
+    // this k-pair's arithmetic
+    __builtin_amdgcn_sched_barrier(0);
+    issue_x(p + NW < pend ? p + NW : p, nxt);
+    __builtin_amdgcn_sched_barrier(0);
+    finish_x(gm, cur);
     uint32_t d[4];
     _Float16 sc[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const _Float16 s = quantize_group_row4(v[2 * h], v[2 * h + 1], d[2 * h], d[2 * h + 1]);
+      const _Float16 s = quantize_group_row4(cur[2 * h], cur[2 * h + 1], d[2 * h], d[2 * h + 1]);
       sc[h] = valid ? s : (_Float16)0.0f;
     }
     uint8_t* tile = codes + (size_t)(rt * KP + p) * kTileBytes;
@@ -159,9 +176,27 @@ __global__ __launch_bounds__(NW * 64) void quantize_rows_kernel(
 #pragma unroll
       for (int t = 0; t < RT; ++t)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) acc[t] = mfma_f16_16x16x32(v[s], lb[t][s], acc[t]);
+        for (int s = 0; s < 4; ++s) acc[t] = mfma_f16_16x16x32(cur[s], lb[t][s], acc[t]);
     }
+  };
+
+  // The wave's k-pairs pbeg + wave, + NW, ... two per trip, the X buffers
+  // alternating so that no register copy waits on a load in flight.
+  // pbeg < pend: the activation layout never splits K into more ranges than
+  // k-pairs.
+  // The trip count is uniform and each trip straight-line, so every path
+  // into the loop head has the same loads in flight (a break between the
+  // two steps would add one with the other buffer still loading, and the
+  // compiler would drain every load there).
+  v8h xa[4], xb[4];
+  int64_t p = pbeg + wave;
+  const int64_t n = p < pend ? (pend - p + NW - 1) / NW : 0;   // this wave's k-pairs
+  issue_x(p < pend ? p : pbeg, xa);
+  for (int64_t i = 0; i + 2 <= n; i += 2, p += 2 * NW) {
+    step(p, xa, xb);
+    step(p + NW, xb, xa);
   }
+  if (n & 1) step(p, xa, xb);
 
   if constexpr (RT > 0) {
     // red[w][t*4 + i][lane]: partial of rows 4c+i, rank 16t + (lane & 15);

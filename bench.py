@@ -639,11 +639,13 @@ def main(argv=None):
     args = ap.parse_args(argv)
     if args.workload is None:
         args.workload = "mlp_up" if args.mlp else "prefill"
+    # records are keyed as the run that reads them looks them up: decode by its M
+    record = args.workload if args.m is None else f"{args.workload}-{args.m}"
     if args.ingest_pmc:
-        ingest_pmc(args.workload, *args.ingest_pmc, command=args.pmc_command)
+        ingest_pmc(record, *args.ingest_pmc, command=args.pmc_command)
         return 0
     if args.ingest_sq:
-        ingest_sq(args.workload, args.ingest_sq, command=args.pmc_command)
+        ingest_sq(record, args.ingest_sq, command=args.pmc_command)
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the layer's "

@@ -559,6 +559,57 @@ def test_rmsnorm_fp32_step_of_the_fp16_conversion():
     _check_lora_act(a, la, M)
 
 
+# Activation-pass launch shapes (M, K, R, RMSNorm): the pass splits K into
+# ks ranges (the library's act layout reports ks), gives each workgroup
+# NW = 16, 8, 4 or 2 waves by its k-pairs (16 only with < 256 workgroups and
+# a rank its registers allow), and wave w takes k-pairs w, w + NW, ... of its
+# range: two per loop trip, one more after the loop when the count is odd.
+QUANT_SHAPES = [(1, 128, 16, False),     # 1 k-pair, 2 waves: wave 1 has none
+                (1, 640, 32, True),      # 5 k-pairs, 4 waves: 2, 1, 1, 1
+                (8, 2304, 48, False),    # 4 ranges of 4-5 k-pairs, 4 waves
+                (40, 4224, 64, True),    # 4 ranges of 8-9, 8 waves
+                (40, 8320, 16, True),    # 4 ranges of 16-17, 16 waves
+                (4096, 3072, 32, False),  # 24 k-pairs, 8 waves: 3 each (a trip and a peeled step)
+                (4096, 4096, 16, True)]  # 32 k-pairs, 8 waves: 4 each (two trips)
+
+
+def _quant_waves(M, K, R, norm):
+    """(NW, sorted set of k-pairs per wave) of the activation pass's launch."""
+    _, _, ks = W.w4a4_act_layout(M, K, R, with_splits=True)
+    KP, mt = K // 128, -(-M // 16)
+    rh = 16
+    while rh > 8 and mt * (16 // rh) * ks < 256:
+        rh //= 2
+    wgs, kp_wg = mt * ks, KP // ks
+    if kp_wg >= 16 and wgs < 256 and R <= (16 if norm else 32):
+        nw = 16
+    else:
+        nw = 8 if kp_wg >= 8 else (4 if kp_wg >= 4 else 2)
+    counts = set()
+    for j in range(ks):
+        n = (j + 1) * KP // ks - j * KP // ks
+        counts |= {len(range(w, n, nw)) for w in range(nw)}
+    return nw, counts
+
+
+@pytest.mark.parametrize("M,K,R,norm", QUANT_SHAPES)
+def test_quantizer_launch_shapes(M, K, R, norm):
+    """Codes and scales bit-exact, lora_act within 1e-4 * rms, for every
+    wave count and every number of k-pairs per wave the loop handles."""
+    case = workloads.random_case(M, K, 16, R, seed=4400 + M + K + R)
+    nw, counts = _quant_waves(M, K, R, norm)
+    _say(f"[quant shape] M={M} K={K} R={R} norm={norm}: {nw} waves, k-pairs per wave {sorted(counts)}")
+    if norm:
+        gamma = np.random.default_rng(4401 + K).uniform(0.5, 2.0, K).astype(np.float16)
+        _, qx, sx, la = O.quantize_act_rmsnorm(case["x"], gamma, 1e-6, case["lora_down"])
+        run = GpuRun(case, norm=(gamma, 1e-6))
+    else:
+        qx, sx, la = O.quantize_act(case["x"], case["lora_down"])
+        run = GpuRun(case)
+    a = _check_quant(run, case, qx, sx)
+    _check_lora_act(a, la, M)
+
+
 def test_svdquant_checkpoint_layer():
     """A checkpoint derived offline (w4a4_gemm_lora_amd.svdquant: RTN int4 plus
     rank-32 factors of the quantization error) packed through the qweight

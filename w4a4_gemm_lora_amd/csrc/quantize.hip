@@ -6,7 +6,7 @@
 // LoRA down-projection lora_act = X L_down on the fp16 values.  Section 2.3 /
 // 3.10: weights are repacked once at load into the kernel's layout.
 //
-// gfx950 design: one workgroup of 4, 8 or 16 waves per (16-row tile, k-pair
+// gfx950 design: one workgroup of 2, 4, 8 or 16 waves per (16-row tile, k-pair
 // range); a wave owns whole 16 x 128 k-pairs.  Lane l = r + 16c loads the 32 fp16 values
 // of row r at k = 128p + 64j + 16c + [0,16) (j = group in the pair) with four
 // 128-bit loads, and those registers serve three purposes without any LDS
@@ -129,11 +129,12 @@ __global__ __launch_bounds__(NW * 64) void quantize_rows_kernel(
     }
   };
 
-  // One k-pair: its L_down fragments (L2-resident, shared by every row tile)
-  // and, under NORM, gamma are loaded first, then the next k-pair's X into `nxt` (its index clamped
-  // to a k-pair of the range, so the loads need no branch; on a wave's last
-  // k-pair it re-reads the current one, from cache), so that the LoRA MFMAs'
-  // wait for L_down leaves the next X in flight while this one is quantized.
+  // One k-pair.  Its L_down fragments (L2-resident, shared by every row
+  // tile) and, under NORM, gamma are loaded first, then the next k-pair's X
+  // into `nxt`, so that the LoRA MFMAs' wait for L_down leaves the next X in
+  // flight while this one is quantized.  The next index is clamped to a
+  // k-pair of the range, so the loads need no branch; on a wave's last
+  // k-pair they re-read the current one, from cache.
   auto step = [&](int64_t p, v8h* cur, v8h* nxt) {
     constexpr int RTL = RT > 0 ? RT : 1;
     v8h lb[RTL][4];
@@ -181,13 +182,12 @@ __global__ __launch_bounds__(NW * 64) void quantize_rows_kernel(
   };
 
   // The wave's k-pairs pbeg + wave, + NW, ... two per trip, the X buffers
-  // alternating so that no register copy waits on a load in flight.
-  // pbeg < pend: the activation layout never splits K into more ranges than
-  // k-pairs.
-  // The trip count is uniform and each trip straight-line, so every path
-  // into the loop head has the same loads in flight (a break between the
-  // two steps would add one with the other buffer still loading, and the
-  // compiler would drain every load there).
+  // alternating so that no register copy waits on a load in flight.  The
+  // trip count is uniform and each trip straight-line, so every path into
+  // the loop head has the same loads in flight (a break between the two
+  // steps would add one with the other buffer still loading, and the
+  // compiler would drain every load there).  pbeg < pend: the activation
+  // layout never splits K into more ranges than k-pairs.
   v8h xa[4], xb[4];
   int64_t p = pbeg + wave;
   const int64_t n = p < pend ? (pend - p + NW - 1) / NW : 0;   // this wave's k-pairs

@@ -530,6 +530,14 @@ def measured_peaks(torch, W):
     r_m, r_f = roles(1, 0, rit_m, 0), roles(2, 0, rit_f, 0)
     r_ff, r_mf = roles(2, 2, rit_f, rit_f), roles(1, 2, rit_m, rit_f)
     fma_rate = 2 * lib.w4a4_peak_roles_ops(2, rit_f) / (r_ff * 1e-3) / 1e12
+    # the GEMM loop's per-tile mix in every wave, whole and by parts; MFMA
+    # issue costs (two waves per SIMD, 8 independent MFMAs per iteration)
+    rit_t = 4000
+    r_mix, r_mpart, r_vpart = roles(3, 3, rit_t, rit_t), roles(4, 4, rit_t, rit_t), roles(5, 5, rit_t, rit_t)
+    r_i8, r_4b, r_k32 = roles(1, 1, rit_t, rit_t), roles(6, 6, rit_t, rit_t), roles(7, 7, rit_t, rit_t)
+
+    def per_mfma_cycles(ms):
+        return round(ms * 1e-3 * CLOCK_GHZ * 1e9 / (2 * 8 * rit_t), 1)
     return {"int8_mfma": {"unit": "TOPS", "published": PEAK_INT8_TOPS,
                           "measured": round(lib.w4a4_peak_i8_mfma_ops(iters) / (t_m * 1e-3) / 1e12, 1)},
             "hbm_read": {"unit": "GB/s", "published": PEAK_HBM_GBPS,
@@ -541,7 +549,17 @@ def measured_peaks(torch, W):
                                 "both_on_every_simd_ms": round(r_mf, 3),
                                 "overlap_of_shorter": round((r_m + r_f - r_mf) / min(r_m, r_f), 3),
                                 "note": "one int8-MFMA wave and one fp32-FMA wave on each SIMD; overlap 1 = "
-                                        "the shorter one hidden entirely, 0 = run one after the other"}}
+                                        "the shorter one hidden entirely, 0 = run one after the other"},
+            "mfma_within_fma_stream": {"tile_mix_ms": round(r_mix, 3), "mfma_part_ms": round(r_mpart, 3),
+                                       "valu_part_ms": round(r_vpart, 3),
+                                       "overlap_of_shorter": round((r_mpart + r_vpart - r_mix) / min(r_mpart, r_vpart), 3),
+                                       "note": "every wave interleaves the GEMM loop's per-tile int8 MFMA, 4 fp32 "
+                                               "fmas and 2 integer ops (two waves per SIMD), against the MFMA and "
+                                               "VALU parts alone"},
+            "mfma_issue_cycles": {"i8_16x16x64": per_mfma_cycles(r_i8), "f16_16x16x4_4b": per_mfma_cycles(r_4b),
+                                  "f16_16x16x32": per_mfma_cycles(r_k32),
+                                  "note": "SIMD cycles per MFMA at the nominal clock, two waves of 8 independent "
+                                          "chains per SIMD"}}
 
 
 def read_floor_us(torch, W, nbytes, rotate=12, n=48):

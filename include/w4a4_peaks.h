@@ -46,7 +46,12 @@ int64_t w4a4_peak_hbm_read_out_ints(void);
  * iters_b.  Roles: 0 nothing, 1 = 8 independent v_mfma_i32_16x16x64_i8 per
  * iteration, 2 = 32 independent wave64 v_fma_f32 per iteration.  Timing one
  * role alone and both together gives the unpacked fp32 VALU rate and how
- * far the two overlap.  out: int32 device buffer of
+ * far the two overlap.  Roles 3..5 time the GEMM loop's per-tile mix within
+ * one wave, 8 tiles per iteration: 3 = per tile one int8 MFMA and, on the
+ * tile before's sums, 4 v_fma_f32 and 2 integer ops; 4 = its MFMAs alone;
+ * 5 = its VALU ops alone.  Roles 6 and 7 = 8 independent
+ * v_mfma_f32_16x16x4_4b_f16 or v_mfma_f32_16x16x32_f16 per iteration (their
+ * issue cost).  out: int32 device buffer of
  * w4a4_peak_roles_out_ints() entries.  w4a4_peak_roles_ops(role, iters):
  * int8 operations (role 1) or fp32 FMA lane operations (role 2) of the
  * four waves of one role on every CU. */

@@ -53,7 +53,8 @@ def test_peaks_library_exports_every_declared_symbol():
     assert lib.w4a4_peak_roles_out_ints() == 256 * 512
     assert lib.w4a4_peak_roles_ops(1, 10) == 256 * 4 * 8 * 10 * 2 * 16 * 16 * 64
     assert lib.w4a4_peak_roles_ops(2, 10) == 256 * 4 * 32 * 10 * 64
-    assert lib.w4a4_peak_roles(3, 0, 1, 1, ctypes.c_void_p(1 << 20), None) == 4
+    assert lib.w4a4_peak_roles(8, 0, 1, 1, ctypes.c_void_p(1 << 20), None) == 4   # roles are 0..7
+    assert lib.w4a4_peak_roles(0, -1, 1, 1, ctypes.c_void_p(1 << 20), None) == 4
     assert lib.w4a4_peak_roles(1, 2, 1, 1, None, None) == 4
 
 

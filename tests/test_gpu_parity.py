@@ -57,7 +57,7 @@ def _to_dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-class GpuRun:
+class GpuLayerRun:
     """Pack, quantize and run one layer on the GPU; keep host copies."""
 
     def __init__(self, case, use_qweight=False, ldx=None, ldy=None, R=None, norm=None):
@@ -237,7 +237,7 @@ def _workload(name):
 def test_workload_parity_full_output(name):
     case = _workload(name)
     _say(f"[parity] {name} M={case['M']} K={case['K']} N={case['N']} R={case['R']}")
-    run = GpuRun(case)
+    run = GpuLayerRun(case)
     ref = O.linear(case["x"], case["lora_down"], case["lora_up"], case["col_scale"], case["bias"], w16=case["w"])
     a = _check_quant(run, case, ref["qx"], ref["sx"])
     _check_weights(run, case, ref["qw"], ref["sw"])
@@ -267,7 +267,7 @@ def test_prefill_parity_full():
     case = workloads.generate("prefill")
     M, K, N = case["M"], case["K"], case["N"]
     _say(f"[parity] prefill M={M} K={K} N={N} R={case['R']}")
-    run = GpuRun(case)
+    run = GpuLayerRun(case)
     qx, sx = O.quantize_groups(case["x"])
     qw, sw = O.quantize_groups(case["w"])
     a = _check_quant(run, case, qx, sx)
@@ -302,7 +302,7 @@ def test_ragged_and_rank_edges(M, K, N, R):
     rank 32, 8 at rank 64), K = 16384 at M = 3 eight ways (16 waves)."""
     case = workloads.random_case(M, K, N, R, seed=1000 + M + K + R)
     _say(f"[edge] M={M} K={K} N={N} R={R}")
-    run = GpuRun(case)
+    run = GpuLayerRun(case)
     ref = O.linear(case["x"], case["lora_down"] if R else None, case["lora_up"] if R else None,
                    case["col_scale"], case["bias"], w16=case["w"])
     a = _check_quant(run, case, ref["qx"], ref["sx"])
@@ -345,7 +345,7 @@ def test_small_m_decode_shapes(M, K, N, R):
     case["w"] = w.astype(np.float16)
     _say(f"[decode-shape] M={M} K={K} N={N} R={R}")
     assert W.w4a4_query_variant(M, N, K, R) == 1
-    run = GpuRun(case)
+    run = GpuLayerRun(case)
     ref = O.linear(case["x"], case["lora_down"] if R else None, case["lora_up"] if R else None,
                    case["col_scale"], case["bias"], w16=case["w"])
     a = _check_quant(run, case, ref["qx"], ref["sx"])
@@ -369,7 +369,7 @@ def test_every_tile_shape(cfg, K, R, monkeypatch):
     monkeypatch.setenv("W4A4_TILED_CFG", str(cfg))
     case = workloads.random_case(M, K, N, R, seed=3000 + cfg + K + R)
     _say(f"[tile shape {cfg}] M={M} K={K} N={N} R={R} partials={ks}")
-    run = GpuRun(case)
+    run = GpuLayerRun(case)
     ref = O.linear(case["x"], case["lora_down"], case["lora_up"], case["col_scale"], case["bias"], w16=case["w"])
     _check_y(run.host_y()[:M, :N], ref["y"], f"tile shape {cfg}", y64=ref["y64"], ref=ref, case=case)
     assert np.all(np.isnan(run.host_y()[M:].astype(np.float64)))
@@ -386,7 +386,7 @@ def test_every_lean_tile_shape(cfg, K, R, monkeypatch):
     monkeypatch.setenv("W4A4_TILED_LEAN", "1")
     case = workloads.random_case(M, K, N, R, seed=3500 + cfg + K + R)
     _say(f"[lean tile shape {cfg}] M={M} K={K} N={N} R={R}")
-    run = GpuRun(case)
+    run = GpuLayerRun(case)
     ref = O.linear(case["x"], case["lora_down"], case["lora_up"], case["col_scale"], case["bias"], w16=case["w"])
     _check_y(run.host_y()[:M, :N], ref["y"], f"lean tile shape {cfg}", y64=ref["y64"], ref=ref, case=case)
     assert np.all(np.isnan(run.host_y()[M:].astype(np.float64)))
@@ -404,7 +404,7 @@ def test_every_k_split_tile_shape(cfg, R, monkeypatch):
     monkeypatch.setenv("W4A4_TILED_KSPLIT", "1")
     case = workloads.random_case(M, K, N, R, seed=3700 + cfg + R)
     _say(f"[k-split tile shape {cfg}] M={M} K={K} N={N} R={R}")
-    run = GpuRun(case)
+    run = GpuLayerRun(case)
     ref = O.linear(case["x"], case["lora_down"], case["lora_up"], case["col_scale"], case["bias"], w16=case["w"])
     _check_y(run.host_y()[:M, :N], ref["y"], f"k-split tile shape {cfg}", y64=ref["y64"], ref=ref, case=case)
     assert np.all(np.isnan(run.host_y()[M:].astype(np.float64)))
@@ -413,7 +413,7 @@ def test_every_k_split_tile_shape(cfg, R, monkeypatch):
 def test_strided_x_and_y():
     M, K, N, R = 40, 256, 64, 32
     case = workloads.random_case(M, K, N, R, seed=7)
-    run = GpuRun(case, ldx=K + 64, ldy=N + 24)
+    run = GpuLayerRun(case, ldx=K + 64, ldy=N + 24)
     ref = O.linear(case["x"], case["lora_down"], case["lora_up"], case["col_scale"], case["bias"], w16=case["w"])
     _check_quant(run, case, ref["qx"], ref["sx"])
     y = run.host_y()
@@ -431,7 +431,7 @@ def test_checkpoint_codes_with_minus_eight():
     nib = (q & 0xF).astype(np.uint8)
     case["qweight"] = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
     case["w_scales"] = (rng.uniform(0.001, 0.01, size=(N, K // 64))).astype(np.float16)
-    run = GpuRun(case, use_qweight=True)
+    run = GpuLayerRun(case, use_qweight=True)
     ref = O.linear(case["x"], case["lora_down"], case["lora_up"], case["col_scale"], case["bias"],
                    qweight=case["qweight"], w_scales=case["w_scales"])
     assert np.array_equal(ref["qw"], q.astype(np.int8))
@@ -453,7 +453,7 @@ def test_extreme_rows_and_determinism():
     x[7] = np.where(np.arange(K) % 64 == 0, 60000.0, x[7])
     case["x"] = np.clip(x, -65504, 65504).astype(np.float16)
     case["lora_down"] = (case["lora_down"].astype(np.float64) * 1e-3).astype(np.float16)
-    run = GpuRun(case)
+    run = GpuLayerRun(case)
     ref = O.linear(case["x"], case["lora_down"], case["lora_up"], case["col_scale"], case["bias"], w16=case["w"])
     _check_quant(run, case, ref["qx"], ref["sx"])
     y1 = run.host_y().copy()
@@ -499,7 +499,7 @@ def test_rmsnorm_quantize(M, K, N, R, eps):
     case["x"] = x.astype(np.float16)
     gamma = rng.uniform(0.25, 2.0, K).astype(np.float16)
     _say(f"[rmsnorm] M={M} K={K} N={N} R={R} eps={eps}")
-    run = GpuRun(case, norm=(gamma, eps))
+    run = GpuLayerRun(case, norm=(gamma, eps))
     xn, qx, sx, la = O.quantize_act_rmsnorm(case["x"], gamma, eps, case["lora_down"] if R else None)
     a = _check_quant(run, case, qx, sx)
     _check_lora_act(a, la, M)
@@ -554,7 +554,7 @@ def test_rmsnorm_fp32_step_of_the_fp16_conversion():
     changed = int(np.sum(sx_one_step.view(np.uint16) != sx.view(np.uint16)))
     _say(f"[rmsnorm double rounding] M={M} K={K}: {hits} targeted maxima, {changed} scales differ in one step")
     assert hits > 400 and changed > 100
-    run = GpuRun(case, norm=(gamma, eps))
+    run = GpuLayerRun(case, norm=(gamma, eps))
     a = _check_quant(run, case, qx, sx)
     _check_lora_act(a, la, M)
 
@@ -602,10 +602,10 @@ def test_quantizer_launch_shapes(M, K, R, norm):
     if norm:
         gamma = np.random.default_rng(4401 + K).uniform(0.5, 2.0, K).astype(np.float16)
         _, qx, sx, la = O.quantize_act_rmsnorm(case["x"], gamma, 1e-6, case["lora_down"])
-        run = GpuRun(case, norm=(gamma, 1e-6))
+        run = GpuLayerRun(case, norm=(gamma, 1e-6))
     else:
         qx, sx, la = O.quantize_act(case["x"], case["lora_down"])
-        run = GpuRun(case)
+        run = GpuLayerRun(case)
     a = _check_quant(run, case, qx, sx)
     _check_lora_act(a, la, M)
 
@@ -624,7 +624,7 @@ def test_svdquant_checkpoint_layer():
     case = workloads.random_case(M, K, N, R, seed=4200)
     case.update(qweight=d["qweight"], w_scales=d["w_scales"], lora_down=d["proj_down"], lora_up=d["proj_up"])
     _say(f"[svdquant] M={M} K={K} N={N} R={R} residual/rtn={d['residual_norm'] / d['rtn_error_norm']:.3f}")
-    run = GpuRun(case, use_qweight=True)
+    run = GpuLayerRun(case, use_qweight=True)
     ref = O.linear(case["x"], d["proj_down"], d["proj_up"], case["col_scale"], case["bias"],
                    qweight=d["qweight"], w_scales=d["w_scales"])
     _check_weights(run, case, d["codes"], d["w_scales"])

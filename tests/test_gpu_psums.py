@@ -19,7 +19,7 @@ import pytest
 import w4a4_gemm_lora_amd as W
 from w4a4_gemm_lora_amd import workloads
 from oracle import w4a4_oracle as O
-from tests.test_gpu_parity import GpuRun, _check_y, _say, _to_dev, _torch, _workload
+from tests.test_gpu_parity import GpuLayerRun, _check_y, _say, _to_dev, _torch, _workload
 
 pytestmark = pytest.mark.gpu
 
@@ -51,7 +51,7 @@ def test_psums_whole_output_of_each_workload(name):
     dot kernel, MFMA decode kernel with two column tiles per workgroup, MFMA
     decode kernel)."""
     case = _workload(name)
-    run = GpuRun(case)
+    run = GpuLayerRun(case)
     _say(f"[psums] {name} M={run.M} K={run.K} N={run.N} variant={W.w4a4_query_variant(run.M, run.N, run.K, run.R)}")
     qx, _ = O.quantize_groups(case["x"])
     qw, _ = O.quantize_groups(case["w"])
@@ -86,7 +86,7 @@ def test_psums_every_tiled_instance(cfg, lean, ksplit, monkeypatch):
     case["qweight"] = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
     case["w_scales"] = rng.uniform(1e-3, 1e-2, size=(N, K // 64)).astype(np.float16)
     _say(f"[psums tiled] cfg={cfg} lean={lean} ksplit={ksplit}")
-    run = GpuRun(case, use_qweight=True)
+    run = GpuLayerRun(case, use_qweight=True)
     qx, _ = O.quantize_groups(case["x"])
     _check_window(_full_psums(run), qx, q.astype(np.int8), 0, 0, M, f"cfg {cfg} lean {lean} ksplit {ksplit}")
     ref = O.linear(case["x"], case["lora_down"], case["lora_up"], case["col_scale"], case["bias"],
@@ -131,7 +131,7 @@ def test_psums_decode_kernels_with_minus_eight(M, K, N):
     case["qweight"] = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
     case["w_scales"] = rng.uniform(1e-3, 1e-2, size=(N, K // 64)).astype(np.float16)
     _say(f"[psums decode -8] M={M} K={K} N={N}")
-    run = GpuRun(case, use_qweight=True)
+    run = GpuLayerRun(case, use_qweight=True)
     qx, _ = O.quantize_groups(case["x"])
     assert np.any(qx == -8), "the subnormal rows must carry -8 codes"
     a = run.host_act()
@@ -193,7 +193,7 @@ def test_psums_every_decode_shape_forced(M, waves, tiles, monkeypatch):
     monkeypatch.setenv("W4A4_DECODE_TILES", str(tiles))
     case = workloads.random_case(M, K, N, R, seed=6500 + M + 10 * waves + tiles)
     _say(f"[psums decode forced] M={M} waves={waves} tiles={tiles}")
-    run = GpuRun(case)
+    run = GpuLayerRun(case)
     qx, _ = O.quantize_groups(case["x"])
     qw, _ = O.quantize_groups(case["w"])
     _check_window(_full_psums(run), qx, qw, 0, 0, M, f"decode forced M={M} waves={waves} tiles={tiles}")

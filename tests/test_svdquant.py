@@ -26,10 +26,10 @@ def test_rtn_matches_oracle_quantizer_and_checkpoint_packing():
 
 
 def test_factors_are_truncated_svd_of_the_error():
-    """Round 1's factors are the best rank-R approximation of E = W - deq(Q)
-    (Eckart-Young): the residual equals the norm of E's trailing singular
-    values (up to the fp16 rounding of the factors), and full rank leaves
-    almost nothing."""
+    """With one refinement round (rounds=1) the factors are the best rank-R
+    approximation of E = W - deq(Q) (Eckart-Young): the residual equals the
+    norm of E's trailing singular values (up to the fp16 rounding of the
+    factors), and full rank leaves almost nothing."""
     rng = np.random.default_rng(12)
     w = (rng.standard_normal((64, 128)) * 0.02).astype(np.float16)
     q, s = O.quantize_groups(w)

@@ -28,11 +28,12 @@ if ROOT not in sys.path:
 METRIC = "W4A4+LoRA linear TOPS & HBM GB/s at 1 GPU; % of roofline per shape"
 PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA, 10^12 ops/s
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
-# VALU issue peak for the unpacked 32-bit operations this code issues: a
-# wave64 op takes 4 cycles of a SIMD (16 lanes per clock, measured: ~4.2
-# cycles per dependent-free v_fma_f32 with 2-4 waves per SIMD), so 256 CUs x
-# 4 SIMDs x 16 lanes x 2.4 GHz.  The published 157.3 TFLOP/s fp32 vector rate
-# counts packed two-wide FMAs, which this build does not use.
+# VALU issue peak for the unpacked 32-bit operations this code issues, at 16
+# lanes per SIMD and clock: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz.  (Measured
+# in measured_peaks: ~4.8 cycles per wave64 v_fma_f32 with an SGPR operand in
+# independent chains; ~2.6 per op for v_fmac_f32 mixed with integer ops.)  The
+# published 157.3 TFLOP/s fp32 vector rate counts packed two-wide FMAs, which
+# this library does not use.
 PEAK_VALU_TLANEOPS = 39.3
 CLOCK_GHZ = 2.4             # peak engine clock the utilisation fractions are taken against
 N_SIMDS = 1024

@@ -28,13 +28,12 @@ if ROOT not in sys.path:
 METRIC = "W4A4+LoRA linear TOPS & HBM GB/s at 1 GPU; % of roofline per shape"
 PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA, 10^12 ops/s
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
-# VALU issue peak for the unpacked 32-bit operations this code issues, at 16
-# lanes per SIMD and clock: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz.  (Measured
-# in measured_peaks: ~4.8 cycles per wave64 v_fma_f32 with an SGPR operand in
-# independent chains; ~2.6 per op for v_fmac_f32 mixed with integer ops.)  The
-# published 157.3 TFLOP/s fp32 vector rate counts packed two-wide FMAs, which
-# this library does not use.
-PEAK_VALU_TLANEOPS = 39.3
+# fp32 FMA lane operations per second at MI355X's published 157.3 TFLOP/s
+# fp32 vector rate (2 flops per FMA): 256 CUs x 4 SIMDs x 32 lanes x 2.4 GHz.
+# measured_peaks times what the two-operand v_fmac_f32 reaches (~0.7 of it);
+# the three-operand v_fma_f32 issues ~10% slower, and with an SGPR
+# multiplicand and an inline-constant addend at about half the v_fmac rate.
+PEAK_VALU_TLANEOPS = 78.6
 CLOCK_GHZ = 2.4             # peak engine clock the utilisation fractions are taken against
 N_SIMDS = 1024
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
@@ -543,9 +542,9 @@ def measured_peaks(torch, W):
                           "measured": round(lib.w4a4_peak_i8_mfma_ops(iters) / (t_m * 1e-3) / 1e12, 1)},
             "hbm_read": {"unit": "GB/s", "published": PEAK_HBM_GBPS,
                          "measured": round(nbytes / (t_h * 1e-3) / 1e9, 1)},
-            "fp32_fma_valu": {"unit": "T lane-ops/s", "published_unpacked": PEAK_VALU_TLANEOPS,
+            "fp32_fma_valu": {"unit": "T lane-ops/s", "published": PEAK_VALU_TLANEOPS,
                               "measured": round(fma_rate, 2),
-                              "note": "two waves of independent wave64 v_fma_f32 per SIMD"},
+                              "note": "two waves per SIMD of independent wave64 v_fmac_f32 (acc += x * y)"},
             "mfma_beside_fma": {"mfma_wave_alone_ms": round(r_m, 3), "fma_wave_alone_ms": round(r_f, 3),
                                 "both_on_every_simd_ms": round(r_mf, 3),
                                 "overlap_of_shorter": round((r_m + r_f - r_mf) / min(r_m, r_f), 3),

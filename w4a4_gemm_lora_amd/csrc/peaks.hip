@@ -54,15 +54,19 @@ __global__ __launch_bounds__(256) void peak_hbm_read_kernel(const v4u* __restric
 
 constexpr int kReadWorkgroups = 256 * 8;
 
-// fp32 FMA issue: every wave iters x 32 independent v_fma_f32 (wave64).
+// fp32 FMA issue: every wave iters x 32 independent accumulating FMAs
+// (wave64), acc += x * y with x and y in VGPRs: the two-operand v_fmac_f32
+// form the GEMM's fmas take.  (An FMA with an SGPR multiplicand and an inline
+// constant addend issues at about half that rate on gfx950.)
 template <int N>
 __device__ __forceinline__ float fma_chains(int iters, int lane) {
   float f[N];
 #pragma unroll
   for (int i = 0; i < N; ++i) f[i] = (float)(lane + i);
+  const float x = 1.0001f + (float)lane * 1e-9f, y = 0.5f - (float)lane * 1e-9f;
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
-    for (int i = 0; i < N; ++i) f[i] = __builtin_fmaf(f[i], 1.0001f, 0.5f);
+    for (int i = 0; i < N; ++i) f[i] = __builtin_fmaf(x, y, f[i]);
   }
   float r = 0.f;
 #pragma unroll

@@ -224,7 +224,8 @@ def test_quantizer_every_quotient_on_gpu():
                            f"{[float(x[r, c]) for r, c in bad[:3]]}")
 
 
-WORKLOAD_CASES = ["small", "mlp_up", "mlp_down", "decode-1", "decode-2", "decode-4", "decode-16"]
+WORKLOAD_CASES = ["small", "mlp_up", "mlp_down", "decode-1", "decode-2", "decode-3", "decode-4", "decode-8", "decode-13",
+                  "decode-16"]
 
 
 def _workload(name):
